@@ -1,0 +1,158 @@
+"""CPU oracle for the modulated deformable conv2d forward -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it and it
+loads nothing of the GPU library: the two share no code.
+
+The arithmetic lives in ``dcn_oracle.cpp`` (a plain C++ loop nest written from
+page 1, "deform_conv.py": module docstring and ``deform_conv2d_gather``).  This
+module only compiles it with g++ and marshals numpy arrays through ctypes.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
+that do not come from the oracle itself (direct convolution, integer shifts,
+out-of-image sampling, a hand-derived 2x2 example, tap order, partition of
+unity, linearity, and an independent numpy formulation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dcn_oracle.cpp")
+_LIB = os.path.join(_HERE, "libdcn_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/libdcn_oracle.so`` (g++, no SIMD flags)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-shared",
+           "-fPIC", "-pthread", "-o", tmp, _SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "batch", "in_ch", "height", "width", "out_ch", "kernel_h", "kernel_w", "pad_h", "pad_w")]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        vp = ctypes.c_void_p
+        lib.dcn_oracle_forward.argtypes = [ctypes.POINTER(_Shape), vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_int64, vp, vp, ctypes.c_int]
+        lib.dcn_oracle_forward.restype = ctypes.c_int
+        lib.dcn_oracle_coords.argtypes = [ctypes.POINTER(_Shape), vp, vp, vp, ctypes.c_int]
+        lib.dcn_oracle_coords.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Problem size: x [B,H,W,C] NHWC, weight [O,C,kh,kw], padding (ph, pw)."""
+    B: int
+    C: int
+    H: int
+    W: int
+    O: int
+    kh: int
+    kw: int
+    ph: int
+    pw: int
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    @property
+    def Ho(self) -> int:
+        return self.H + 2 * self.ph - self.kh + 1
+
+    @property
+    def Wo(self) -> int:
+        return self.W + 2 * self.pw - self.kw + 1
+
+    def _c(self) -> _Shape:
+        return _Shape(self.B, self.C, self.H, self.W, self.O, self.kh, self.kw, self.ph, self.pw)
+
+
+def _f32(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(shape: Shape, x, offset, mask, weight, bias, pixels=None, nthreads: int = 0,
+            with_norm: bool = True):
+    """Oracle forward.
+
+    Returns ``(out, norm)`` as float64 arrays of shape [npix, O] (pixel-major;
+    ``pixels`` are linear ids ``(b*Ho + ho)*Wo + wo``; None = all pixels in
+    order).  ``norm`` = sum over (tap, channel) of |weight|*|sample|, the
+    normaliser of the parity tolerance; None when ``with_norm`` is False.
+    """
+    s = shape
+    x, offset, mask, weight, bias = (_f32(a) for a in (x, offset, mask, weight, bias))
+    assert x.shape == (s.B, s.H, s.W, s.C), x.shape
+    assert offset.shape == (s.B, 2 * s.K, s.Ho, s.Wo), offset.shape
+    assert mask is None or mask.shape == (s.B, s.K, s.Ho, s.Wo), mask.shape
+    assert weight.shape == (s.O, s.C, s.kh, s.kw), weight.shape
+    assert bias is None or bias.shape == (s.O,), bias.shape
+    if pixels is None:
+        npix = s.B * s.Ho * s.Wo
+        pix = None
+    else:
+        pix = np.ascontiguousarray(pixels, dtype=np.int64)
+        npix = int(pix.size)
+    out = np.empty((npix, s.O), dtype=np.float64)
+    norm = np.empty((npix, s.O), dtype=np.float64) if with_norm else None
+    cs = s._c()
+    rc = _load().dcn_oracle_forward(ctypes.byref(cs), _ptr(x), _ptr(offset), _ptr(mask),
+                                    _ptr(weight), _ptr(bias), _ptr(pix), npix, _ptr(out),
+                                    _ptr(norm), int(nthreads))
+    if rc != 0:
+        raise ValueError("dcn_oracle_forward failed with code %d" % rc)
+    return out, norm
+
+
+def forward_nchw(shape: Shape, x, offset, mask, weight, bias, nthreads: int = 0):
+    """Whole output as [B, O, Ho, Wo] float64, plus the normaliser in the same layout."""
+    s = shape
+    out, norm = forward(s, x, offset, mask, weight, bias, None, nthreads)
+    to = lambda a: a.reshape(s.B, s.Ho, s.Wo, s.O).transpose(0, 3, 1, 2).copy()
+    return to(out), to(norm)
+
+
+def coords(shape: Shape, offset, nthreads: int = 0):
+    """Sampling corners: ``(y0x0 [B,K,Ho,Wo,2] int32, valid4 [B,K,Ho,Wo] uint8)``."""
+    s = shape
+    offset = _f32(offset)
+    assert offset.shape == (s.B, 2 * s.K, s.Ho, s.Wo), offset.shape
+    y0x0 = np.empty((s.B, s.K, s.Ho, s.Wo, 2), dtype=np.int32)
+    valid4 = np.empty((s.B, s.K, s.Ho, s.Wo), dtype=np.uint8)
+    cs = s._c()
+    rc = _load().dcn_oracle_coords(ctypes.byref(cs), _ptr(offset), _ptr(y0x0), _ptr(valid4),
+                                   int(nthreads))
+    if rc != 0:
+        raise ValueError("dcn_oracle_coords failed with code %d" % rc)
+    return y0x0, valid4

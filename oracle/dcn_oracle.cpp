@@ -1,0 +1,219 @@
+// dcn_oracle.cpp -- CPU oracle for the modulated deformable conv2d forward.
+//
+// TEST INFRASTRUCTURE ONLY (see dcn_oracle.h).  A plain loop nest written
+// from the operator's definition on page 1 ("deform_conv.py", module
+// docstring and deform_conv2d_gather): no SIMD intrinsics, no BLAS, no
+// blocking.  Build: g++ -O2 -std=c++17 -ffp-contract=off -shared -fPIC.
+//
+// Each step below names the part of that page it follows.
+
+#include "dcn_oracle.h"
+
+#include <cmath>
+#include <cstdlib>
+#include <thread>
+#include <vector>
+
+namespace {
+
+struct Dims {
+  int64_t B, C, H, W, O, kh, kw, ph, pw, K, Ho, Wo;
+};
+
+bool make_dims(const dcn_oracle_shape* s, Dims* d) {
+  d->B = s->batch; d->C = s->in_ch; d->H = s->height; d->W = s->width;
+  d->O = s->out_ch; d->kh = s->kernel_h; d->kw = s->kernel_w;
+  d->ph = s->pad_h; d->pw = s->pad_w;
+  if (d->B < 0 || d->C <= 0 || d->H <= 0 || d->W <= 0 || d->O <= 0 || d->kh <= 0 ||
+      d->kw <= 0 || d->ph < 0 || d->pw < 0)
+    return false;
+  d->K = d->kh * d->kw;
+  // Output size for stride 1, dilation 1 (page 1: wo = w + 2*pw - kw + 1;
+  // the row count follows the same rule).
+  d->Ho = d->H + 2 * d->ph - d->kh + 1;
+  d->Wo = d->W + 2 * d->pw - d->kw + 1;
+  return d->Ho > 0 && d->Wo > 0;
+}
+
+// The sampling point of tap (i, j) at output (ho, wo), page 1: the base grid
+// (ho - pad + i) is an exact integer in the input dtype, then ONE fp32 add of
+// the learned offset; floor and fraction are fp32 too.  `volatile` keeps the
+// compiler from forming anything but the single rounded add.
+struct Coord {
+  float y0, x0, ly, lx;
+};
+
+Coord tap_coord(const Dims& d, int64_t ho, int64_t wo, int64_t i, int64_t j, float dy,
+                float dx) {
+  volatile float gy = static_cast<float>(ho - d.ph + i);
+  volatile float gx = static_cast<float>(wo - d.pw + j);
+  volatile float py = gy + dy;
+  volatile float px = gx + dx;
+  Coord c;
+  c.y0 = std::floor(static_cast<float>(py));
+  c.x0 = std::floor(static_cast<float>(px));
+  volatile float ly = py - c.y0;
+  volatile float lx = px - c.x0;
+  c.ly = ly;
+  c.lx = lx;
+  return c;
+}
+
+// Corner (a, b) of the 2x2 neighbourhood is inside the image exactly when
+// 0 <= y0+a <= H-1 and 0 <= x0+b <= W-1 (page 1, the `valid` comparison);
+// compared in float so that no integer conversion of a far-away point is
+// needed.
+bool corner_valid(const Dims& d, float y0, float x0, int a, int b) {
+  volatile float yy = y0 + static_cast<float>(a);
+  volatile float xx = x0 + static_cast<float>(b);
+  return yy >= 0.0f && yy <= static_cast<float>(d.H - 1) && xx >= 0.0f &&
+         xx <= static_cast<float>(d.W - 1);
+}
+
+void forward_pixel(const Dims& d, const float* x, const float* offset, const float* mask,
+                   const float* weight, const float* bias, int64_t p, double* out_row,
+                   double* norm_row, std::vector<double>& s) {
+  const int64_t hw = d.Ho * d.Wo;
+  const int64_t b = p / hw;
+  const int64_t ho = (p % hw) / d.Wo;
+  const int64_t wo = p % d.Wo;
+
+  // s[k][c]: the modulated bilinear sample of channel c at tap k -- one row
+  // of page 1's column matrix `cols`, whose column index is (tap, channel).
+  for (int64_t k = 0; k < d.K; ++k) {
+    // Tap order k = i*kw + j (page 1: ki = arange(kh).repeat_interleave(kw),
+    // kj = arange(kw).repeat(kh)).
+    const int64_t i = k / d.kw;
+    const int64_t j = k % d.kw;
+    // offset viewed as [B, K, 2, Ho, Wo]: row offset first, then column
+    // offset (page 1: off[:, :, 0] feeds py, off[:, :, 1] feeds px).
+    const float dy = offset[((b * 2 * d.K + 2 * k) * d.Ho + ho) * d.Wo + wo];
+    const float dx = offset[((b * 2 * d.K + 2 * k + 1) * d.Ho + ho) * d.Wo + wo];
+    const double m = mask ? static_cast<double>(mask[((b * d.K + k) * d.Ho + ho) * d.Wo + wo])
+                          : 1.0;
+    const Coord cd = tap_coord(d, ho, wo, i, j, dy, dx);
+    const double ly = cd.ly, lx = cd.lx;
+    // The four bilinear weights of corners (0,0), (0,1), (1,0), (1,1)
+    // (page 1, the (dy, dx, wgt) tuple list).
+    const double wgt[2][2] = {{(1.0 - ly) * (1.0 - lx), (1.0 - ly) * lx},
+                              {ly * (1.0 - lx), ly * lx}};
+    double* sk = &s[k * d.C];
+    for (int64_t c = 0; c < d.C; ++c) sk[c] = 0.0;
+    for (int a = 0; a < 2; ++a) {
+      for (int bb = 0; bb < 2; ++bb) {
+        if (!corner_valid(d, cd.y0, cd.x0, a, bb)) continue;  // outside counts as 0
+        const int64_t yy = static_cast<int64_t>(cd.y0) + a;
+        const int64_t xx = static_cast<int64_t>(cd.x0) + bb;
+        const float* v = &x[((b * d.H + yy) * d.W + xx) * d.C];
+        for (int64_t c = 0; c < d.C; ++c) sk[c] += wgt[a][bb] * static_cast<double>(v[c]);
+      }
+    }
+    // Modulation: the blended sample times mask_k (page 1 multiplies each
+    // corner term by msk; doing it once after the sum is the same value).
+    for (int64_t c = 0; c < d.C; ++c) sk[c] *= m;
+  }
+
+  // Contraction over (tap, channel) with weight[o, c, i, j] (page 1:
+  // wmat = weight.permute(2, 3, 1, 0) -> rows (i, j, c); cols @ wmat), then
+  // the bias (page 1: out + bias.view(1, o, 1, 1)).
+  for (int64_t o = 0; o < d.O; ++o) {
+    double acc = 0.0, nrm = 0.0;
+    for (int64_t k = 0; k < d.K; ++k) {
+      const int64_t i = k / d.kw;
+      const int64_t j = k % d.kw;
+      const double* sk = &s[k * d.C];
+      for (int64_t c = 0; c < d.C; ++c) {
+        const double w = weight[((o * d.C + c) * d.kh + i) * d.kw + j];
+        acc += w * sk[c];
+        nrm += std::fabs(w) * std::fabs(sk[c]);
+      }
+    }
+    out_row[o] = acc + (bias ? static_cast<double>(bias[o]) : 0.0);
+    if (norm_row) norm_row[o] = nrm;
+  }
+}
+
+// Float -> int32 that saturates instead of overflowing (only the far-away
+// corners of huge offsets ever reach the limits; they are invalid anyway).
+int32_t to_i32_sat(float v) {
+  if (v >= 2147483648.0f) return 2147483647;
+  if (v < -2147483648.0f) return -2147483647 - 1;
+  return static_cast<int32_t>(v);
+}
+
+int resolve_threads(int nthreads, int64_t work) {
+  int n = nthreads > 0 ? nthreads : static_cast<int>(std::thread::hardware_concurrency());
+  if (n < 1) n = 1;
+  if (work < n) n = static_cast<int>(work > 0 ? work : 1);
+  return n;
+}
+
+}  // namespace
+
+extern "C" int dcn_oracle_forward(const dcn_oracle_shape* s, const float* x,
+                                  const float* offset, const float* mask, const float* weight,
+                                  const float* bias, const int64_t* pixels, int64_t npixels,
+                                  double* out, double* norm, int nthreads) {
+  if (!s || !offset || !weight || !out) return 1;
+  Dims d;
+  if (!make_dims(s, &d)) return 2;
+  const int64_t total = d.B * d.Ho * d.Wo;
+  if (npixels < 0) return 2;
+  if (!pixels && npixels != total) return 2;
+  if (npixels > 0 && !x) return 1;
+  if (pixels) {
+    for (int64_t n = 0; n < npixels; ++n)
+      if (pixels[n] < 0 || pixels[n] >= total) return 2;
+  }
+  const int nt = resolve_threads(nthreads, npixels);
+  std::vector<std::thread> pool;
+  // Static interleaved split over the pixel list; each pixel is computed by
+  // one thread start to finish, so the thread count changes no result.
+  for (int t = 0; t < nt; ++t) {
+    pool.emplace_back([&, t]() {
+      std::vector<double> sbuf(static_cast<size_t>(d.K * d.C));
+      for (int64_t n = t; n < npixels; n += nt) {
+        const int64_t p = pixels ? pixels[n] : n;
+        forward_pixel(d, x, offset, mask, weight, bias, p, out + n * d.O,
+                      norm ? norm + n * d.O : nullptr, sbuf);
+      }
+    });
+  }
+  for (auto& th : pool) th.join();
+  return 0;
+}
+
+extern "C" int dcn_oracle_coords(const dcn_oracle_shape* s, const float* offset,
+                                 int32_t* y0x0, uint8_t* valid4, int nthreads) {
+  if (!s || !offset || !y0x0 || !valid4) return 1;
+  Dims d;
+  if (!make_dims(s, &d)) return 2;
+  const int64_t rows = d.B * d.K * d.Ho;  // one work item per (b, k, ho) row
+  const int nt = resolve_threads(nthreads, rows);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t) {
+    pool.emplace_back([&, t]() {
+      for (int64_t r = t; r < rows; r += nt) {
+        const int64_t b = r / (d.K * d.Ho);
+        const int64_t k = (r / d.Ho) % d.K;
+        const int64_t ho = r % d.Ho;
+        const int64_t i = k / d.kw, j = k % d.kw;
+        for (int64_t wo = 0; wo < d.Wo; ++wo) {
+          const float dy = offset[((b * 2 * d.K + 2 * k) * d.Ho + ho) * d.Wo + wo];
+          const float dx = offset[((b * 2 * d.K + 2 * k + 1) * d.Ho + ho) * d.Wo + wo];
+          const Coord cd = tap_coord(d, ho, wo, i, j, dy, dx);
+          const int64_t e = ((b * d.K + k) * d.Ho + ho) * d.Wo + wo;
+          y0x0[2 * e] = to_i32_sat(cd.y0);
+          y0x0[2 * e + 1] = to_i32_sat(cd.x0);
+          uint8_t v = 0;
+          for (int a = 0; a < 2; ++a)
+            for (int bb = 0; bb < 2; ++bb)
+              if (corner_valid(d, cd.y0, cd.x0, a, bb)) v |= static_cast<uint8_t>(1u << (2 * a + bb));
+          valid4[e] = v;
+        }
+      }
+    });
+  }
+  for (auto& th : pool) th.join();
+  return 0;
+}

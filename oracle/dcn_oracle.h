@@ -1,0 +1,75 @@
+/*
+ * dcn_oracle.h -- CPU oracle for the modulated deformable 2-D convolution
+ * forward (DCNv2; stride 1, dilation 1, one offset group, groups = 1).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, obviously correct
+ * definition that the GPU path is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It
+ * shares no code, header, table or helper with the GPU library.
+ *
+ * What it computes is the operator as page 1 ("deform_conv.py", litert-
+ * community/Idol; module docstring and the body of deform_conv2d_gather)
+ * states it: for output pixel (h, w) and tap k = (i, j), k = i*kw + j,
+ * sample the input bilinearly at (h - pad_h + i + dy_k, w - pad_w + j + dx_k),
+ * corners outside the image count as zero, multiply by mask_k, contract over
+ * (tap, channel) with weight[o, c, i, j], add bias[o].
+ *
+ * Precision: the sampling coordinate and its floor/fraction are formed in
+ * fp32 (page 1 builds them in the input dtype: an exact integer grid plus
+ * one add of the offset); everything after that (bilinear weights, blend,
+ * contraction, bias) is fp64.
+ *
+ * Layouts (all dense, row-major, no padding):
+ *   x      [B, H, W, C]       token-major NHWC (page 1, "token-major input")
+ *   offset [B, 2K, Ho, Wo]    channel 2k = dy (row), 2k+1 = dx (column)
+ *   mask   [B, K, Ho, Wo]     NULL means all ones (v1 deformable conv)
+ *   weight [O, C, kh, kw]
+ *   bias   [O]                NULL means zero
+ * with Ho = H + 2*pad_h - kh + 1, Wo = W + 2*pad_w - kw + 1.
+ */
+#ifndef DCN_ORACLE_H
+#define DCN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int64_t batch, in_ch, height, width;
+  int64_t out_ch, kernel_h, kernel_w;
+  int64_t pad_h, pad_w;
+} dcn_oracle_shape;
+
+/* Return codes: 0 ok, 1 null pointer, 2 bad shape. */
+
+/*
+ * Forward on a list of output pixels.
+ *   pixels  linear pixel ids p = (b*Ho + ho)*Wo + wo, or NULL for all B*Ho*Wo
+ *           pixels in order (then npixels must equal B*Ho*Wo).
+ *   out     [npixels, O] fp64: bias[o] + sum_k sum_c weight[o,c,i_k,j_k]*s[k][c]
+ *   norm    [npixels, O] fp64 (may be NULL): sum_k sum_c |weight| * |s[k][c]|,
+ *           the error normaliser (it excludes the bias).
+ *   nthreads <= 0 means std::thread::hardware_concurrency().
+ * Every element's arithmetic is independent of the thread count.
+ */
+int dcn_oracle_forward(const dcn_oracle_shape* s, const float* x, const float* offset,
+                       const float* mask, const float* weight, const float* bias,
+                       const int64_t* pixels, int64_t npixels, double* out, double* norm,
+                       int nthreads);
+
+/*
+ * Sampling corners alone, for every (b, k, ho, wo):
+ *   y0x0   [B, K, Ho, Wo, 2] int32: floor of the fp32 sampling row / column
+ *          (defined when |floor| < 2^31)
+ *   valid4 [B, K, Ho, Wo] uint8: bit (2a + b) set when corner (y0+a, x0+b)
+ *          lies inside the image.
+ */
+int dcn_oracle_coords(const dcn_oracle_shape* s, const float* offset, int32_t* y0x0,
+                      uint8_t* valid4, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,30 @@
+"""Shared pytest set-up: repo root on sys.path, the ``gpu`` marker, helpers.
+
+Tests marked ``gpu`` need an MI355X; everything else runs on a CPU-only host.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def read_golden(name):
+    """Parse a ``key value value ...`` fixture under tests/golden/ (``#`` = comment)."""
+    path = os.path.join(ROOT, "tests", "golden", name)
+    out = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            out[key] = [float(v) for v in vals]
+    return out
