@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Throughput of the modulated deformable conv2d forward on one MI355X.
+
+One step = the whole forward over one batch of synthetic input already
+resident in HBM: dcn_forward = weight-pack kernel + fused sample-and-contract
+kernel, both launched through the C ABI on torch's current stream.
+
+Prints ONE JSON line: output pixels/s (``value``), effective TFLOP/s
+(2 * P * O * K * C per step), the fused kernel's roofline fraction against the
+dense fp32 (or bf16) MFMA peak, and the CPU oracle timed on this host on a
+bounded sample of the same workload.
+
+Default workload: the BiRefNet-decoder-like 7x7, 64-channel deformable conv at
+1024 input (256x256 map, fp32).  ``--workload`` picks another; ``--gpus`` > 1
+is refused (this path runs on one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "deform-conv output pixels/s + effective TFLOP/s and % roofline, 256^2x64ch 7x7"
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("modulated_deformable_convolution_dcn_amd/csrc/dcn_kernels.hip",
+                  "modulated_deformable_convolution_dcn_amd/csrc/dcn_device.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per fused launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "fused_kernel_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(spec, d, seconds: float):
+    """The oracle (as it stands) on evenly spaced output pixels of the workload."""
+    import numpy as np
+    import oracle
+    s = oracle.Shape(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    P = spec.pixels
+    args = (d["x"], d["offset"], d["mask"], d["weight"], d["bias"])
+    probe = np.linspace(0, P - 1, num=min(P, 512)).astype(np.int64)
+    t = time.perf_counter()
+    oracle.forward(s, *args, pixels=probe, nthreads=cores, with_norm=False)
+    rate = probe.size / max(time.perf_counter() - t, 1e-6)
+    n = int(min(P, max(probe.size, rate * seconds)))
+    pix = np.linspace(0, P - 1, num=n).astype(np.int64)
+    t = time.perf_counter()
+    oracle.forward(s, *args, pixels=pix, nthreads=cores, with_norm=False)
+    dt = time.perf_counter() - t
+    return {"value": n / dt, "unit": "px/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d output pixels (evenly spaced, all %d output channels), %.1f s"
+                      % (n, P, spec.O, dt)}
+
+
+def copy_calibration(mib: int, reps: int) -> None:
+    """A plain device-to-device copy of known size, for scaling PMC byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="birefnet1024_fp32")
+    ap.add_argument("--layout", default="nchw", choices=["nchw", "nhwc"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the deformable-conv forward on one GPU only; "
+              "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, max(1, args.steps))
+        return 0
+
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan, synth
+
+    spec = synth.WORKLOADS[args.workload]
+    d = synth.make_inputs(spec)
+    dev = {}
+    for k in ("x", "offset", "mask", "weight", "bias"):
+        v = d[k]
+        if v is None:
+            dev[k] = None
+        elif spec.dtype == "f32":
+            dev[k] = torch.from_numpy(v).cuda()
+        else:
+            dev[k] = torch.from_numpy(d["bits"][k].astype("int16")).cuda().view(torch.bfloat16)
+    plan = Plan(Desc(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw,
+                     spec.dtype, args.layout))
+    ws = plan.new_workspace()
+    out = plan.new_output()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        plan.pack_weight(dev["weight"], ws)
+        if ev is not None:
+            ev[1].record()
+        plan.forward_packed(dev["x"], dev["offset"], dev["mask"], ws, dev["bias"], out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    fused_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    P = spec.pixels
+    flops = spec.gemm_flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[spec.dtype]
+    fused_tflops = flops / (fused_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": P / (ms_per_step * 1e-3),
+        "unit": "px/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "C": spec.C, "O": spec.O, "H": spec.H,
+                   "W": spec.W, "kernel": "%dx%d" % (spec.kh, spec.kw),
+                   "pad": [spec.ph, spec.pw], "out_layout": args.layout,
+                   "input_layout": "nhwc"},
+        "tflops": tflops,
+        "pct_roofline": 100.0 * tflops / peak,
+        "roofline": {"bound": "mfma", "achieved": fused_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": fused_tflops / peak,
+                     "traffic": measured_traffic(spec.name)},
+        "kernels_us": {"fused": fused_ms * 1e3, "pack": pack_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(spec, d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

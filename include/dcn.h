@@ -1,0 +1,155 @@
+/*
+ * dcn.h -- C ABI of the MI355X (gfx950) modulated deformable conv2d forward.
+ *
+ * The operation (page 1, "deform_conv.py", litert-community/Idol: module
+ * docstring and deform_conv2d_gather; page 5, deformops README, section
+ * "Deformable convolution"): for every output pixel (h, w) and kernel tap
+ * k = (i, j), k = i*kw + j, sample the input bilinearly at
+ *     (h - pad_h + i + dy_k,  w - pad_w + j + dx_k),
+ * with each of the four neighbouring corners that lies outside the image
+ * counting as zero; multiply the sample by mask_k; contract over
+ * (tap, channel) with weight[o, c, i, j]; add bias[o].  Stride 1,
+ * dilation 1, one offset group, groups = 1.  A NULL mask is the unmodulated
+ * (v1) operator, i.e. mask = 1 (page 5 "v2 with a mask and v1 without").
+ *
+ * Layouts (dense, row-major, no padding or strides):
+ *   x      [B, H, W, C]       NHWC, "token-major": row (b, y, x) holds the C
+ *                             channels of one pixel (page 1 builds exactly
+ *                             this token table before gathering)
+ *   offset [B, 2K, Ho, Wo]    channel 2k = dy (row), 2k+1 = dx (column) of
+ *                             tap k (page 1 views it as [B, K, 2, Ho, Wo])
+ *   mask   [B, K, Ho, Wo]     or NULL
+ *   weight [O, C, kh, kw]     the usual conv weight
+ *   bias   [O]                or NULL (zero)
+ *   out    [B, O, Ho, Wo] (DCN_OUT_NCHW) or [B, Ho, Wo, O] (DCN_OUT_NHWC)
+ * with Ho = H + 2*pad_h - kh + 1 and Wo = W + 2*pad_w - kw + 1.
+ * x, offset, mask, weight and bias all have the plan's in_dtype; out is fp32.
+ * Accumulation is fp32 for every dtype (page 5: float32 accumulation, no
+ * TF32-style reduced-precision contraction).
+ *
+ * Memory: every pointer passed to a dcn_* call that takes a stream is a
+ * DEVICE pointer (hipMalloc / torch CUDA tensor) on the current device, and
+ * must be 16-byte aligned.  The caller owns all device memory, including the
+ * workspace; the library never allocates or frees device memory and never
+ * synchronises.  A plan owns only host memory and is immutable after
+ * dcn_create, so one plan may be used from several threads at once.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
+ * Calls are asynchronous on that stream; device-side faults surface at the
+ * caller's next synchronisation, as for any HIP launch.
+ *
+ * Errors: every call returns a dcn_status; no C++ exception crosses the ABI.
+ * Descriptor problems are reported by dcn_create; pointer problems by the
+ * call that receives the pointer.  dcn_last_error() gives a message for the
+ * most recent failure on the calling thread.
+ */
+#ifndef DCN_H
+#define DCN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dcn_plan_s* dcn_plan;
+
+typedef enum {
+  DCN_OK = 0,
+  DCN_E_NULL = 1,        /* a required pointer is NULL                     */
+  DCN_E_SHAPE = 2,       /* sizes out of range, Ho or Wo <= 0, overflow     */
+  DCN_E_DTYPE = 3,       /* unknown dtype / layout value                    */
+  DCN_E_UNSUPPORTED = 4, /* valid operator, but outside this build's limits */
+  DCN_E_ALIGN = 5,       /* a device pointer is not 16-byte aligned         */
+  DCN_E_HIP = 6,         /* a HIP runtime call or kernel launch failed      */
+  DCN_E_INTERNAL = 7,    /* unexpected host-side failure                    */
+  DCN_E_WORKSPACE = 8    /* workspace NULL or smaller than required         */
+} dcn_status;
+
+typedef enum { DCN_F32 = 0, DCN_BF16 = 1 } dcn_dtype;
+typedef enum { DCN_OUT_NCHW = 0, DCN_OUT_NHWC = 1 } dcn_layout;
+
+/*
+ * Problem descriptor.  Limits of this build (DCN_E_UNSUPPORTED otherwise):
+ *   in_ch  a multiple of 4 (fp32) or 8 (bf16): each pixel's channel vector is
+ *          fetched with 16-byte loads
+ *   the bytes of x, and B*O*Ho*Wo*4, below 2^31
+ *   out_dtype DCN_F32
+ * Any kernel_h, kernel_w >= 1 and pad >= 0 with Ho, Wo >= 1 is accepted.
+ */
+typedef struct {
+  int32_t batch;      /* B                                   */
+  int32_t in_ch;      /* C                                   */
+  int32_t height;     /* H                                   */
+  int32_t width;      /* W                                   */
+  int32_t out_ch;     /* O                                   */
+  int32_t kernel_h;   /* kh                                  */
+  int32_t kernel_w;   /* kw                                  */
+  int32_t pad_h;      /* ph (zero padding of the grid, rows)  */
+  int32_t pad_w;      /* pw                                  */
+  int32_t in_dtype;   /* dcn_dtype of x/offset/mask/weight/bias */
+  int32_t out_dtype;  /* dcn_dtype of out: DCN_F32            */
+  int32_t out_layout; /* dcn_layout                           */
+} dcn_desc;
+
+/* Validate `desc` and build a plan (host memory only).  *plan is set to NULL
+ * on failure.  Does not touch the GPU. */
+dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan);
+
+/* Free a plan.  NULL is accepted and ignored. */
+dcn_status dcn_destroy(dcn_plan plan);
+
+/* Output size of a plan: Ho, Wo (either pointer may be NULL). */
+dcn_status dcn_output_size(dcn_plan plan, int32_t* ho, int32_t* wo);
+
+/* Bytes of device workspace dcn_forward needs: the weight repacked as
+ * [tap][channel block][out channel] tiles (page 1 reorders the weight to
+ * rows (i, j, c), columns o before its one matmul), zero-padded to the
+ * kernel's tile sizes. */
+dcn_status dcn_workspace_bytes(dcn_plan plan, size_t* bytes);
+
+/* Repack `weight` [O, C, kh, kw] into `workspace` (device, >= the size
+ * dcn_workspace_bytes reports).  One kernel launch on `stream`.  Callers
+ * whose weight does not change may call this once and then reuse the
+ * packed workspace with dcn_forward_packed. */
+dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* The forward from an already packed weight: one fused kernel launch on
+ * `stream` (sampling point, bilinear gather and modulation into an on-chip
+ * column tile, MFMA contraction, bias epilogue).  `mask` and `bias` may be
+ * NULL.  `out` must not overlap any input. */
+dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset,
+                              const void* mask, const void* packed_weight,
+                              size_t workspace_bytes, const void* bias, void* out,
+                              void* stream);
+
+/* The whole forward: dcn_pack_weight then dcn_forward_packed, both on
+ * `stream`. */
+dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                       const void* weight, const void* bias, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Test hook, not on the timed path: the sampling-corner stage alone, from
+ * the same device function the fused kernel uses.  For every (b, k, ho, wo)
+ * it writes y0x0[2e], y0x0[2e+1] = floor of the fp32 sampling row / column
+ * (saturated to int32) and valid4[e] = bit (2a + b) set when corner
+ * (y0 + a, x0 + b) is inside the image, where e = ((b*K + k)*Ho + ho)*Wo + wo.
+ * Both are device buffers of B*K*Ho*Wo (x2 for y0x0) elements. */
+dcn_status dcn_debug_coords(dcn_plan plan, const void* offset, int32_t* y0x0, uint8_t* valid4,
+                            void* stream);
+
+/* Static string naming a status. */
+const char* dcn_status_string(dcn_status status);
+
+/* Message describing the most recent failing call on this thread ("" if none). */
+const char* dcn_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int32_t dcn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DCN_H */

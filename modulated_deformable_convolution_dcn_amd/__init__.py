@@ -1,1 +1,213 @@
-"""MI355X-native modulated deformable conv2d forward (DCNv2)."""
+"""MI355X-native modulated deformable conv2d forward (DCNv2, gfx950).
+
+The operator (page 1, "deform_conv.py": module docstring; page 5, deformops
+README, "Deformable convolution"): for each output pixel and kernel tap,
+sample the NHWC input bilinearly at the offset point (corners outside the
+image count as zero), multiply by the tap's mask, contract over
+(tap, channel) with the weight and add the bias.  Stride 1, dilation 1, one
+offset group.
+
+Everything is computed by the HIP kernels of ``libdcn_mi355x.so`` behind the C
+ABI of ``include/dcn.h``; this module only marshals torch tensors (device
+memory and the current stream) into those calls.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import DcnError  # noqa: F401
+
+__all__ = ["Plan", "deform_conv2d_nhwc", "DcnError"]
+
+_DTYPES = {"f32": _lib.DCN_F32, "bf16": _lib.DCN_BF16}
+_LAYOUTS = {"nchw": _lib.DCN_OUT_NCHW, "nhwc": _lib.DCN_OUT_NHWC}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass(frozen=True)
+class Desc:
+    batch: int
+    in_ch: int
+    height: int
+    width: int
+    out_ch: int
+    kernel_h: int
+    kernel_w: int
+    pad_h: int
+    pad_w: int
+    dtype: str = "f32"          # storage type of x, offset, mask, weight, bias
+    out_layout: str = "nchw"    # "nchw" -> [B,O,Ho,Wo], "nhwc" -> [B,Ho,Wo,O]; fp32
+
+
+class Plan:
+    """One validated problem size (``dcn_create``); reusable, immutable."""
+
+    def __init__(self, desc: Desc):
+        lib = _lib.load()
+        if desc.dtype not in _DTYPES:
+            raise ValueError("dtype must be one of %s" % list(_DTYPES))
+        if desc.out_layout not in _LAYOUTS:
+            raise ValueError("out_layout must be one of %s" % list(_LAYOUTS))
+        self.desc = desc
+        c = _lib.DcnDesc(desc.batch, desc.in_ch, desc.height, desc.width, desc.out_ch,
+                         desc.kernel_h, desc.kernel_w, desc.pad_h, desc.pad_w,
+                         _DTYPES[desc.dtype], _lib.DCN_F32, _LAYOUTS[desc.out_layout])
+        h = ctypes.c_void_p()
+        _lib.check(lib.dcn_create(ctypes.byref(c), ctypes.byref(h)), "dcn_create")
+        self._h = h
+        ho, wo = ctypes.c_int32(), ctypes.c_int32()
+        _lib.check(lib.dcn_output_size(h, ctypes.byref(ho), ctypes.byref(wo)), "dcn_output_size")
+        self.Ho, self.Wo = ho.value, wo.value
+        ws = ctypes.c_size_t()
+        _lib.check(lib.dcn_workspace_bytes(h, ctypes.byref(ws)), "dcn_workspace_bytes")
+        self.workspace_bytes = ws.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.load().dcn_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    # -- shapes -------------------------------------------------------------
+    @property
+    def K(self) -> int:
+        return self.desc.kernel_h * self.desc.kernel_w
+
+    def _torch_dtype(self):
+        torch = _torch()
+        return torch.float32 if self.desc.dtype == "f32" else torch.bfloat16
+
+    def out_shape(self):
+        d = self.desc
+        if d.out_layout == "nchw":
+            return (d.batch, d.out_ch, self.Ho, self.Wo)
+        return (d.batch, self.Ho, self.Wo, d.out_ch)
+
+    def _check(self, name, t, shape, dtype=None, optional=False):
+        if t is None:
+            if optional:
+                return
+            raise ValueError("%s is required" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        want = dtype if dtype is not None else self._torch_dtype()
+        if t.dtype != want:
+            raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, want))
+
+    def _check_inputs(self, x, offset, mask, bias):
+        d = self.desc
+        self._check("x", x, (d.batch, d.height, d.width, d.in_ch))
+        self._check("offset", offset, (d.batch, 2 * self.K, self.Ho, self.Wo))
+        self._check("mask", mask, (d.batch, self.K, self.Ho, self.Wo), optional=True)
+        self._check("bias", bias, (d.out_ch,), optional=True)
+
+    # -- calls --------------------------------------------------------------
+    def new_workspace(self):
+        torch = _torch()
+        return torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def new_output(self):
+        torch = _torch()
+        return torch.empty(self.out_shape(), dtype=torch.float32, device="cuda")
+
+    def pack_weight(self, weight, workspace=None, stream=None):
+        """``dcn_pack_weight``: weight [O,C,kh,kw] -> packed workspace (returned)."""
+        d = self.desc
+        self._check("weight", weight, (d.out_ch, d.in_ch, d.kernel_h, d.kernel_w))
+        ws = workspace if workspace is not None else self.new_workspace()
+        _lib.check(_lib.load().dcn_pack_weight(self._h, _ptr(weight), _ptr(ws), ws.numel(),
+                                               ctypes.c_void_p(_stream_handle(stream))),
+                   "dcn_pack_weight")
+        return ws
+
+    def forward_packed(self, x, offset, mask, packed, bias=None, out=None, stream=None):
+        """``dcn_forward_packed``: the fused forward from a packed weight."""
+        self._check_inputs(x, offset, mask, bias)
+        out = out if out is not None else self.new_output()
+        self._check("out", out, self.out_shape(), dtype=_torch().float32)
+        _lib.check(_lib.load().dcn_forward_packed(
+            self._h, _ptr(x), _ptr(offset), _ptr(mask), _ptr(packed), packed.numel(),
+            _ptr(bias), _ptr(out), ctypes.c_void_p(_stream_handle(stream))),
+            "dcn_forward_packed")
+        return out
+
+    def forward(self, x, offset, mask, weight, bias=None, out=None, workspace=None,
+                stream=None):
+        """``dcn_forward``: pack the weight and run the fused forward."""
+        d = self.desc
+        self._check_inputs(x, offset, mask, bias)
+        self._check("weight", weight, (d.out_ch, d.in_ch, d.kernel_h, d.kernel_w))
+        out = out if out is not None else self.new_output()
+        self._check("out", out, self.out_shape(), dtype=_torch().float32)
+        ws = workspace if workspace is not None else self.new_workspace()
+        _lib.check(_lib.load().dcn_forward(
+            self._h, _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(bias), _ptr(out),
+            _ptr(ws), ws.numel(), ctypes.c_void_p(_stream_handle(stream))), "dcn_forward")
+        return out
+
+    def debug_coords(self, offset, stream=None):
+        """``dcn_debug_coords``: (y0x0 [B,K,Ho,Wo,2] int32, valid4 [B,K,Ho,Wo] uint8)."""
+        torch = _torch()
+        d = self.desc
+        self._check("offset", offset, (d.batch, 2 * self.K, self.Ho, self.Wo))
+        y0x0 = torch.empty((d.batch, self.K, self.Ho, self.Wo, 2), dtype=torch.int32,
+                           device="cuda")
+        valid4 = torch.empty((d.batch, self.K, self.Ho, self.Wo), dtype=torch.uint8,
+                             device="cuda")
+        _lib.check(_lib.load().dcn_debug_coords(self._h, _ptr(offset), _ptr(y0x0), _ptr(valid4),
+                                                ctypes.c_void_p(_stream_handle(stream))),
+                   "dcn_debug_coords")
+        return y0x0, valid4
+
+
+_PLANS = {}
+
+
+def plan_for(desc: Desc) -> Plan:
+    p = _PLANS.get(desc)
+    if p is None:
+        p = Plan(desc)
+        _PLANS[desc] = p
+    return p
+
+
+def deform_conv2d_nhwc(x, offset, weight, bias=None, padding=0, mask=None, out_layout="nchw"):
+    """Modulated deformable conv2d on an NHWC input (stride 1, dilation 1).
+
+    x [B,H,W,C]; offset [B,2*kh*kw,Ho,Wo] (dy, dx per tap); mask [B,kh*kw,Ho,Wo]
+    or None; weight [O,C,kh,kw]; bias [O] or None; all float32 or all bfloat16
+    device tensors.  Returns fp32 [B,O,Ho,Wo] (``out_layout="nchw"``) or
+    [B,Ho,Wo,O] (``"nhwc"``).
+    """
+    torch = _torch()
+    ph, pw = (padding, padding) if isinstance(padding, int) else tuple(padding)
+    B, H, W, C = x.shape
+    O, _, kh, kw = weight.shape
+    dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(x.dtype)
+    if dtype is None:
+        raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
+    plan = plan_for(Desc(B, C, H, W, O, kh, kw, ph, pw, dtype, out_layout))
+    return plan.forward(x, offset, mask, weight, bias)

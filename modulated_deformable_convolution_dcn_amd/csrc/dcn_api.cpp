@@ -1,0 +1,289 @@
+// dcn_api.cpp -- C ABI of the gfx950 DCNv2 forward (declared in include/dcn.h).
+//
+// Host side only: descriptor validation, tile-configuration choice, pointer
+// checks and kernel launches on the caller's stream.  Nothing here allocates
+// device memory or synchronises.  Shapes are refused rather than guessed
+// (page 2, "patch_deform.py", refuses a rewrite it cannot prove in range;
+// page 5 names its errors instead of falling back silently).
+
+#include "dcn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "dcn_launch.h"
+
+struct dcn_plan_s {
+  dcn_desc d;
+  int K, Ho, Wo;
+  dcn::KernelConfig kc;
+  size_t ws_bytes;
+  uint32_t x_bytes;
+};
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dcn_status fail(dcn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dcn_status fail(dcn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dcn_status ok() {
+  g_last_error[0] = '\0';
+  return DCN_OK;
+}
+
+constexpr int64_t kLimit31 = int64_t(1) << 31;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile configuration for a validated descriptor.
+dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
+  dcn::KernelConfig kc{};
+  kc.bf16 = d.in_dtype == DCN_BF16;
+  kc.M = 64;
+  const int O = d.out_ch, C = d.in_ch;
+  kc.NO = O <= 16 ? 16 : O <= 64 ? 64 : O <= 128 ? 128 : 256;
+  if (kc.bf16) {
+    kc.CB = C <= 32 ? 32 : 64;
+  } else {
+    kc.CB = C <= 16 ? 16 : (kc.NO == 256 ? 32 : 64);
+  }
+  kc.nhwc = d.out_layout == DCN_OUT_NHWC;
+  kc.nchunk = (int)ceil_div(C, kc.CB);
+  kc.n_otiles = (int)ceil_div(O, kc.NO);
+  kc.tiles_per_img = (int)ceil_div(HoWo, kc.M);
+  return kc;
+}
+
+dcn_status hip_fail(hipError_t e, const char* what) {
+  return fail(DCN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dcn_version(void) { return 10000; }
+
+const char* dcn_status_string(dcn_status s) {
+  switch (s) {
+    case DCN_OK: return "DCN_OK";
+    case DCN_E_NULL: return "DCN_E_NULL: a required pointer is NULL";
+    case DCN_E_SHAPE: return "DCN_E_SHAPE: invalid sizes";
+    case DCN_E_DTYPE: return "DCN_E_DTYPE: unknown dtype or layout";
+    case DCN_E_UNSUPPORTED: return "DCN_E_UNSUPPORTED: outside this build's limits";
+    case DCN_E_ALIGN: return "DCN_E_ALIGN: misaligned device pointer";
+    case DCN_E_HIP: return "DCN_E_HIP: HIP runtime error";
+    case DCN_E_INTERNAL: return "DCN_E_INTERNAL: internal error";
+    case DCN_E_WORKSPACE: return "DCN_E_WORKSPACE: workspace missing or too small";
+  }
+  return "unknown dcn_status";
+}
+
+const char* dcn_last_error(void) { return g_last_error; }
+
+dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_create: plan output pointer is NULL");
+    *plan = nullptr;
+    if (!desc) return fail(DCN_E_NULL, "dcn_create: desc is NULL");
+    const dcn_desc& d = *desc;
+    if (d.in_dtype != DCN_F32 && d.in_dtype != DCN_BF16)
+      return fail(DCN_E_DTYPE, "in_dtype %d is not DCN_F32 or DCN_BF16", d.in_dtype);
+    if (d.out_dtype != DCN_F32 && d.out_dtype != DCN_BF16)
+      return fail(DCN_E_DTYPE, "out_dtype %d is not a dcn_dtype", d.out_dtype);
+    if (d.out_layout != DCN_OUT_NCHW && d.out_layout != DCN_OUT_NHWC)
+      return fail(DCN_E_DTYPE, "out_layout %d is not a dcn_layout", d.out_layout);
+    if (d.batch < 0 || d.in_ch < 1 || d.height < 1 || d.width < 1 || d.out_ch < 1 ||
+        d.kernel_h < 1 || d.kernel_w < 1 || d.pad_h < 0 || d.pad_w < 0)
+      return fail(DCN_E_SHAPE,
+                  "sizes must satisfy B>=0, C,H,W,O,kh,kw>=1, pad>=0 (got B=%d C=%d H=%d W=%d "
+                  "O=%d kh=%d kw=%d ph=%d pw=%d)",
+                  d.batch, d.in_ch, d.height, d.width, d.out_ch, d.kernel_h, d.kernel_w,
+                  d.pad_h, d.pad_w);
+    const int64_t Ho = (int64_t)d.height + 2 * (int64_t)d.pad_h - d.kernel_h + 1;
+    const int64_t Wo = (int64_t)d.width + 2 * (int64_t)d.pad_w - d.kernel_w + 1;
+    if (Ho < 1 || Wo < 1)
+      return fail(DCN_E_SHAPE, "output size %lld x %lld is empty (kernel larger than padded input)",
+                  (long long)Ho, (long long)Wo);
+    if (d.out_dtype != DCN_F32)
+      return fail(DCN_E_UNSUPPORTED, "only fp32 output is built (out_dtype=%d)", d.out_dtype);
+    const int64_t E = d.in_dtype == DCN_BF16 ? 2 : 4;
+    const int vec = (int)(16 / E);
+    if (d.in_ch % vec != 0)
+      return fail(DCN_E_UNSUPPORTED,
+                  "in_ch=%d must be a multiple of %d: channel vectors are fetched with 16-byte "
+                  "loads",
+                  d.in_ch, vec);
+    const int64_t K = (int64_t)d.kernel_h * d.kernel_w;
+    const int64_t HoWo = Ho * Wo;
+    const int64_t x_bytes = (int64_t)d.batch * d.height * d.width * d.in_ch * E;
+    if (x_bytes >= kLimit31 || (int64_t)d.height * d.width * d.in_ch * E >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "input is %lld bytes; this build addresses < 2^31",
+                  (long long)x_bytes);
+    if (K >= kLimit31 / 2 || HoWo >= kLimit31 ||
+        (int64_t)d.batch * 2 * K * HoWo >= kLimit31 ||
+        (int64_t)d.batch * d.out_ch * HoWo >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "offset/output element counts must stay below 2^31");
+
+    dcn::KernelConfig kc = choose_config(d, (int)HoWo);
+    if (!dcn::config_supported(kc))
+      return fail(DCN_E_INTERNAL, "no kernel variant for CB=%d NO=%d", kc.CB, kc.NO);
+    const int64_t wp = dcn::packed_weight_elems(kc, (int)K);
+    if (wp * E >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "packed weight of %lld bytes is too large",
+                  (long long)(wp * E));
+    if ((int64_t)d.batch * kc.tiles_per_img * kc.n_otiles >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "too many tiles");
+
+    dcn_plan p = new (std::nothrow) dcn_plan_s;
+    if (!p) return fail(DCN_E_INTERNAL, "out of host memory");
+    p->d = d;
+    p->K = (int)K;
+    p->Ho = (int)Ho;
+    p->Wo = (int)Wo;
+    p->kc = kc;
+    p->ws_bytes = (size_t)((wp * E + 255) / 256 * 256);
+    p->x_bytes = (uint32_t)x_bytes;
+    *plan = p;
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_create: unexpected exception");
+  }
+}
+
+dcn_status dcn_destroy(dcn_plan plan) {
+  delete plan;
+  return ok();
+}
+
+dcn_status dcn_output_size(dcn_plan plan, int32_t* ho, int32_t* wo) {
+  if (!plan) return fail(DCN_E_NULL, "dcn_output_size: plan is NULL");
+  if (ho) *ho = plan->Ho;
+  if (wo) *wo = plan->Wo;
+  return ok();
+}
+
+dcn_status dcn_workspace_bytes(dcn_plan plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(DCN_E_NULL, "dcn_workspace_bytes: NULL argument");
+  *bytes = plan->ws_bytes;
+  return ok();
+}
+
+dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_pack_weight: plan is NULL");
+    if (!weight) return fail(DCN_E_NULL, "dcn_pack_weight: weight is NULL");
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(DCN_E_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", plan->ws_bytes,
+                  workspace_bytes, workspace);
+    const size_t E = plan->kc.bf16 ? 2 : 4;
+    if (!aligned(weight, E)) return fail(DCN_E_ALIGN, "weight is not %zu-byte aligned", E);
+    if (!aligned(workspace, 16)) return fail(DCN_E_ALIGN, "workspace is not 16-byte aligned");
+    const dcn_desc& d = plan->d;
+    hipError_t e = dcn::launch_pack(plan->kc, weight, workspace, d.out_ch, d.in_ch, d.kernel_h,
+                                    d.kernel_w, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "weight pack launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_pack_weight: unexpected exception");
+  }
+}
+
+dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                              const void* packed_weight, size_t workspace_bytes,
+                              const void* bias, void* out, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_forward_packed: plan is NULL");
+    const dcn_desc& d = plan->d;
+    if (d.batch == 0) return ok();  // empty batch: nothing to read or write
+    if (!x || !offset || !out) return fail(DCN_E_NULL, "x, offset and out are required");
+    if (!packed_weight || workspace_bytes < plan->ws_bytes)
+      return fail(DCN_E_WORKSPACE, "packed weight needs %zu bytes, got %zu at %p",
+                  plan->ws_bytes, workspace_bytes, packed_weight);
+    const size_t E = plan->kc.bf16 ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(packed_weight, 16))
+      return fail(DCN_E_ALIGN, "x, out and the packed weight must be 16-byte aligned");
+    if (!aligned(offset, E) || (mask && !aligned(mask, E)) || (bias && !aligned(bias, E)))
+      return fail(DCN_E_ALIGN, "offset, mask and bias must be %zu-byte aligned", E);
+    dcn::FusedArgs a{};
+    a.x = x;
+    a.offset = offset;
+    a.mask = mask;
+    a.wpack = packed_weight;
+    a.bias = bias;
+    a.out = static_cast<float*>(out);
+    a.B = d.batch;
+    a.C = d.in_ch;
+    a.H = d.height;
+    a.W = d.width;
+    a.O = d.out_ch;
+    a.kh = d.kernel_h;
+    a.kw = d.kernel_w;
+    a.K = plan->K;
+    a.ph = d.pad_h;
+    a.pw = d.pad_w;
+    a.Ho = plan->Ho;
+    a.Wo = plan->Wo;
+    a.HoWo = plan->Ho * plan->Wo;
+    a.nchunk = plan->kc.nchunk;
+    a.n_otiles = plan->kc.n_otiles;
+    a.tiles_per_img = plan->kc.tiles_per_img;
+    a.x_bytes = plan->x_bytes;
+    a.vec_store = (a.HoWo % 4) == 0;
+    hipError_t e = dcn::launch_fused(plan->kc, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_forward_packed: unexpected exception");
+  }
+}
+
+dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                       const void* weight, const void* bias, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(DCN_E_NULL, "dcn_forward: plan is NULL");
+  if (plan->d.batch == 0) return ok();
+  dcn_status s = dcn_pack_weight(plan, weight, workspace, workspace_bytes, stream);
+  if (s != DCN_OK) return s;
+  return dcn_forward_packed(plan, x, offset, mask, workspace, workspace_bytes, bias, out,
+                            stream);
+}
+
+dcn_status dcn_debug_coords(dcn_plan plan, const void* offset, int32_t* y0x0, uint8_t* valid4,
+                            void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_debug_coords: plan is NULL");
+    const dcn_desc& d = plan->d;
+    if (d.batch == 0) return ok();
+    if (!offset || !y0x0 || !valid4)
+      return fail(DCN_E_NULL, "dcn_debug_coords: offset, y0x0 and valid4 are required");
+    const size_t E = plan->kc.bf16 ? 2 : 4;
+    if (!aligned(offset, E) || !aligned(y0x0, 4))
+      return fail(DCN_E_ALIGN, "dcn_debug_coords: misaligned pointer");
+    hipError_t e = dcn::launch_coords(plan->kc.bf16, offset, y0x0, valid4, d.batch, plan->K,
+                                      d.kernel_w, plan->Ho, plan->Wo, d.pad_h, d.pad_w,
+                                      d.height, d.width, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "coords launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_debug_coords: unexpected exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,532 @@
+// dcn_kernels.hip -- gfx950 kernels of the modulated deformable conv2d forward.
+//
+// The operator (page 1, "deform_conv.py": module docstring and
+// deform_conv2d_gather; page 5, deformops README, "Deformable convolution"):
+//   out[b,o,h,w] = bias[o] + sum_{k=(i,j)} sum_c weight[o,c,i,j] *
+//                  mask[b,k,h,w] * bilinear(x[b,:,:,c], h-ph+i+dy, w-pw+j+dx)
+// with corners outside the image counting as zero.
+//
+// Page 1 evaluates it as GATHER -> elementwise bilinear weights -> one matmul
+// over a materialised [pixels, taps*channels] column matrix; page 5 notes the
+// fused form in which that column matrix never exists.  Here one workgroup
+// owns M output pixels x NO output channels and walks the (tap, channel
+// block) axis.  Per step it:
+//   (a) forms the sampling point, the four corner weights (bilinear weight x
+//       validity x mask) and the four corner byte offsets for each of its M
+//       pixels once per tap (shared through LDS);
+//   (b) fetches each corner's 16-byte channel slice from the NHWC input with
+//       buffer loads (a corner outside the image is a load past the buffer's
+//       end, which returns zero without a memory access), blends the four
+//       corners in registers and writes the blended row into an LDS column
+//       tile [M x CB] -- the only place the column matrix ever exists;
+//   (c) contracts that tile against the matching [CB x NO] block of the
+//       packed weight with MFMA (fp32: v_mfma_f32_16x16x4_f32; bf16:
+//       v_mfma_f32_16x16x32_bf16, fp32 accumulate), while the next step's
+//       corner loads and weight block are already in flight;
+// and finally adds the bias and writes NCHW or NHWC fp32 output.
+
+#include "dcn_device.h"
+#include "dcn_launch.h"
+
+namespace dcn {
+
+// Per (pixel, tap): corner weights (bilinear x validity x mask) and byte
+// offsets of the four corners' channel vectors in x (kNoCorner if outside).
+struct alignas(16) Coef {
+  f32x4 w;
+  u32x4 off;
+};
+
+template <class T>
+struct Ops;
+
+template <>
+struct Ops<float> {
+  typedef f32x4 frag;
+  static constexpr int VEC = 4;
+  // blended = w0*c0 + w1*c1 + w2*c2 + w3*c3 on 4 fp32 channels
+  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
+                                                u32x4 c3) {
+    const f32x4 v0 = __builtin_bit_cast(f32x4, c0), v1 = __builtin_bit_cast(f32x4, c1);
+    const f32x4 v2 = __builtin_bit_cast(f32x4, c2), v3 = __builtin_bit_cast(f32x4, c3);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = w[0] * v0[e];
+      s = __builtin_fmaf(w[1], v1[e], s);
+      s = __builtin_fmaf(w[2], v2[e], s);
+      s = __builtin_fmaf(w[3], v3[e], s);
+      r[e] = s;
+    }
+    return __builtin_bit_cast(u32x4, r);
+  }
+};
+
+template <>
+struct Ops<__bf16> {
+  typedef bf16x8 frag;
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
+  __device__ static __forceinline__ float hi(uint32_t u) {
+    return __uint_as_float(u & 0xffff0000u);
+  }
+  // Blend 8 bf16 channels in fp32, round the result to bf16 (nearest-even).
+  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
+                                                u32x4 c3) {
+    bf16x8 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float sl = w[0] * lo(c0[q]);
+      sl = __builtin_fmaf(w[1], lo(c1[q]), sl);
+      sl = __builtin_fmaf(w[2], lo(c2[q]), sl);
+      sl = __builtin_fmaf(w[3], lo(c3[q]), sl);
+      float sh = w[0] * hi(c0[q]);
+      sh = __builtin_fmaf(w[1], hi(c1[q]), sh);
+      sh = __builtin_fmaf(w[2], hi(c2[q]), sh);
+      sh = __builtin_fmaf(w[3], hi(c3[q]), sh);
+      r[2 * q] = static_cast<__bf16>(sl);
+      r[2 * q + 1] = static_cast<__bf16>(sh);
+    }
+    return __builtin_bit_cast(u32x4, r);
+  }
+};
+
+// One 16-byte fragment read from LDS.
+template <class T>
+__device__ __forceinline__ u32x4 lds16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// XCD-aware block order: the dispatcher deals consecutive workgroup ids to
+// the 8 XCDs in turn, so logical tile t is given to hardware id
+// (t % per_xcd) * 8 + t / per_xcd -- each XCD then walks one contiguous run
+// of tiles and its private L2 holds one band of the input map.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+  const int full = (nblk / 8) * 8;
+  if (bid >= full) return bid;
+  const int per_xcd = full / 8;
+  return (bid % 8) * per_xcd + bid / 8;
+}
+
+template <class T, int M, int CB, int NO, int WM, int WN, bool NHWC>
+__global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
+  constexpr int E = sizeof(T);
+  constexpr int VEC = Ops<T>::VEC;       // elements per 16-byte fragment
+  constexpr int LPR = CB / VEC;          // lanes that gather one pixel's CB channels
+  constexpr int PPP = 256 / LPR;         // pixels per gather pass
+  constexpr int NPASS = M / PPP;         // gather passes per k-block
+  constexpr int AST = CB + VEC;          // LDS column-tile row stride (one pad fragment)
+  constexpr int A_ELEMS = M * AST;
+  constexpr int B_ELEMS = CB * NO;
+  constexpr int B_PIECES = B_ELEMS * E / 16;
+  constexpr int B_PER_T = (B_PIECES + 255) / 256;
+  constexpr int R = CB / 4 / VEC;        // fragment reads per k-slot group per k-block
+  constexpr int WROWS = M / WM, WCOLS = NO / WN;
+  constexpr int MT = WROWS / 16, NT = WCOLS / 16;
+  static_assert(LPR >= 1 && 256 % LPR == 0 && NPASS >= 1 && M % PPP == 0, "gather shape");
+  static_assert(R >= 1 && CB % (4 * VEC) == 0, "k-block shape");
+  static_assert(WM * WN == 4 && MT >= 1 && NT >= 1, "wave tiling");
+
+  __shared__ __attribute__((aligned(16))) T As[2][A_ELEMS];
+  __shared__ __attribute__((aligned(16))) T Bs[2][B_ELEMS];
+  __shared__ Coef Cs[2][M];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // ---- which tile: (image b, pixel tile, output-channel tile)
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int otile = logical % a.n_otiles;
+  const int t2 = logical / a.n_otiles;
+  const int tile = t2 % a.tiles_per_img;
+  const int b = t2 / a.tiles_per_img;
+  const int hw0 = tile * M;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const T* wtiles = static_cast<const T*>(a.wpack) +
+                    (size_t)otile * a.K * a.nchunk * B_ELEMS;
+  const T* offp = static_cast<const T*>(a.offset);
+  const T* maskp = static_cast<const T*>(a.mask);
+  const uint32_t row_bytes = (uint32_t)a.C * E;
+
+  // ---- (a) sampling point -> corner weights and offsets, one tap, M pixels
+  auto coef_stage = [&](int kt, int slot) {
+    const int i = kt / a.kw;
+    const int j = kt - i * a.kw;
+    for (int m = tid; m < M; m += 256) {
+      Coef cf;
+      cf.w = f32x4{0.f, 0.f, 0.f, 0.f};
+      cf.off = u32x4{kNoCorner, kNoCorner, kNoCorner, kNoCorner};
+      const int hw = hw0 + m;
+      if (hw < a.HoWo) {
+        const int ho = hw / a.Wo;
+        const int wo = hw - ho * a.Wo;
+        const size_t ob = (size_t)(b * 2 * a.K + 2 * kt) * a.HoWo + hw;
+        const float dy = to_f32<T>(offp[ob]);
+        const float dx = to_f32<T>(offp[ob + a.HoWo]);
+        const float mk =
+            maskp ? to_f32<T>(maskp[(size_t)(b * a.K + kt) * a.HoWo + hw]) : 1.0f;
+        const TapPoint t = tap_point(dy, dx, ho - a.ph + i, wo - a.pw + j, a.H, a.W);
+        const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
+        const float wv[4] = {hy * hx, hy * t.lx, t.ly * hx, t.ly * t.lx};
+        if (t.valid) {
+          const int y0 = (int)t.y0, x0 = (int)t.x0;  // in [-1, H-1] x [-1, W-1] here
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (t.valid & (1u << c)) {
+              const int yy = y0 + (c >> 1), xx = x0 + (c & 1);
+              cf.w[c] = wv[c] * mk;
+              cf.off[c] = (uint32_t)((b * a.H + yy) * a.W + xx) * row_bytes;
+            }
+          }
+        }
+      }
+      Cs[slot][m] = cf;
+    }
+  };
+
+  // ---- (b) corner loads for k-block kb into registers
+  const int li = tid % LPR;  // which 16-byte slice of the channel block
+  const int pr = tid / LPR;  // which pixel of the pass
+  u32x4 gv[NPASS][4];
+  f32x4 gw[NPASS];
+  auto issue_gather = [&](int kb) {
+    const int kt = kb / a.nchunk;
+    const int cc = kb - kt * a.nchunk;
+    const int ch = cc * CB + li * VEC;
+    const bool chan_ok = ch < a.C;
+    const uint32_t cbyte = (uint32_t)ch * E;
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const Coef& cf = Cs[kt & 1][ps * PPP + pr];
+      gw[ps] = cf.w;
+      const u32x4 off = cf.off;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        gv[ps][c] = load16(xr, chan_ok ? off[c] + cbyte : kNoCorner);
+    }
+  };
+  auto finish_gather = [&](T* A) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const u32x4 r = Ops<T>::blend(gw[ps], gv[ps][0], gv[ps][1], gv[ps][2], gv[ps][3]);
+      *reinterpret_cast<u32x4*>(&A[(ps * PPP + pr) * AST + li * VEC]) = r;
+    }
+  };
+
+  // ---- weight block kb (contiguous in the packed layout) into registers
+  u32x4 bq[B_PER_T];
+  auto issue_b = [&](int kb) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(wtiles + (size_t)kb * B_ELEMS);
+#pragma unroll
+    for (int r = 0; r < B_PER_T; ++r) {
+      const int idx = tid + r * 256;
+      if (B_PIECES % 256 == 0 || idx < B_PIECES) bq[r] = src[idx];
+    }
+  };
+  auto store_b = [&](T* Bt) {
+#pragma unroll
+    for (int r = 0; r < B_PER_T; ++r) {
+      const int idx = tid + r * 256;
+      if (B_PIECES % 256 == 0 || idx < B_PIECES) reinterpret_cast<u32x4*>(Bt)[idx] = bq[r];
+    }
+  };
+
+  // ---- (c) MFMA over one k-block.  Channel order inside the block: k-slot
+  // group g (lane / 16) owns channels [g*CB/4, (g+1)*CB/4); fragment read q
+  // of a lane holds channels g*CB/4 + q*VEC + [0, VEC).  The packed weight
+  // uses the same order, so any assignment is a permutation of the sum.
+  const int rl = lane & 15;
+  const int g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_block = [&](const T* A, const T* Bt) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      u32x4 af[MT], bf[NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = lds16(&A[(wm * WROWS + mt * 16 + rl) * AST + g * (CB / 4) + q * VEC]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bf[nt] = lds16(&Bt[((g * R + q) * NO + wn * WCOLS + nt * 16 + rl) * VEC]);
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                  __uint_as_float(af[mt][e]), __uint_as_float(bf[nt][e]), acc[mt][nt], 0, 0,
+                  0);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, af[mt]), __builtin_bit_cast(bf16x8, bf[nt]),
+                acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline over k-blocks (tap-major, channel chunk minor)
+  const int NKB = a.K * a.nchunk;
+  coef_stage(0, 0);
+  if (a.K > 1) coef_stage(1, 1);
+  __syncthreads();
+  issue_gather(0);
+  issue_b(0);
+  finish_gather(As[0]);
+  store_b(Bs[0]);
+
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int buf = kb & 1;
+    __syncthreads();  // block kb is in LDS; every wave is done with block kb-1
+    const bool has_next = kb + 1 < NKB;
+    if (has_next) {
+      issue_gather(kb + 1);
+      issue_b(kb + 1);
+      const int kt1 = (kb + 1) / a.nchunk;
+      if (kt1 * a.nchunk == kb + 1 && kt1 + 1 < a.K) coef_stage(kt1 + 1, (kt1 + 1) & 1);
+    }
+    mfma_block(As[buf], Bs[buf]);
+    if (has_next) {
+      finish_gather(As[buf ^ 1]);
+      store_b(Bs[buf ^ 1]);
+    }
+  }
+
+  // ---- epilogue: + bias, fp32 store.  MFMA 16x16 result layout: lane l,
+  // register r holds row 4*(l/16) + r, column l % 16.
+  const T* biasp = static_cast<const T*>(a.bias);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int o = otile * NO + wn * WCOLS + nt * 16 + rl;
+    if (o >= a.O) continue;
+    const float bo = biasp ? to_f32<T>(biasp[o]) : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int hw_r0 = hw0 + wm * WROWS + mt * 16 + g * 4;
+      f32x4 v = acc[mt][nt];
+      v += bo;
+      if constexpr (NHWC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (hw_r0 + r < a.HoWo) a.out[((size_t)b * a.HoWo + hw_r0 + r) * a.O + o] = v[r];
+      } else {
+        float* dst = a.out + ((size_t)b * a.O + o) * a.HoWo + hw_r0;
+        if (a.vec_store && hw_r0 + 3 < a.HoWo) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (hw_r0 + r < a.HoWo) dst[r] = v[r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- packing
+// wpack[otile][tap][chunk][CB/VEC][NO][VEC] = weight[o][c][i][j] with
+// o = otile*NO + n, c = chunk*CB + cg*VEC + v, tap = i*kw + j (zero-padded):
+// page 1 reorders the weight to rows (i, j, c) x columns o for its matmul;
+// this is that matrix cut into the kernel's [CB x NO] blocks, with each
+// lane's VEC consecutive channels contiguous.
+template <class T>
+__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* __restrict__ wp,
+                                                   int O, int C, int kh, int kw, int CB, int NO,
+                                                   int VEC, int nchunk, int64_t total) {
+  const int K = kh * kw;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    int64_t r = idx;
+    const int v = (int)(r % VEC);
+    r /= VEC;
+    const int n = (int)(r % NO);
+    r /= NO;
+    const int cg = (int)(r % (CB / VEC));
+    r /= (CB / VEC);
+    const int chunk = (int)(r % nchunk);
+    r /= nchunk;
+    const int tap = (int)(r % K);
+    const int otile = (int)(r / K);
+    const int o = otile * NO + n;
+    const int c = chunk * CB + cg * VEC + v;
+    const int i = tap / kw, j = tap % kw;
+    T val = static_cast<T>(0.0f);
+    if (o < O && c < C) val = w[(((int64_t)o * C + c) * kh + i) * kw + j];
+    wp[idx] = val;
+  }
+}
+
+// ---------------------------------------------------------------- corners
+template <class T>
+__global__ __launch_bounds__(256) void coords_kernel(const T* __restrict__ offset,
+                                                     int32_t* __restrict__ y0x0,
+                                                     uint8_t* __restrict__ valid4, int B, int K,
+                                                     int kw, int Ho, int Wo, int ph, int pw,
+                                                     int H, int W) {
+  const int HoWo = Ho * Wo;
+  const int64_t total = (int64_t)B * K * HoWo;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int hw = (int)(e % HoWo);
+    const int k = (int)((e / HoWo) % K);
+    const int b = (int)(e / ((int64_t)HoWo * K));
+    const int ho = hw / Wo, wo = hw % Wo;
+    const int i = k / kw, j = k % kw;
+    const int64_t ob = ((int64_t)b * 2 * K + 2 * k) * HoWo + hw;
+    const TapPoint t =
+        tap_point(to_f32<T>(offset[ob]), to_f32<T>(offset[ob + HoWo]), ho - ph + i, wo - pw + j,
+                  H, W);
+    y0x0[2 * e] = sat_i32(t.y0);
+    y0x0[2 * e + 1] = sat_i32(t.x0);
+    valid4[e] = (uint8_t)t.valid;
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+namespace {
+
+template <class T, int CB, int NO, bool NHWC>
+hipError_t launch_variant(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  constexpr int M = 64;
+  constexpr int WM = NO == 256 ? 1 : (NO == 128 ? 2 : 4);
+  constexpr int WN = 4 / WM;
+  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * kc.n_otiles;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fused_kernel<T, M, CB, NO, WM, WN, NHWC>), dim3((unsigned)nblk),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, int CB, bool NHWC>
+hipError_t launch_no(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  switch (kc.NO) {
+    case 16: return launch_variant<T, CB, 16, NHWC>(kc, a, s);
+    case 64: return launch_variant<T, CB, 64, NHWC>(kc, a, s);
+    case 128: return launch_variant<T, CB, 128, NHWC>(kc, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T, bool NHWC>
+hipError_t launch_cb(const KernelConfig& kc, const FusedArgs& a, hipStream_t s);
+
+template <>
+hipError_t launch_cb<float, false>(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.NO == 256) {
+    if (kc.CB == 16) return launch_variant<float, 16, 256, false>(kc, a, s);
+    if (kc.CB == 32) return launch_variant<float, 32, 256, false>(kc, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (kc.CB == 16) return launch_no<float, 16, false>(kc, a, s);
+  if (kc.CB == 64) return launch_no<float, 64, false>(kc, a, s);
+  return hipErrorInvalidValue;
+}
+template <>
+hipError_t launch_cb<float, true>(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.NO == 256) {
+    if (kc.CB == 16) return launch_variant<float, 16, 256, true>(kc, a, s);
+    if (kc.CB == 32) return launch_variant<float, 32, 256, true>(kc, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (kc.CB == 16) return launch_no<float, 16, true>(kc, a, s);
+  if (kc.CB == 64) return launch_no<float, 64, true>(kc, a, s);
+  return hipErrorInvalidValue;
+}
+template <>
+hipError_t launch_cb<__bf16, false>(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.NO == 256) {
+    if (kc.CB == 32) return launch_variant<__bf16, 32, 256, false>(kc, a, s);
+    if (kc.CB == 64) return launch_variant<__bf16, 64, 256, false>(kc, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (kc.CB == 32) return launch_no<__bf16, 32, false>(kc, a, s);
+  if (kc.CB == 64) return launch_no<__bf16, 64, false>(kc, a, s);
+  return hipErrorInvalidValue;
+}
+template <>
+hipError_t launch_cb<__bf16, true>(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.NO == 256) {
+    if (kc.CB == 32) return launch_variant<__bf16, 32, 256, true>(kc, a, s);
+    if (kc.CB == 64) return launch_variant<__bf16, 64, 256, true>(kc, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (kc.CB == 32) return launch_no<__bf16, 32, true>(kc, a, s);
+  if (kc.CB == 64) return launch_no<__bf16, 64, true>(kc, a, s);
+  return hipErrorInvalidValue;
+}
+
+unsigned grid_for(int64_t total) {
+  int64_t g = (total + 255) / 256;
+  if (g < 1) g = 1;
+  if (g > 65535) g = 65535;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+bool config_supported(const KernelConfig& kc) {
+  if (kc.M != 64) return false;
+  if (kc.NO != 16 && kc.NO != 64 && kc.NO != 128 && kc.NO != 256) return false;
+  if (kc.bf16) return kc.CB == 32 || kc.CB == 64;
+  if (kc.NO == 256) return kc.CB == 16 || kc.CB == 32;
+  return kc.CB == 16 || kc.CB == 64;
+}
+
+int64_t packed_weight_elems(const KernelConfig& kc, int K) {
+  return (int64_t)kc.n_otiles * K * kc.nchunk * kc.CB * kc.NO;
+}
+
+hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, int O, int C,
+                       int kh, int kw, hipStream_t s) {
+  const int64_t total = packed_weight_elems(kc, kh * kw);
+  if (kc.bf16) {
+    hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s,
+                       static_cast<const __bf16*>(weight), static_cast<__bf16*>(wpack), O, C,
+                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, total);
+  } else {
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
+                       static_cast<const float*>(weight), static_cast<float*>(wpack), O, C, kh,
+                       kw, kc.CB, kc.NO, 4, kc.nchunk, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.bf16) {
+    return kc.nhwc ? launch_cb<__bf16, true>(kc, a, s) : launch_cb<__bf16, false>(kc, a, s);
+  }
+  return kc.nhwc ? launch_cb<float, true>(kc, a, s) : launch_cb<float, false>(kc, a, s);
+}
+
+hipError_t launch_coords(int bf16, const void* offset, int32_t* y0x0, uint8_t* valid4, int B,
+                         int K, int kw, int Ho, int Wo, int ph, int pw, int H, int W,
+                         hipStream_t s) {
+  const int64_t total = (int64_t)B * K * Ho * Wo;
+  if (total <= 0) return hipSuccess;
+  if (bf16) {
+    hipLaunchKernelGGL(coords_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s,
+                       static_cast<const __bf16*>(offset), y0x0, valid4, B, K, kw, Ho, Wo, ph,
+                       pw, H, W);
+  } else {
+    hipLaunchKernelGGL(coords_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
+                       static_cast<const float*>(offset), y0x0, valid4, B, K, kw, Ho, Wo, ph,
+                       pw, H, W);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dcn

@@ -1,0 +1,51 @@
+// dcn_launch.h -- internal interface between the C ABI (dcn_api.cpp) and the
+// kernels (dcn_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace dcn {
+
+// Tile configuration chosen once per plan.
+struct KernelConfig {
+  int bf16;       // 0: fp32 operands, 1: bf16 operands
+  int M;          // output pixels per workgroup
+  int CB;         // channels per k-block (one tap, one channel chunk)
+  int NO;         // output channels per workgroup (padded)
+  int nhwc;       // output layout: 0 NCHW, 1 NHWC
+  int nchunk;     // ceil(C / CB)
+  int n_otiles;   // ceil(O / NO)
+  int tiles_per_img;  // ceil(Ho*Wo / M)
+};
+
+// Arguments of the fused forward kernel (passed by value).
+struct FusedArgs {
+  const void* x;       // [B,H,W,C] in_dtype
+  const void* offset;  // [B,2K,Ho,Wo] in_dtype
+  const void* mask;    // [B,K,Ho,Wo] in_dtype or nullptr
+  const void* wpack;   // packed weight (see dcn_pack_weight)
+  const void* bias;    // [O] in_dtype or nullptr
+  float* out;          // [B,O,Ho,Wo] or [B,Ho,Wo,O] fp32
+  int B, C, H, W, O, kh, kw, K, ph, pw, Ho, Wo, HoWo;
+  int nchunk, n_otiles, tiles_per_img;
+  uint32_t x_bytes;    // bytes of x (< 2^31)
+  int vec_store;       // NCHW: Ho*Wo % 4 == 0, so 4 consecutive pixels store as one 16-B write
+};
+
+// Kernel variants compiled into the library; false if none matches.
+bool config_supported(const KernelConfig& kc);
+
+// Elements (of the operand dtype) of the packed weight for `kc`, C/O/K sizes.
+int64_t packed_weight_elems(const KernelConfig& kc, int K);
+
+hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, int O, int C,
+                       int kh, int kw, hipStream_t stream);
+
+hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+
+hipError_t launch_coords(int bf16, const void* offset, int32_t* y0x0, uint8_t* valid4, int B,
+                         int K, int kw, int Ho, int Wo, int ph, int pw, int H, int W,
+                         hipStream_t stream);
+
+}  // namespace dcn

@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed: no compute call is made).
+
+The library must load and export every symbol ``include/dcn.h`` declares;
+``dcn_create`` must validate descriptors and refuse what this build cannot
+run (page 2, "patch_deform.py", refuses what it cannot prove in range rather
+than guessing); pointer checks must fire before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from modulated_deformable_convolution_dcn_amd import _lib, Desc, Plan, DcnError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "dcn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _header_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.dcn_version() == 10000
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.dcn_status_string(code).decode().startswith(name)
+
+
+def _desc(**kw):
+    base = dict(batch=1, in_ch=64, height=16, width=16, out_ch=64, kernel_h=3, kernel_w=3,
+                pad_h=1, pad_w=1, in_dtype=_lib.DCN_F32, out_dtype=_lib.DCN_F32,
+                out_layout=_lib.DCN_OUT_NCHW)
+    base.update(kw)
+    return _lib.DcnDesc(**base)
+
+
+def _create(**kw):
+    lib = _lib.load()
+    h = ctypes.c_void_p(1234)
+    st = lib.dcn_create(ctypes.byref(_desc(**kw)), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), _lib.DCN_OK),
+    (dict(batch=0), _lib.DCN_OK),
+    (dict(kernel_h=7, kernel_w=7, pad_h=3, pad_w=3), _lib.DCN_OK),
+    (dict(in_dtype=_lib.DCN_BF16, in_ch=8), _lib.DCN_OK),
+    (dict(out_layout=_lib.DCN_OUT_NHWC), _lib.DCN_OK),
+    (dict(out_ch=300), _lib.DCN_OK),
+    (dict(batch=-1), 2),
+    (dict(in_ch=0), 2),
+    (dict(height=0), 2),
+    (dict(kernel_w=0), 2),
+    (dict(pad_h=-1), 2),
+    (dict(height=2, kernel_h=5, pad_h=1), 2),        # Ho = 2 + 2 - 5 + 1 = 0
+    (dict(in_dtype=7), 3),
+    (dict(out_layout=5), 3),
+    (dict(out_dtype=9), 3),
+    (dict(out_dtype=_lib.DCN_BF16), 4),
+    (dict(in_ch=6), 4),                                 # not a multiple of 4 (fp32)
+    (dict(in_dtype=_lib.DCN_BF16, in_ch=12), 4),        # not a multiple of 8 (bf16)
+    (dict(batch=1024, height=1024, width=1024, in_ch=4), 4),  # x >= 2^31 bytes
+])
+def test_create_validates(kw, status):
+    lib = _lib.load()
+    st, h = _create(**kw)
+    assert st == status, lib.dcn_last_error()
+    if st == 0:
+        assert h.value
+        assert lib.dcn_destroy(h) == 0
+    else:
+        assert not h.value  # *plan set to NULL on failure
+        assert lib.dcn_last_error().decode()
+
+
+def test_null_arguments():
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    assert lib.dcn_create(None, ctypes.byref(h)) == 1
+    assert lib.dcn_create(ctypes.byref(_desc()), None) == 1
+    assert lib.dcn_destroy(None) == 0
+    sz = ctypes.c_size_t()
+    assert lib.dcn_workspace_bytes(None, ctypes.byref(sz)) == 1
+
+
+def test_output_size_and_workspace():
+    p = Plan(Desc(2, 128, 200, 176, 128, 5, 5, 2, 2))
+    assert (p.Ho, p.Wo) == (200, 176)
+    # packed weight: 25 taps x 2 chunks of 64 channels x 128 outputs, fp32
+    assert p.workspace_bytes == 25 * 128 * 128 * 4
+    p2 = Plan(Desc(1, 64, 33, 40, 256, 7, 7, 3, 3))
+    assert (p2.Ho, p2.Wo) == (33, 40)
+    p3 = Plan(Desc(1, 4, 8, 8, 4, 3, 3, 1, 1))
+    assert p3.workspace_bytes == 9 * 16 * 16 * 4  # padded to a 16-channel block, 16 outputs
+
+
+def test_pointer_checks_fire_before_any_launch():
+    """Null / misaligned / short-workspace errors are reported without touching the GPU."""
+    lib = _lib.load()
+    p = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1))
+    h = p._h
+    fake = ctypes.c_void_p(0x10000)
+    ws = p.workspace_bytes
+    assert lib.dcn_forward_packed(h, None, fake, None, fake, ws, None, fake, None) == 1
+    assert lib.dcn_forward_packed(h, fake, None, None, fake, ws, None, fake, None) == 1
+    assert lib.dcn_forward_packed(h, fake, fake, None, fake, ws, None, None, None) == 1
+    assert lib.dcn_forward_packed(h, fake, fake, None, None, ws, None, fake, None) == 8
+    assert lib.dcn_forward_packed(h, fake, fake, None, fake, ws - 1, None, fake, None) == 8
+    odd = ctypes.c_void_p(0x10004)
+    assert lib.dcn_forward_packed(h, odd, fake, None, fake, ws, None, fake, None) == 5
+    assert lib.dcn_forward_packed(h, fake, ctypes.c_void_p(0x10002), None, fake, ws, None, fake,
+                                  None) == 5
+    assert lib.dcn_pack_weight(h, None, fake, ws, None) == 1
+    assert lib.dcn_pack_weight(h, fake, fake, ws - 256, None) == 8
+    assert lib.dcn_forward(None, fake, fake, None, fake, None, fake, fake, ws, None) == 1
+    assert lib.dcn_debug_coords(h, None, fake, fake, None) == 1
+    assert "required" in lib.dcn_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op():
+    lib = _lib.load()
+    p = Plan(Desc(0, 64, 16, 16, 64, 3, 3, 1, 1))
+    # nothing to read or write: succeeds even with NULL buffers, no launch
+    assert lib.dcn_forward(p._h, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.dcn_forward_packed(p._h, None, None, None, None, 0, None, None, None) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    p = Plan(Desc(1, 4, 8, 8, 4, 3, 3, 1, 1))
+    with pytest.raises(ValueError):
+        p.forward(torch.zeros(1, 8, 8, 4), torch.zeros(1, 18, 8, 8), None,
+                  torch.zeros(4, 4, 3, 3))  # CPU tensors are refused
+    with pytest.raises(DcnError):
+        Plan(Desc(1, 3, 8, 8, 4, 3, 3, 1, 1))

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Same seeded inputs on both sides (modulated_deformable_convolution_dcn_amd.synth).
+Tolerance per output element (N = the oracle's sum of |weight| * |sample|):
+fp32 1e-4 * N, bf16 operands with fp32 accumulation 2e-2 * N, plus one fp32
+ulp of |ref| for the final bias add; N == 0 must give the bias exactly.
+Corner indices and validity are compared bit for bit in test_gpu_coords.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from modulated_deformable_convolution_dcn_amd import synth
+from dcn_testlib import compare, oracle_shape, run_gpu, sample_pixels, device_inputs, pixel_major
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+# Full-output comparisons: sizes the oracle finishes in seconds that still
+# span several 64-pixel tiles, ragged tails, several channel chunks and
+# output-channel tiles.
+FULL_CASES = {
+    "tiny_fp32": W["tiny_fp32"],
+    "birefnet512_fp32": W["birefnet512_fp32"],
+    "edge_stress_fp32_small": W["edge_stress_fp32"].scaled(H=40, W=36),
+    "detection_bf16_small": W["detection_bf16"].scaled(B=2, H=20, W=20),
+    "p1_k1": W["p1_k1"],
+    "p1_k3": W["p1_k3"],
+    "p1_k7": W["p1_k7"],
+    # C = 132: two full 64-channel chunks plus a 4-channel tail; O = 300: a
+    # second, ragged 256-wide output tile
+    "ragged_c132_o300": W["edge_stress_fp32"].scaled(B=1, C=132, O=300, H=13, W=11, kh=3, kw=3,
+                                                     ph=1, pw=1),
+    "bf16_c40_o20": W["detection_bf16"].scaled(B=1, C=40, O=20, H=9, W=23, kh=5, kw=3, ph=2,
+                                               pw=0),
+}
+
+
+def _oracle_full(spec, d):
+    return oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"], d["bias"])
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+@pytest.mark.parametrize("name", sorted(FULL_CASES))
+def test_full_parity(name, layout):
+    spec = FULL_CASES[name]
+    d = synth.make_inputs(spec)
+    ref, norm = _oracle_full(spec, d)
+    print("case", name, layout, spec, flush=True)
+    got = run_gpu(spec, d, layout)
+    worst = compare(got, ref, norm, d["bias"], spec.dtype, "%s/%s" % (name, layout))
+    print("worst err/N %.3g" % worst)
+
+
+@pytest.mark.parametrize("use_mask,use_bias", [(False, True), (True, False), (False, False)])
+def test_optional_mask_and_bias(use_mask, use_bias):
+    spec = W["edge_stress_fp32"].scaled(B=1, C=64, O=64, H=17, W=19, kh=3, kw=3, ph=1, pw=1)
+    d = synth.make_inputs(spec)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"],
+                               d["mask"] if use_mask else None, d["weight"],
+                               d["bias"] if use_bias else None)
+    got = run_gpu(spec, d, "nchw", use_mask=use_mask, use_bias=use_bias)
+    compare(got, ref, norm, d["bias"] if use_bias else None, spec.dtype, "optional")
+
+
+# Full-size workloads in the launch configuration the benchmark times:
+# sampled pixels from the oracle, plus properties that hold at any size.
+FULL_SIZE = ["birefnet1024_fp32", "detection_bf16", "edge_stress_fp32"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_full_size_sampled_parity(name):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan
+    spec = W[name]
+    d = synth.make_inputs(spec)
+    pix = sample_pixels(spec, 1500, seed=11)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                               d["bias"], pixels=pix)
+    print("case", name, "pixels", pix.size, flush=True)
+    dev = device_inputs(spec, d)
+    outs = {}
+    for layout in ("nchw", "nhwc"):
+        plan = Plan(Desc(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph,
+                         spec.pw, spec.dtype, layout))
+        o1 = plan.forward(dev["x"], dev["offset"], dev["mask"], dev["weight"], dev["bias"])
+        o2 = plan.forward(dev["x"], dev["offset"], dev["mask"], dev["weight"], dev["bias"])
+        torch.cuda.synchronize()
+        a1, a2 = o1.cpu().numpy(), o2.cpu().numpy()
+        # deterministic: no atomics, fixed summation order
+        assert np.array_equal(a1.view(np.uint32), a2.view(np.uint32))
+        outs[layout] = pixel_major(a1, layout)
+        assert np.isfinite(outs[layout]).all()
+    # both layouts run the same arithmetic; only the store differs
+    assert np.array_equal(outs["nchw"].view(np.uint32), outs["nhwc"].view(np.uint32))
+    worst = compare(outs["nchw"][pix], ref, norm, d["bias"], spec.dtype, name)
+    print("worst err/N %.3g" % worst)
+
+
+def test_packed_weight_reuse_matches_forward():
+    import torch
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan
+    spec = W["birefnet512_fp32"].scaled(H=32, W=40)
+    d = synth.make_inputs(spec)
+    dev = device_inputs(spec, d)
+    plan = Plan(Desc(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw))
+    ws = plan.pack_weight(dev["weight"])
+    a = plan.forward_packed(dev["x"], dev["offset"], dev["mask"], ws, dev["bias"])
+    b = plan.forward(dev["x"], dev["offset"], dev["mask"], dev["weight"], dev["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- edge cases
+def _spec(**kw):
+    base = dict(name="edge", B=1, C=4, O=4, H=8, W=8, kh=3, kw=3, ph=1, pw=1, dtype="f32",
+                seed=21, offset_dist="normal1.5", mask_dist="uniform", weight_std=0.3,
+                bias_dist="normal1")
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_corners_outside_give_bias_exactly(dtype):
+    spec = _spec(C=8, O=24, H=10, W=12, dtype=dtype)
+    d = synth.make_inputs(spec)
+    off = d["offset"]
+    off[:, 0::2] = 1000.0
+    off[:, 1::2] = -1000.0
+    if dtype == "bf16":
+        d["offset"], d["bits"]["offset"] = synth.round_bf16(off)
+    got = run_gpu(spec, d, "nchw")
+    assert np.array_equal(got, np.broadcast_to(d["bias"], got.shape))
+
+
+def test_worked_example_2x2():
+    """The hand-derived example (tests/golden/worked_example_2x2.txt) on the GPU:
+    C = 1 padded to 4 channels with zero input and zero weight."""
+    from conftest import read_golden
+    g = read_golden("worked_example_2x2.txt")
+    spec = _spec(C=4, O=1, H=2, W=2, kh=1, kw=1, ph=0, pw=0)
+    x = np.zeros((1, 2, 2, 4), np.float32)
+    x[..., 0] = np.array(g["x"]).reshape(2, 2)
+    off = np.stack([np.array(g["dy"]).reshape(2, 2), np.array(g["dx"]).reshape(2, 2)])
+    d = {"x": x, "offset": off.reshape(1, 2, 2, 2).astype(np.float32),
+         "mask": np.array(g["mask"], np.float32).reshape(1, 1, 2, 2),
+         "weight": np.array([g["weight"][0], 0, 0, 0], np.float32).reshape(1, 4, 1, 1),
+         "bias": np.array(g["bias"], np.float32)}
+    got = run_gpu(spec, d, "nchw")
+    assert np.array_equal(got[:, 0], np.array(g["out"], np.float32))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=1, W=1, kh=1, kw=1, ph=0, pw=0),            # one pixel
+    dict(H=2, W=3, kh=5, kw=5, ph=2, pw=2),            # kernel larger than the image
+    dict(H=1, W=70, kh=1, kw=3, ph=0, pw=1),           # one row, ragged tile
+    dict(H=67, W=1, kh=3, kw=1, ph=1, pw=0),           # one column
+    dict(B=3, H=5, W=7, kh=2, kw=4, ph=0, pw=1),       # even kernel, asymmetric pad
+    dict(C=16, O=17, H=9, W=9),                        # O not a multiple of 16
+    dict(C=64, O=65, H=9, W=9, kh=7, kw=7, ph=3, pw=3),
+])
+def test_shape_edge_cases(kw):
+    spec = _spec(**kw)
+    d = synth.make_inputs(spec)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                               d["bias"])
+    for layout in ("nchw", "nhwc"):
+        got = run_gpu(spec, d, layout)
+        compare(got, ref, norm, d["bias"], spec.dtype, "edge %s %s" % (kw, layout))
+
+
+def test_empty_batch_leaves_output_untouched():
+    import torch
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan
+    plan = Plan(Desc(0, 8, 6, 6, 8, 3, 3, 1, 1))
+    x = torch.zeros((0, 6, 6, 8), device="cuda")
+    off = torch.zeros((0, 18, 6, 6), device="cuda")
+    w = torch.zeros((8, 8, 3, 3), device="cuda")
+    out = plan.forward(x, off, None, w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 6, 6)
+
+
+def test_integer_offsets_equal_shifted_direct_conv():
+    """Integer offsets: every sample is an input pixel (or zero); the GPU
+    must match the oracle, which is pinned to a shifted direct conv."""
+    spec = _spec(C=64, O=64, H=30, W=26, kh=3, kw=3)
+    d = synth.make_inputs(spec)
+    rng = np.random.default_rng(3)
+    d["offset"] = rng.integers(-3, 4, size=d["offset"].shape).astype(np.float32)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                               d["bias"])
+    got = run_gpu(spec, d, "nchw")
+    compare(got, ref, norm, d["bias"], "f32", "integer offsets")
