@@ -136,7 +136,7 @@ dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan) {
       return fail(DCN_E_UNSUPPORTED, "input is %lld bytes; this build addresses < 2^31",
                   (long long)x_bytes);
     if (K >= kLimit31 / 2 || HoWo >= kLimit31 ||
-        (int64_t)d.batch * 2 * K * HoWo >= kLimit31 ||
+        (int64_t)d.batch * 2 * K * HoWo * E >= kLimit31 ||
         (int64_t)d.batch * d.out_ch * HoWo >= kLimit31)
       return fail(DCN_E_UNSUPPORTED, "offset/output element counts must stay below 2^31");
 
@@ -245,6 +245,8 @@ dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, 
     a.n_otiles = plan->kc.n_otiles;
     a.tiles_per_img = plan->kc.tiles_per_img;
     a.x_bytes = plan->x_bytes;
+    a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
+    a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
     a.vec_store = (a.HoWo % 4) == 0;
     hipError_t e = dcn::launch_fused(plan->kc, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused forward launch");

@@ -78,4 +78,18 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// One operand element through a buffer descriptor, as fp32 (0 when the byte
+// offset is past the descriptor's size).
+template <class T>
+__device__ __forceinline__ float load_scalar(__amdgpu_buffer_rsrc_t r, uint32_t byte_off);
+template <>
+__device__ __forceinline__ float load_scalar<float>(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float load_scalar<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+  return __uint_as_float(u << 16);
+}
+
 }  // namespace dcn

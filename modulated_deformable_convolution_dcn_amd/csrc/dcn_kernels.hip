@@ -25,6 +25,8 @@
 //       corner loads and weight block are already in flight;
 // and finally adds the bias and writes NCHW or NHWC fp32 output.
 
+#include <type_traits>
+
 #include "dcn_device.h"
 #include "dcn_launch.h"
 
@@ -150,39 +152,55 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
   const T* maskp = static_cast<const T*>(a.mask);
   const uint32_t row_bytes = (uint32_t)a.C * E;
 
-  // ---- (a) sampling point -> corner weights and offsets, one tap, M pixels
-  auto coef_stage = [&](int kt, int slot) {
+  // ---- (a) sampling point -> corner weights and offsets, one tap, M pixels.
+  // Split in two so that the offset/mask loads are issued ahead of the
+  // corner loads and consumed after the MFMAs: vmcnt counts in order, so a
+  // load issued after the gather could only be waited for behind it, and a
+  // load under a data-dependent branch makes the compiler drain the counter.
+  // Hence buffer loads with no branches (a NULL mask is a zero-size buffer
+  // that reads as 0, replaced by 1).  Thread (wave w, lane l) owns pixel l
+  // (+64 r) and corner w, so all four waves share the work evenly.
+  static_assert(M % 64 == 0, "one lane per pixel in the coefficient stage");
+  constexpr int CPL = M / 64;  // pixels per lane in the coefficient stage
+  const bool has_mask = maskp != nullptr;
+  const __amdgpu_buffer_rsrc_t offr = make_rsrc(offp, a.offset_bytes);
+  const __amdgpu_buffer_rsrc_t mskr = make_rsrc(has_mask ? (const void*)maskp : (const void*)offp,
+                                                has_mask ? a.mask_bytes : 0u);
+  const int corner = wave;  // (a, b) = (corner >> 1, corner & 1)
+  float c_dy[CPL], c_dx[CPL], c_mk[CPL];
+  auto coef_load = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) {
+      const uint32_t hw = (uint32_t)(hw0 + r * 64 + lane);
+      const uint32_t ob = ((uint32_t)(b * 2 * a.K + 2 * kt) * (uint32_t)a.HoWo + hw) * E;
+      const uint32_t mb = ((uint32_t)(b * a.K + kt) * (uint32_t)a.HoWo + hw) * E;
+      c_dy[r] = load_scalar<T>(offr, ob);
+      c_dx[r] = load_scalar<T>(offr, ob + (uint32_t)a.HoWo * E);
+      c_mk[r] = load_scalar<T>(mskr, mb);
+    }
+  };
+  auto coef_finish = [&](int kt, int slot) {
     const int i = kt / a.kw;
     const int j = kt - i * a.kw;
-    for (int m = tid; m < M; m += 256) {
-      Coef cf;
-      cf.w = f32x4{0.f, 0.f, 0.f, 0.f};
-      cf.off = u32x4{kNoCorner, kNoCorner, kNoCorner, kNoCorner};
-      const int hw = hw0 + m;
-      if (hw < a.HoWo) {
-        const int ho = hw / a.Wo;
-        const int wo = hw - ho * a.Wo;
-        const size_t ob = (size_t)(b * 2 * a.K + 2 * kt) * a.HoWo + hw;
-        const float dy = to_f32<T>(offp[ob]);
-        const float dx = to_f32<T>(offp[ob + a.HoWo]);
-        const float mk =
-            maskp ? to_f32<T>(maskp[(size_t)(b * a.K + kt) * a.HoWo + hw]) : 1.0f;
-        const TapPoint t = tap_point(dy, dx, ho - a.ph + i, wo - a.pw + j, a.H, a.W);
-        const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
-        const float wv[4] = {hy * hx, hy * t.lx, t.ly * hx, t.ly * t.lx};
-        if (t.valid) {
-          const int y0 = (int)t.y0, x0 = (int)t.x0;  // in [-1, H-1] x [-1, W-1] here
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (t.valid & (1u << c)) {
-              const int yy = y0 + (c >> 1), xx = x0 + (c & 1);
-              cf.w[c] = wv[c] * mk;
-              cf.off[c] = (uint32_t)((b * a.H + yy) * a.W + xx) * row_bytes;
-            }
-          }
-        }
-      }
-      Cs[slot][m] = cf;
+    for (int r = 0; r < CPL; ++r) {
+      const int m = r * 64 + lane;
+      const int hw = hw0 + m;
+      const int ho = hw / a.Wo;
+      const int wo = hw - ho * a.Wo;
+      const TapPoint t = tap_point(c_dy[r], c_dx[r], ho - a.ph + i, wo - a.pw + j, a.H, a.W);
+      const int ca = corner >> 1, cb = corner & 1;
+      const float wy = ca ? t.ly : 1.0f - t.ly;
+      const float wx = cb ? t.lx : 1.0f - t.lx;
+      const float mk = has_mask ? c_mk[r] : 1.0f;
+      const bool ok = (hw < a.HoWo) && ((t.valid >> corner) & 1u);
+      // clamp before converting: only inside corners are used, but the
+      // conversion of a far point must stay defined
+      const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
+      const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
+      Cs[slot][m].w[corner] = ok ? wy * wx * mk : 0.0f;
+      Cs[slot][m].off[corner] =
+          ok ? (uint32_t)((b * a.H + y0 + ca) * a.W + x0 + cb) * row_bytes : kNoCorner;
     }
   };
 
@@ -246,16 +264,23 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Fragments for read q+1 are fetched from LDS before the MFMAs of read q
+  // are issued, so LDS latency hides behind the matrix pipe.
   auto mfma_block = [&](const T* A, const T* Bt) {
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      u32x4 af[MT], bf[NT];
+    u32x4 af[2][MT], bf[2][NT];
+    auto fetch = [&](int q, int s) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        af[mt] = lds16(&A[(wm * WROWS + mt * 16 + rl) * AST + g * (CB / 4) + q * VEC]);
+        af[s][mt] = lds16(&A[(wm * WROWS + mt * 16 + rl) * AST + g * (CB / 4) + q * VEC]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bf[nt] = lds16(&Bt[((g * R + q) * NO + wn * WCOLS + nt * 16 + rl) * VEC]);
+        bf[s][nt] = lds16(&Bt[((g * R + q) * NO + wn * WCOLS + nt * 16 + rl) * VEC]);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int s = q & 1;
+      if (q + 1 < R) fetch(q + 1, s ^ 1);
       if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -264,45 +289,66 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
               acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                  __uint_as_float(af[mt][e]), __uint_as_float(bf[nt][e]), acc[mt][nt], 0, 0,
-                  0);
+                  __uint_as_float(af[s][mt][e]), __uint_as_float(bf[s][nt][e]), acc[mt][nt], 0,
+                  0, 0);
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, af[mt]), __builtin_bit_cast(bf16x8, bf[nt]),
+                __builtin_bit_cast(bf16x8, af[s][mt]), __builtin_bit_cast(bf16x8, bf[s][nt]),
                 acc[mt][nt], 0, 0, 0);
       }
     }
   };
 
-  // ---- pipeline over k-blocks (tap-major, channel chunk minor)
+  // ---- pipeline over k-blocks (tap-major, channel chunk minor).  While the
+  // MFMAs of block kb run, the corner loads and weight block of kb+1 and, on
+  // a tap's last chunk, the offsets/mask of tap kt+2 are in flight.  The
+  // load sequence of every step is branch-free (the last step re-loads the
+  // final block into the idle buffer instead of skipping), so the only
+  // waits are the in-order ones each consumer needs.
   const int NKB = a.K * a.nchunk;
-  coef_stage(0, 0);
-  if (a.K > 1) coef_stage(1, 1);
+  coef_load(0);
+  coef_finish(0, 0);
+  coef_load(a.K > 1 ? 1 : 0);
+  coef_finish(a.K > 1 ? 1 : 0, 1);
   __syncthreads();
   issue_gather(0);
   issue_b(0);
   finish_gather(As[0]);
   store_b(Bs[0]);
 
-  for (int kb = 0; kb < NKB; ++kb) {
+  auto step = [&](int kt, int cc, auto last_chunk_tag) {
+    constexpr bool kLastChunk = decltype(last_chunk_tag)::value;
+    const int kb = kt * a.nchunk + cc;
     const int buf = kb & 1;
+    const int kn = kb + 1 < NKB ? kb + 1 : kb;
     __syncthreads();  // block kb is in LDS; every wave is done with block kb-1
-    const bool has_next = kb + 1 < NKB;
-    if (has_next) {
-      issue_gather(kb + 1);
-      issue_b(kb + 1);
-      const int kt1 = (kb + 1) / a.nchunk;
-      if (kt1 * a.nchunk == kb + 1 && kt1 + 1 < a.K) coef_stage(kt1 + 1, (kt1 + 1) & 1);
+    // The scheduling barriers keep the phases in this order: the machine
+    // scheduler would otherwise sink loads to their first use, i.e. behind
+    // the MFMAs, and issue the offset loads after the corner loads.
+    if constexpr (kLastChunk) {
+      coef_load(kt + 2 < a.K ? kt + 2 : a.K - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    issue_gather(kn);
+    issue_b(kn);
+    __builtin_amdgcn_sched_barrier(0);
     mfma_block(As[buf], Bs[buf]);
-    if (has_next) {
-      finish_gather(As[buf ^ 1]);
-      store_b(Bs[buf ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // tap kt+2 goes to slot kt&1: tap kt's gathers were all issued before
+    // this step's barrier
+    if constexpr (kLastChunk) {
+      if (kt + 2 < a.K) coef_finish(kt + 2, kt & 1);
     }
+    finish_gather(As[buf ^ 1]);
+    store_b(Bs[buf ^ 1]);
+  };
+  for (int kt = 0; kt < a.K; ++kt) {
+    for (int cc = 0; cc + 1 < a.nchunk; ++cc) step(kt, cc, std::false_type{});
+    step(kt, a.nchunk - 1, std::true_type{});
   }
 
   // ---- epilogue: + bias, fp32 store.  MFMA 16x16 result layout: lane l,

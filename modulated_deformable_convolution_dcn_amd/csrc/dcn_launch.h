@@ -30,6 +30,8 @@ struct FusedArgs {
   int B, C, H, W, O, kh, kw, K, ph, pw, Ho, Wo, HoWo;
   int nchunk, n_otiles, tiles_per_img;
   uint32_t x_bytes;    // bytes of x (< 2^31)
+  uint32_t offset_bytes;  // bytes of offset (< 2^31)
+  uint32_t mask_bytes;    // bytes of mask (< 2^31; 0 when mask is NULL)
   int vec_store;       // NCHW: Ho*Wo % 4 == 0, so 4 consecutive pixels store as one 16-B write
 };
 
