@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcn_mi355x.so")
 
-SOURCES = ["dcn_kernels.hip", "dcn_api.cpp"]
+SOURCES = ["dcn_kernels.hip", "dcn_wsk.hip", "dcn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,7 +32,7 @@ def _obj(src: str, build_dir: str) -> str:
     return os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
 
 
-def build(verbose: bool = False, jobs: int = 2) -> str:
+def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)

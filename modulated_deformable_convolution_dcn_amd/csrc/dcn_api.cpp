@@ -54,13 +54,23 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
   dcn::KernelConfig kc{};
   kc.bf16 = d.in_dtype == DCN_BF16;
-  kc.M = 64;
   const int O = d.out_ch, C = d.in_ch;
-  kc.NO = O <= 16 ? 16 : O <= 64 ? 64 : O <= 128 ? 128 : 256;
-  if (kc.bf16) {
-    kc.CB = C <= 32 ? 32 : 64;
+  if (!kc.bf16 && O > 16 && O <= 128 && C >= 32) {
+    // fp32 with a small output tile: k split over the four waves, no
+    // workgroup barrier in the main loop (dcn_wsk.hip)
+    kc.kind = 1;
+    kc.CB = 64;
+    kc.NO = O <= 64 ? 64 : 128;
+    kc.M = kc.NO == 64 ? 64 : 32;
   } else {
-    kc.CB = C <= 16 ? 16 : (kc.NO == 256 ? 32 : 64);
+    kc.kind = 0;
+    kc.M = 64;
+    kc.NO = O <= 16 ? 16 : O <= 64 ? 64 : O <= 128 ? 128 : 256;
+    if (kc.bf16) {
+      kc.CB = C <= 32 ? 32 : 64;
+    } else {
+      kc.CB = C <= 16 ? 16 : (kc.NO == 256 ? 32 : 64);
+    }
   }
   kc.nhwc = d.out_layout == DCN_OUT_NHWC;
   kc.nchunk = (int)ceil_div(C, kc.CB);

@@ -8,6 +8,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace dcn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -90,6 +93,91 @@ template <>
 __device__ __forceinline__ float load_scalar<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
   return __uint_as_float(u << 16);
+}
+
+// ---- shared by the fused kernels
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled, so
+// that the body can select registers and instructions at compile time.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+
+template <class T>
+struct Ops;
+
+template <>
+struct Ops<float> {
+  typedef f32x4 frag;
+  static constexpr int VEC = 4;
+  // blended = w0*c0 + w1*c1 + w2*c2 + w3*c3 on 4 fp32 channels
+  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
+                                                u32x4 c3) {
+    const f32x4 v0 = __builtin_bit_cast(f32x4, c0), v1 = __builtin_bit_cast(f32x4, c1);
+    const f32x4 v2 = __builtin_bit_cast(f32x4, c2), v3 = __builtin_bit_cast(f32x4, c3);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = w[0] * v0[e];
+      s = __builtin_fmaf(w[1], v1[e], s);
+      s = __builtin_fmaf(w[2], v2[e], s);
+      s = __builtin_fmaf(w[3], v3[e], s);
+      r[e] = s;
+    }
+    return __builtin_bit_cast(u32x4, r);
+  }
+};
+
+template <>
+struct Ops<__bf16> {
+  typedef bf16x8 frag;
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
+  __device__ static __forceinline__ float hi(uint32_t u) {
+    return __uint_as_float(u & 0xffff0000u);
+  }
+  // Blend 8 bf16 channels in fp32, round the result to bf16 (nearest-even).
+  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
+                                                u32x4 c3) {
+    bf16x8 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float sl = w[0] * lo(c0[q]);
+      sl = __builtin_fmaf(w[1], lo(c1[q]), sl);
+      sl = __builtin_fmaf(w[2], lo(c2[q]), sl);
+      sl = __builtin_fmaf(w[3], lo(c3[q]), sl);
+      float sh = w[0] * hi(c0[q]);
+      sh = __builtin_fmaf(w[1], hi(c1[q]), sh);
+      sh = __builtin_fmaf(w[2], hi(c2[q]), sh);
+      sh = __builtin_fmaf(w[3], hi(c3[q]), sh);
+      r[2 * q] = static_cast<__bf16>(sl);
+      r[2 * q + 1] = static_cast<__bf16>(sh);
+    }
+    return __builtin_bit_cast(u32x4, r);
+  }
+};
+
+// One 16-byte fragment read from LDS.
+template <class T>
+__device__ __forceinline__ u32x4 lds16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// XCD-aware block order: the dispatcher deals consecutive workgroup ids to
+// the 8 XCDs in turn, so logical tile t is given to hardware id
+// (t % per_xcd) * 8 + t / per_xcd -- each XCD then walks one contiguous run
+// of tiles and its private L2 holds one band of the input map.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+  const int full = (nblk / 8) * 8;
+  if (bid >= full) return bid;
+  const int per_xcd = full / 8;
+  return (bid % 8) * per_xcd + bid / 8;
 }
 
 }  // namespace dcn

@@ -32,84 +32,6 @@
 
 namespace dcn {
 
-// Per (pixel, tap): corner weights (bilinear x validity x mask) and byte
-// offsets of the four corners' channel vectors in x (kNoCorner if outside).
-struct alignas(16) Coef {
-  f32x4 w;
-  u32x4 off;
-};
-
-template <class T>
-struct Ops;
-
-template <>
-struct Ops<float> {
-  typedef f32x4 frag;
-  static constexpr int VEC = 4;
-  // blended = w0*c0 + w1*c1 + w2*c2 + w3*c3 on 4 fp32 channels
-  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
-                                                u32x4 c3) {
-    const f32x4 v0 = __builtin_bit_cast(f32x4, c0), v1 = __builtin_bit_cast(f32x4, c1);
-    const f32x4 v2 = __builtin_bit_cast(f32x4, c2), v3 = __builtin_bit_cast(f32x4, c3);
-    f32x4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float s = w[0] * v0[e];
-      s = __builtin_fmaf(w[1], v1[e], s);
-      s = __builtin_fmaf(w[2], v2[e], s);
-      s = __builtin_fmaf(w[3], v3[e], s);
-      r[e] = s;
-    }
-    return __builtin_bit_cast(u32x4, r);
-  }
-};
-
-template <>
-struct Ops<__bf16> {
-  typedef bf16x8 frag;
-  static constexpr int VEC = 8;
-  __device__ static __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
-  __device__ static __forceinline__ float hi(uint32_t u) {
-    return __uint_as_float(u & 0xffff0000u);
-  }
-  // Blend 8 bf16 channels in fp32, round the result to bf16 (nearest-even).
-  __device__ static __forceinline__ u32x4 blend(f32x4 w, u32x4 c0, u32x4 c1, u32x4 c2,
-                                                u32x4 c3) {
-    bf16x8 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float sl = w[0] * lo(c0[q]);
-      sl = __builtin_fmaf(w[1], lo(c1[q]), sl);
-      sl = __builtin_fmaf(w[2], lo(c2[q]), sl);
-      sl = __builtin_fmaf(w[3], lo(c3[q]), sl);
-      float sh = w[0] * hi(c0[q]);
-      sh = __builtin_fmaf(w[1], hi(c1[q]), sh);
-      sh = __builtin_fmaf(w[2], hi(c2[q]), sh);
-      sh = __builtin_fmaf(w[3], hi(c3[q]), sh);
-      r[2 * q] = static_cast<__bf16>(sl);
-      r[2 * q + 1] = static_cast<__bf16>(sh);
-    }
-    return __builtin_bit_cast(u32x4, r);
-  }
-};
-
-// One 16-byte fragment read from LDS.
-template <class T>
-__device__ __forceinline__ u32x4 lds16(const T* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-// XCD-aware block order: the dispatcher deals consecutive workgroup ids to
-// the 8 XCDs in turn, so logical tile t is given to hardware id
-// (t % per_xcd) * 8 + t / per_xcd -- each XCD then walks one contiguous run
-// of tiles and its private L2 holds one band of the input map.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
-  const int full = (nblk / 8) * 8;
-  if (bid >= full) return bid;
-  const int per_xcd = full / 8;
-  return (bid % 8) * per_xcd + bid / 8;
-}
-
 template <class T, int M, int CB, int NO, int WM, int WN, bool NHWC>
 __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
   constexpr int E = sizeof(T);
@@ -125,13 +47,16 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
   constexpr int R = CB / 4 / VEC;        // fragment reads per k-slot group per k-block
   constexpr int WROWS = M / WM, WCOLS = NO / WN;
   constexpr int MT = WROWS / 16, NT = WCOLS / 16;
+  constexpr int NSLOT = 3;               // coefficient ring (taps in flight)
   static_assert(LPR >= 1 && 256 % LPR == 0 && NPASS >= 1 && M % PPP == 0, "gather shape");
   static_assert(R >= 1 && CB % (4 * VEC) == 0, "k-block shape");
   static_assert(WM * WN == 4 && MT >= 1 && NT >= 1, "wave tiling");
+  static_assert(M % 64 == 0, "one lane per pixel in the coefficient stage");
 
   __shared__ __attribute__((aligned(16))) T As[2][A_ELEMS];
   __shared__ __attribute__((aligned(16))) T Bs[2][B_ELEMS];
-  __shared__ Coef Cs[2][M];
+  __shared__ f32x4 Cw[NSLOT][M];   // corner weights: bilinear x validity x mask
+  __shared__ u32x4 Co[NSLOT][M];   // corner byte offsets in x (kNoCorner: outside)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,16 +76,15 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
   const T* offp = static_cast<const T*>(a.offset);
   const T* maskp = static_cast<const T*>(a.mask);
   const uint32_t row_bytes = (uint32_t)a.C * E;
+  const int NKB = a.K * a.nchunk;
 
   // ---- (a) sampling point -> corner weights and offsets, one tap, M pixels.
-  // Split in two so that the offset/mask loads are issued ahead of the
-  // corner loads and consumed after the MFMAs: vmcnt counts in order, so a
-  // load issued after the gather could only be waited for behind it, and a
-  // load under a data-dependent branch makes the compiler drain the counter.
-  // Hence buffer loads with no branches (a NULL mask is a zero-size buffer
-  // that reads as 0, replaced by 1).  Thread (wave w, lane l) owns pixel l
-  // (+64 r) and corner w, so all four waves share the work evenly.
-  static_assert(M % 64 == 0, "one lane per pixel in the coefficient stage");
+  // Split in two: the offset/mask loads are issued at the top of a step and
+  // consumed after its MFMAs.  vmcnt counts in order, and a load under a
+  // data-dependent branch makes the compiler drain the counter, so these are
+  // branch-free buffer loads (a NULL mask is a zero-size buffer that reads as
+  // 0, replaced by 1).  Thread (wave w, lane l) owns pixel l (+64 r) and
+  // corner w, so the four waves share the work evenly.
   constexpr int CPL = M / 64;  // pixels per lane in the coefficient stage
   const bool has_mask = maskp != nullptr;
   const __amdgpu_buffer_rsrc_t offr = make_rsrc(offp, a.offset_bytes);
@@ -179,7 +103,8 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
       c_mk[r] = load_scalar<T>(mskr, mb);
     }
   };
-  auto coef_finish = [&](int kt, int slot) {
+  auto coef_finish = [&](int kt) {
+    const int slot = kt % NSLOT;
     const int i = kt / a.kw;
     const int j = kt - i * a.kw;
 #pragma unroll
@@ -198,18 +123,20 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
       // conversion of a far point must stay defined
       const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
       const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
-      Cs[slot][m].w[corner] = ok ? wy * wx * mk : 0.0f;
-      Cs[slot][m].off[corner] =
+      Cw[slot][m][corner] = ok ? wy * wx * mk : 0.0f;
+      Co[slot][m][corner] =
           ok ? (uint32_t)((b * a.H + y0 + ca) * a.W + x0 + cb) * row_bytes : kNoCorner;
     }
   };
 
-  // ---- (b) corner loads for k-block kb into registers
+  // ---- (b) corner loads into one of two register sets: the loads of block
+  // kb+2 are in flight while block kb+1 (loaded a whole step earlier) is
+  // blended and block kb is multiplied.
   const int li = tid % LPR;  // which 16-byte slice of the channel block
   const int pr = tid / LPR;  // which pixel of the pass
-  u32x4 gv[NPASS][4];
-  f32x4 gw[NPASS];
-  auto issue_gather = [&](int kb) {
+  u32x4 gv[2][NPASS][4];
+  auto issue_gather = [&](int kb, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
     const int kt = kb / a.nchunk;
     const int cc = kb - kt * a.nchunk;
     const int ch = cc * CB + li * VEC;
@@ -217,18 +144,19 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
     const uint32_t cbyte = (uint32_t)ch * E;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const Coef& cf = Cs[kt & 1][ps * PPP + pr];
-      gw[ps] = cf.w;
-      const u32x4 off = cf.off;
+      const u32x4 off = Co[kt % NSLOT][ps * PPP + pr];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        gv[ps][c] = load16(xr, chan_ok ? off[c] + cbyte : kNoCorner);
+        gv[S][ps][c] = load16(xr, chan_ok ? off[c] + cbyte : kNoCorner);
     }
   };
-  auto finish_gather = [&](T* A) {
+  auto finish_gather = [&](int kb, T* A, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
+    const int kt = kb / a.nchunk;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const u32x4 r = Ops<T>::blend(gw[ps], gv[ps][0], gv[ps][1], gv[ps][2], gv[ps][3]);
+      const f32x4 w = Cw[kt % NSLOT][ps * PPP + pr];
+      const u32x4 r = Ops<T>::blend(w, gv[S][ps][0], gv[S][ps][1], gv[S][ps][2], gv[S][ps][3]);
       *reinterpret_cast<u32x4*>(&A[(ps * PPP + pr) * AST + li * VEC]) = r;
     }
   };
@@ -255,6 +183,7 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
   // group g (lane / 16) owns channels [g*CB/4, (g+1)*CB/4); fragment read q
   // of a lane holds channels g*CB/4 + q*VEC + [0, VEC).  The packed weight
   // uses the same order, so any assignment is a permutation of the sum.
+  // Fragments for read q+1 are fetched before the MFMAs of read q issue.
   const int rl = lane & 15;
   const int g = lane >> 4;
   const int wm = wave / WN, wn = wave % WN;
@@ -264,8 +193,6 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Fragments for read q+1 are fetched from LDS before the MFMAs of read q
-  // are issued, so LDS latency hides behind the matrix pipe.
   auto mfma_block = [&](const T* A, const T* Bt) {
     u32x4 af[2][MT], bf[2][NT];
     auto fetch = [&](int q, int s) {
@@ -303,53 +230,54 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
     }
   };
 
-  // ---- pipeline over k-blocks (tap-major, channel chunk minor).  While the
-  // MFMAs of block kb run, the corner loads and weight block of kb+1 and, on
-  // a tap's last chunk, the offsets/mask of tap kt+2 are in flight.  The
-  // load sequence of every step is branch-free (the last step re-loads the
-  // final block into the idle buffer instead of skipping), so the only
-  // waits are the in-order ones each consumer needs.
-  const int NKB = a.K * a.nchunk;
+  // ---- pipeline.  Step i (one barrier): load the offsets/mask of the tap
+  // whose coefficients this step may produce, the weight block of i+1 and
+  // the corners of i+2 -- in that order, so each consumer waits only for
+  // what is older than the loads still in flight -- then MFMA block i, then
+  // write coefficients (tap t is produced in step t*nchunk - 3), blend block
+  // i+1 into the idle column buffer and store weight block i+1.  Every load
+  // sequence is branch-free; past the end the last block is re-loaded into
+  // the idle buffers instead of branching.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int k1 = a.K > 1 ? 1 : 0;
   coef_load(0);
-  coef_finish(0, 0);
-  coef_load(a.K > 1 ? 1 : 0);
-  coef_finish(a.K > 1 ? 1 : 0, 1);
+  coef_finish(0);
+  coef_load(k1);
+  coef_finish(k1);
   __syncthreads();
-  issue_gather(0);
   issue_b(0);
-  finish_gather(As[0]);
+  issue_gather(0, S0{});
+  issue_gather(NKB > 1 ? 1 : 0, S1{});
+  __syncthreads();  // every wave has read the offsets of blocks 0 and 1
+  if (a.nchunk == 1 && a.K > 2) {
+    coef_load(2);
+    coef_finish(2);
+  }
+  finish_gather(0, As[0], S0{});
   store_b(Bs[0]);
 
-  auto step = [&](int kt, int cc, auto last_chunk_tag) {
-    constexpr bool kLastChunk = decltype(last_chunk_tag)::value;
-    const int kb = kt * a.nchunk + cc;
-    const int buf = kb & 1;
-    const int kn = kb + 1 < NKB ? kb + 1 : kb;
-    __syncthreads();  // block kb is in LDS; every wave is done with block kb-1
-    // The scheduling barriers keep the phases in this order: the machine
-    // scheduler would otherwise sink loads to their first use, i.e. behind
-    // the MFMAs, and issue the offset loads after the corner loads.
-    if constexpr (kLastChunk) {
-      coef_load(kt + 2 < a.K ? kt + 2 : a.K - 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    issue_gather(kn);
-    issue_b(kn);
+  auto step = [&](int i, auto par) {
+    constexpr int P = decltype(par)::value;  // i & 1: buffers and register set
+    __syncthreads();  // block i is in LDS; every wave is done with block i-1
+    const int tc = (i + 3) / a.nchunk;
+    const bool coef_due = (i + 3) - tc * a.nchunk == 0 && tc < a.K;
+    coef_load(tc < a.K ? tc : a.K - 1);
+    issue_b(i + 1 < NKB ? i + 1 : NKB - 1);
+    issue_gather(i + 2 < NKB ? i + 2 : NKB - 1, std::integral_constant<int, P>{});
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(As[buf], Bs[buf]);
+    mfma_block(As[P], Bs[P]);
     __builtin_amdgcn_sched_barrier(0);
-    // tap kt+2 goes to slot kt&1: tap kt's gathers were all issued before
-    // this step's barrier
-    if constexpr (kLastChunk) {
-      if (kt + 2 < a.K) coef_finish(kt + 2, kt & 1);
-    }
-    finish_gather(As[buf ^ 1]);
-    store_b(Bs[buf ^ 1]);
+    if (coef_due) coef_finish(tc);
+    finish_gather(i + 1 < NKB ? i + 1 : NKB - 1, As[P ^ 1], std::integral_constant<int, P ^ 1>{});
+    store_b(Bs[P ^ 1]);
   };
-  for (int kt = 0; kt < a.K; ++kt) {
-    for (int cc = 0; cc + 1 < a.nchunk; ++cc) step(kt, cc, std::false_type{});
-    step(kt, a.nchunk - 1, std::true_type{});
+  int i = 0;
+  for (; i + 1 < NKB; i += 2) {
+    step(i, S0{});
+    step(i + 1, S1{});
   }
+  if (i < NKB) step(i, S0{});
 
   // ---- epilogue: + bias, fp32 store.  MFMA 16x16 result layout: lane l,
   // register r holds row 4*(l/16) + r, column l % 16.
@@ -383,31 +311,43 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 }
 
 // ---------------------------------------------------------------- packing
-// wpack[otile][tap][chunk][CB/VEC][NO][VEC] = weight[o][c][i][j] with
-// o = otile*NO + n, c = chunk*CB + cg*VEC + v, tap = i*kw + j (zero-padded):
-// page 1 reorders the weight to rows (i, j, c) x columns o for its matmul;
-// this is that matrix cut into the kernel's [CB x NO] blocks, with each
-// lane's VEC consecutive channels contiguous.
+// The packed weight is page 1's matrix (rows (i, j, c), columns o: it
+// reorders weight[o, c, i, j] that way before its one matmul) cut into the
+// kernels' [CB x NO] k-blocks, zero-padded, ordered
+//   [o_tile][tap][c_chunk][block]
+// where the block layout serves one kernel's fragment reads:
+//   layout 0 (shared column tile): [CB/VEC][NO][VEC] -- each lane's VEC
+//            consecutive channels of one output channel are contiguous;
+//   layout 1 (k split over waves, CB = 64, VEC = 4): [wave][NO/16][g][16][4]
+//            = channel 16*wave + 4g + e, output 16*nt + col -- one wave's MFMA
+//            B fragments for a block are one contiguous run per nt.
 template <class T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* __restrict__ wp,
                                                    int O, int C, int kh, int kw, int CB, int NO,
-                                                   int VEC, int nchunk, int64_t total) {
+                                                   int VEC, int nchunk, int layout, int64_t total) {
   const int K = kh * kw;
+  const int blk = CB * NO;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
-    int64_t r = idx;
-    const int v = (int)(r % VEC);
-    r /= VEC;
-    const int n = (int)(r % NO);
-    r /= NO;
-    const int cg = (int)(r % (CB / VEC));
-    r /= (CB / VEC);
+    const int ib = (int)(idx % blk);
+    int64_t r = idx / blk;
     const int chunk = (int)(r % nchunk);
     r /= nchunk;
     const int tap = (int)(r % K);
     const int otile = (int)(r / K);
-    const int o = otile * NO + n;
-    const int c = chunk * CB + cg * VEC + v;
+    int c_in, o_in;
+    if (layout == 0) {
+      const int v = ib % VEC;
+      o_in = (ib / VEC) % NO;
+      c_in = (ib / (VEC * NO)) * VEC + v;
+    } else {
+      const int e = ib & 3, col = (ib >> 2) & 15, g = (ib >> 6) & 3;
+      const int nt = (ib >> 8) % (NO / 16), wv = (ib >> 8) / (NO / 16);
+      c_in = 16 * wv + 4 * g + e;
+      o_in = 16 * nt + col;
+    }
+    const int o = otile * NO + o_in;
+    const int c = chunk * CB + c_in;
     const int i = tap / kw, j = tap % kw;
     T val = static_cast<T>(0.0f);
     if (o < O && c < C) val = w[(((int64_t)o * C + c) * kh + i) * kw + j];
@@ -525,6 +465,7 @@ unsigned grid_for(int64_t total) {
 }  // namespace
 
 bool config_supported(const KernelConfig& kc) {
+  if (kc.kind == 1) return wsk_supported(kc);
   if (kc.M != 64) return false;
   if (kc.NO != 16 && kc.NO != 64 && kc.NO != 128 && kc.NO != 256) return false;
   if (kc.bf16) return kc.CB == 32 || kc.CB == 64;
@@ -542,16 +483,17 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
   if (kc.bf16) {
     hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s,
                        static_cast<const __bf16*>(weight), static_cast<__bf16*>(wpack), O, C,
-                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, total);
+                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, 0, total);
   } else {
     hipLaunchKernelGGL(pack_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
                        static_cast<const float*>(weight), static_cast<float*>(wpack), O, C, kh,
-                       kw, kc.CB, kc.NO, 4, kc.nchunk, total);
+                       kw, kc.CB, kc.NO, 4, kc.nchunk, kc.kind == 1 ? 1 : 0, total);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  if (kc.kind == 1) return launch_fused_wsk(kc, a, s);
   if (kc.bf16) {
     return kc.nhwc ? launch_cb<__bf16, true>(kc, a, s) : launch_cb<__bf16, false>(kc, a, s);
   }
