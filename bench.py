@@ -29,15 +29,17 @@ sys.path.insert(0, ROOT)
 METRIC = "deform-conv output pixels/s + effective TFLOP/s and % roofline, 256^2x64ch 7x7"
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("modulated_deformable_convolution_dcn_amd/csrc/dcn_kernels.hip",
-                  "modulated_deformable_convolution_dcn_amd/csrc/dcn_device.h")
+KERNEL_DIR = os.path.join(ROOT, "modulated_deformable_convolution_dcn_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
+    """sha256 over every kernel source and internal header (sorted by name)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_DIR, name), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()
 
 

@@ -34,12 +34,14 @@
 namespace dcn {
 
 template <int M, int NO, bool NHWC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_wsk_kernel(FusedArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+fused_wsk_kernel(FusedArgs a) {
   constexpr int CB = 64;          // channels per k-block
-  constexpr int NPASS = M / 16;   // gather passes: 16 pixels x 4 channel quads each
-  constexpr int MT = M / 16, NT = NO / 16;
+  constexpr int MT = M / 16;      // row groups = gather passes (16 pixels x 4 quads each)
+  constexpr int NT = NO / 16;
+  constexpr int NSLOT = 3;        // coefficient ring: taps whose tables are live at once
   constexpr int A_FLOATS = M * 16;                       // one wave's column tile
-  constexpr int MAIN_BYTES = 4 * 2 * A_FLOATS * 4 + 4 * 2 * M * 32;
+  constexpr int MAIN_BYTES = 4 * A_FLOATS * 4 + 4 * NSLOT * M * 32;
   constexpr int RST = M + 4;                             // reduction row stride
   constexpr int RED_BYTES = 4 * NO * RST * 4;
   constexpr int SMEM = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(NO % 16 == 0, "tile columns");
 
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  float* const As = reinterpret_cast<float*>(smem);                       // [w][2][M][16]
-  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * 2 * A_FLOATS * 4);  // [w][2][M]
-  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * 2 * A_FLOATS * 4 + 4 * 2 * M * 16);
-  float* const red = reinterpret_cast<float*>(smem);                      // [w][NO][RST]
+  float* const As = reinterpret_cast<float*>(smem);                          // [w][M][16]
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * A_FLOATS * 4);       // [w][slot][M]
+  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * A_FLOATS * 4 + 4 * NSLOT * M * 16);
+  float* const red = reinterpret_cast<float*>(smem);                         // [w][NO][RST]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -65,95 +67,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int NKB = a.K * a.nchunk;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
-  const float* maskp = static_cast<const float*>(a.mask);
-  const bool has_mask = maskp != nullptr;
+  const bool has_mask = a.mask != nullptr;
   const __amdgpu_buffer_rsrc_t offr = make_rsrc(a.offset, a.offset_bytes);
   const __amdgpu_buffer_rsrc_t mskr =
       make_rsrc(has_mask ? a.mask : a.offset, has_mask ? a.mask_bytes : 0u);
   const float* wblocks = static_cast<const float*>(a.wpack) +
                          (size_t)otile * a.K * a.nchunk * (CB * NO);
   const uint32_t row_bytes = (uint32_t)a.C * 4;
+  float* const Aw = As + wave * A_FLOATS;
+  f32x4* const Cww = Cw + wave * NSLOT * M;
+  u32x4* const Cow = Co + wave * NSLOT * M;
 
-  // ---- (a) coefficients: lane m computes pixel m's four corners for a tap
+  // ---- (a) coefficients.  Lane m owns pixel m of the tile (all four
+  // corners); the pixel's grid position is fixed, so it is computed once.
+  const int c_hw = hw0 + lane;
+  const bool c_in = c_hw < a.HoWo && lane < M;
+  const int c_ho = c_hw / a.Wo;
+  const int c_wo = c_hw - c_ho * a.Wo;
   float c_dy[2], c_dx[2], c_mk[2];
-  auto coef_load = [&](int kt, auto set_tag) {
-    constexpr int S = decltype(set_tag)::value;
-    const uint32_t hw = (uint32_t)(hw0 + lane);
-    const uint32_t ob = ((uint32_t)(b * 2 * a.K + 2 * kt) * (uint32_t)a.HoWo + hw) * 4;
-    const uint32_t mb = ((uint32_t)(b * a.K + kt) * (uint32_t)a.HoWo + hw) * 4;
-    c_dy[S] = load_scalar<float>(offr, ob);
-    c_dx[S] = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
-    c_mk[S] = load_scalar<float>(mskr, mb);
+  auto coef_addr = [&](int kt, uint32_t& ob, uint32_t& mb) {
+    ob = ((uint32_t)(b * 2 * a.K + 2 * kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
+    mb = ((uint32_t)(b * a.K + kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
   };
   auto coef_finish = [&](int kt, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
-    const int slot = kt & 1;
+    const int slot = kt % NSLOT;
     const int i = kt / a.kw;
     const int j = kt - i * a.kw;
-    const int hw = hw0 + lane;
-    const int ho = hw / a.Wo;
-    const int wo = hw - ho * a.Wo;
-    const TapPoint t = tap_point(c_dy[S], c_dx[S], ho - a.ph + i, wo - a.pw + j, a.H, a.W);
+    const TapPoint t = tap_point(c_dy[S], c_dx[S], c_ho - a.ph + i, c_wo - a.pw + j, a.H, a.W);
     const float mk = has_mask ? c_mk[S] : 1.0f;
     const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
     const float wv[4] = {hy * hx, hy * t.lx, t.ly * hx, t.ly * t.lx};
-    const bool in_tile = hw < a.HoWo;
     const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
     const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
+    const uint32_t base = (uint32_t)((b * a.H + y0) * a.W + x0) * row_bytes;
     f32x4 w4;
     u32x4 o4;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bool ok = in_tile && ((t.valid >> c) & 1u);
+      const bool ok = c_in && ((t.valid >> c) & 1u);
       w4[c] = ok ? wv[c] * mk : 0.0f;
-      o4[c] = ok ? (uint32_t)((b * a.H + y0 + (c >> 1)) * a.W + x0 + (c & 1)) * row_bytes
-                 : kNoCorner;
+      o4[c] = ok ? base + (uint32_t)((c >> 1) * a.W + (c & 1)) * row_bytes : kNoCorner;
     }
     if (lane < M) {
-      Cw[(wave * 2 + slot) * M + lane] = w4;
-      Co[(wave * 2 + slot) * M + lane] = o4;
+      Cww[slot * M + lane] = w4;
+      Cow[slot * M + lane] = o4;
     }
   };
+  auto coef_now = [&](int kt, auto set_tag) {  // prologue: load and finish at once
+    constexpr int S = decltype(set_tag)::value;
+    uint32_t ob, mb;
+    coef_addr(kt, ob, mb);
+    c_dy[S] = load_scalar<float>(offr, ob);
+    c_dx[S] = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
+    c_mk[S] = load_scalar<float>(mskr, mb);
+    coef_finish(kt, set_tag);
+  };
 
-  // ---- (b) corners: lane = (pixel of the pass, channel quad of the wave's 16)
+  // ---- (b) corners: lane = (pixel pp of a pass, channel quad q4 of the
+  // wave's 16).  gv[p] holds pass p's four corners of one block.
   const int pp = lane >> 2;
   const int q4 = lane & 3;
-  u32x4 gv[NPASS][4];
-  uint32_t goff[NPASS][4];  // byte offsets of the next block's corner loads
-  auto gather_offsets = [&](int kb) {
+  u32x4 gv[MT][4];
+  // Byte offset of this lane's channel quad inside a corner's channel vector
+  // for block kb, and whether that quad exists (C need not fill the block).
+  auto gather_base = [&](int kb, uint32_t& cbyte, bool& chan_ok) {
     const int kt = kb / a.nchunk;
-    const int cc = kb - kt * a.nchunk;
-    const int ch = cc * CB + wave * 16 + q4 * 4;
-    const bool chan_ok = ch < a.C;
-    const uint32_t cbyte = (uint32_t)ch * 4;
-    const u32x4* co = Co + (wave * 2 + (kt & 1)) * M;
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const u32x4 off = co[ps * 16 + pp];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) goff[ps][c] = chan_ok ? off[c] + cbyte : kNoCorner;
-    }
+    const int ch = (kb - kt * a.nchunk) * CB + wave * 16 + q4 * 4;
+    chan_ok = ch < a.C;
+    cbyte = (uint32_t)ch * 4;
+    return kt % NSLOT;
   };
   // Column tile row p holds the wave's 16 channels as 4 quads; quad q sits at
   // position q ^ ((p >> 2) & 3) so that both the blend writes (16 lanes = 4
   // pixels x 4 quads) and the MFMA reads (16 lanes = 16 pixels, one quad) hit
   // 64 distinct banks.
   auto a_index = [](int p, int q) { return p * 16 + ((q ^ ((p >> 2) & 3)) << 2); };
-  auto finish_gather = [&](int kb, int buf) {
-    const int kt = kb / a.nchunk;
-    const f32x4* cw = Cw + (wave * 2 + (kt & 1)) * M;
-    float* A = As + (wave * 2 + buf) * A_FLOATS;
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int p = ps * 16 + pp;
-      const u32x4 r = Ops<float>::blend(cw[p], gv[ps][0], gv[ps][1], gv[ps][2], gv[ps][3]);
-      *reinterpret_cast<u32x4*>(&A[a_index(p, q4)]) = r;
-    }
-  };
 
   // ---- weight fragments: block kb is [wave][nt][g][col][e] in the packed
-  // layout, channel 16*wave + 4g + e, column 16*nt + col; lane (col, g) of
-  // wave w reads its NT 16-byte pieces, one coalesced 1 KB run per nt.
+  // layout (channel 16*wave + 4g + e, column 16*nt + col); lane (col, g)
+  // reads NT 16-byte pieces, one coalesced 1 KB run per nt.
   const int rl = lane & 15;
   const int g = lane >> 4;
   f32x4 bw[2][NT];
@@ -161,96 +154,147 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return wblocks + (size_t)kb * (CB * NO) + (size_t)wave * (NT * 256) + (g * 16 + rl) * 4;
   };
 
-  // ---- (c) MFMA: k-slot g of step e is channel 16*wave + 4g + e, on both sides
+  // ---- (c) MFMA: k-slot g of step e is channel 16*wave + 4g + e, on both
+  // sides; row group mt uses column-tile rows [16 mt, 16 mt + 16).
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 af[MT];
 
-  // ---- prologue: coefficients of taps 0 and 1, registers for the tap the
-  // first step turns into coefficients, weight and column tile of block 0
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  const int k1 = a.K > 1 ? 1 : 0;
-  coef_load(0, S0{});
-  coef_finish(0, S0{});
-  coef_load(k1, S1{});
-  coef_finish(k1, S1{});
+  auto clampb = [&](int kb) { return kb < NKB ? kb : NKB - 1; };
+  auto clampt = [&](int kt) { return kt < a.K ? kt : a.K - 1; };
+
+  // ---- prologue: coefficient tables of taps 0..2, offsets of the tap the
+  // first step finishes, weights of block 0, all corners of block 0, pass 0
+  // blended, pass 0 of block 1 in flight.
+  coef_now(0, S0{});
+  coef_now(clampt(1), S0{});
+  coef_now(clampt(2), S0{});
   {
-    const int t = 2 / a.nchunk;
-    coef_load(t < a.K ? t : a.K - 1, S0{});
+    uint32_t ob, mb;
+    coef_addr(clampt(3 / a.nchunk), ob, mb);
+    c_dy[0] = load_scalar<float>(offr, ob);
+    c_dx[0] = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
+    c_mk[0] = load_scalar<float>(mskr, mb);
   }
   {
     const float* src = b_src(0);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bw[0][nt] = *reinterpret_cast<const f32x4*>(src + nt * 256);
   }
-  gather_offsets(0);
+  {
+    uint32_t cb0;
+    bool ok0;
+    const int sl0 = gather_base(0, cb0, ok0);
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps)
+    for (int p = 0; p < MT; ++p) {
+      const u32x4 off = Cow[sl0 * M + p * 16 + pp];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) gv[ps][c] = load16(xr, goff[ps][c]);
-  finish_gather(0, 0);
-
-  // One step = block kb's MFMAs with the loads for later blocks threaded
-  // through them: the texture-address queue is shared by all waves of a CU,
-  // and a burst of loads would stall the wave at issue, before its MFMAs.
-  // Load order: corners of kb+1 (needed at the end of this step), weight
-  // fragments of kb+1 (next step), offsets/mask of a tap three steps ahead
-  // (turned into coefficients next step); one load after every second MFMA.
-  constexpr int NG = NPASS * 4;       // corner loads
-  constexpr int NLOAD = NG + NT + 3;  // + weight fragments + dy, dx, mask
-  constexpr int NMFMA = 4 * MT * NT;
-  static_assert(2 * NLOAD <= NMFMA, "every load rides behind two MFMAs");
-  auto step = [&](int kb, auto par) {
-    constexpr int P = decltype(par)::value;  // kb & 1
-    using SP = std::integral_constant<int, P>;
-    const int kn = kb + 1 < NKB ? kb + 1 : NKB - 1;
-    const int tl = (kb + 3) / a.nchunk;
-    const int tload = tl < a.K ? tl : a.K - 1;
-    gather_offsets(kn);
-    const float* bsrc = b_src(kn);
-    const uint32_t c_hw = (uint32_t)(hw0 + lane);
-    const uint32_t c_ob = ((uint32_t)(b * 2 * a.K + 2 * tload) * (uint32_t)a.HoWo + c_hw) * 4;
-    const uint32_t c_mb = ((uint32_t)(b * a.K + tload) * (uint32_t)a.HoWo + c_hw) * 4;
-    const float* A = As + (wave * 2 + P) * A_FLOATS;
-    f32x4 af[MT];
+      for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok0 ? off[c] + cb0 : kNoCorner);
+    }
+    const f32x4 w = Cww[sl0 * M + pp];
+    *reinterpret_cast<u32x4*>(&Aw[a_index(pp, q4)]) =
+        Ops<float>::blend(w, gv[0][0], gv[0][1], gv[0][2], gv[0][3]);
+    uint32_t cb1;
+    bool ok1;
+    const int sl1 = gather_base(clampb(1), cb1, ok1);
+    const u32x4 off = Cow[sl1 * M + pp];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      af[mt] = *reinterpret_cast<const f32x4*>(&A[a_index(mt * 16 + rl, g)]);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<NMFMA>([&](auto I) {
-      constexpr int idx = decltype(I)::value;
-      constexpr int e = idx / (MT * NT), mt = (idx / NT) % MT, nt = idx % NT;
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][e], bw[P][nt][e], acc[mt][nt], 0,
-                                                         0, 0);
-      if constexpr (idx % 2 == 1 && idx / 2 < NLOAD) {
-        constexpr int L = idx / 2;
-        if constexpr (L < NG) {
-          gv[L / 4][L % 4] = load16(xr, goff[L / 4][L % 4]);
-        } else if constexpr (L < NG + NT) {
-          bw[P ^ 1][L - NG] = *reinterpret_cast<const f32x4*>(bsrc + (L - NG) * 256);
-        } else if constexpr (L == NG + NT) {
-          c_dy[P ^ 1] = load_scalar<float>(offr, c_ob);
-        } else if constexpr (L == NG + NT + 1) {
-          c_dx[P ^ 1] = load_scalar<float>(offr, c_ob + (uint32_t)a.HoWo * 4);
-        } else {
-          c_mk[P ^ 1] = load_scalar<float>(mskr, c_mb);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    const int tc = (kb + 2) / a.nchunk;
-    if (tc * a.nchunk == kb + 2 && tc < a.K) coef_finish(tc, SP{});
-    finish_gather(kn, P ^ 1);
-  };
-  int kb = 0;
-  for (; kb + 1 < NKB; kb += 2) {
-    step(kb, S0{});
-    step(kb + 1, S1{});
+    for (int c = 0; c < 4; ++c) gv[0][c] = load16(xr, ok1 ? off[c] + cb1 : kNoCorner);
+    af[0] = *reinterpret_cast<const f32x4*>(&Aw[a_index(rl, g)]);
   }
-  if (kb < NKB) step(kb, S0{});
+
+  // ---- one step = the MFMAs of block s, row group by row group.  Under the
+  // MFMAs of row group q run: the blend of pass q+1 of block s (pass 0 of
+  // block s+1 under the last group), the corner loads of the block after that
+  // pass's block into the registers the blend just freed (one full step
+  // before they are blended), the column-tile read for the next row group;
+  // in group 0 the weight fragments of block s+1 and the offsets/mask of a
+  // tap four steps ahead; in the last group the coefficient table of tap
+  // (s+3)/nchunk (from offsets loaded one step earlier).  Each item is pinned
+  // after a given MFMA, so the matrix pipe never waits for a burst of other
+  // work, and every load has a static position, so each wait is exact.
+  constexpr int NMF = 4 * NT;  // MFMAs per row group
+  auto step = [&](int s, auto par) {
+    constexpr int P = decltype(par)::value;  // s & 1: weight / offset register sets
+    using SP = std::integral_constant<int, P>;
+    const int tl = (s + 4) / a.nchunk;
+    uint32_t c_ob, c_mb;
+    coef_addr(clampt(tl), c_ob, c_mb);
+    const float* bsrc = b_src(clampb(s + 1));
+    static_for<MT>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      constexpr int p = (q + 1) % MT;           // pass blended under this group
+      constexpr bool LAST = q + 1 == MT;
+      const int blk = clampb(LAST ? s + 1 : s);  // block of that pass
+      const int nblk = clampb(blk + 1);          // block whose pass-p corners load next
+      uint32_t cb_b, cb_n;
+      bool ok_b, ok_n;
+      const int sl_b = gather_base(blk, cb_b, ok_b);
+      const int sl_n = gather_base(nblk, cb_n, ok_n);
+      (void)cb_b;
+      (void)ok_b;
+      f32x4 w;
+      u32x4 off, r;
+      constexpr int NACT = 12 + (q == 0 ? NT + 3 : 0) + (LAST ? 1 : 0);
+      static_for<NMF>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int e = j / NT, nt = j % NT;
+        acc[q][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[q][e], bw[P][nt][e], acc[q][nt], 0,
+                                                          0, 0);
+        static_for<NACT>([&](auto X) {
+          constexpr int x = decltype(X)::value;
+          if constexpr (x * NMF / NACT == j) {  // action x rides behind MFMA j
+            if constexpr (x == 0) {
+              w = Cww[sl_b * M + p * 16 + pp];
+            } else if constexpr (x == 1) {
+              off = Cow[sl_n * M + p * 16 + pp];
+            } else if constexpr (x <= 5) {
+              constexpr int c = x - 2;
+              const f32x4 v = __builtin_bit_cast(f32x4, gv[p][c]);
+              if constexpr (c == 0) {
+                r = __builtin_bit_cast(u32x4, v * w[0]);
+              } else {
+                f32x4 t = __builtin_bit_cast(f32x4, r);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) t[k] = __builtin_fmaf(w[c], v[k], t[k]);
+                r = __builtin_bit_cast(u32x4, t);
+              }
+            } else if constexpr (x == 6) {
+              *reinterpret_cast<u32x4*>(&Aw[a_index(p * 16 + pp, q4)]) = r;
+            } else if constexpr (x == 7) {
+              af[p] = *reinterpret_cast<const f32x4*>(&Aw[a_index(p * 16 + rl, g)]);
+            } else if constexpr (x <= 11) {
+              constexpr int c = x - 8;
+              gv[p][c] = load16(xr, ok_n ? off[c] + cb_n : kNoCorner);
+            } else if constexpr (q == 0 && x < 12 + NT) {
+              bw[P ^ 1][x - 12] = *reinterpret_cast<const f32x4*>(bsrc + (x - 12) * 256);
+            } else if constexpr (q == 0 && x == 12 + NT) {
+              c_dy[P ^ 1] = load_scalar<float>(offr, c_ob);
+            } else if constexpr (q == 0 && x == 13 + NT) {
+              c_dx[P ^ 1] = load_scalar<float>(offr, c_ob + (uint32_t)a.HoWo * 4);
+            } else if constexpr (q == 0 && x == 14 + NT) {
+              c_mk[P ^ 1] = load_scalar<float>(mskr, c_mb);
+            } else if constexpr (LAST) {
+              const int tc = (s + 3) / a.nchunk;
+              if (tc * a.nchunk == s + 3 && tc < a.K) coef_finish(tc, SP{});
+            }
+          }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+  int s = 0;
+  for (; s + 1 < NKB; s += 2) {
+    step(s, S0{});
+    step(s + 1, S1{});
+  }
+  if (s < NKB) step(s, S0{});
 
   // ---- epilogue: sum the four waves' partial tiles through LDS, + bias, store
   __syncthreads();  // every wave is done with the column tiles and coefficients
