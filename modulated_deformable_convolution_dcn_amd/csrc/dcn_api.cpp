@@ -55,7 +55,14 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
   dcn::KernelConfig kc{};
   kc.bf16 = d.in_dtype == DCN_BF16;
   const int O = d.out_ch, C = d.in_ch;
-  if (!kc.bf16 && O > 16 && O <= 128 && C >= 32) {
+  if (!kc.bf16 && O > 16 && O <= 64 && C >= 32) {
+    // fp32, up to 64 output channels: each wave owns 32 pixels x 32
+    // channels of every k-block, no workgroup barrier (dcn_quad.hip)
+    kc.kind = 2;
+    kc.CB = 64;
+    kc.NO = 64;
+    kc.M = 64;
+  } else if (!kc.bf16 && O > 16 && O <= 128 && C >= 32) {
     // fp32 with a small output tile: k split over the four waves, no
     // workgroup barrier in the main loop (dcn_wsk.hip)
     kc.kind = 1;

@@ -1,0 +1,358 @@
+// dcn_quad.hip -- fp32 fused DCNv2 forward: each wave owns 32 pixels x 32
+// channels of every k-block.
+//
+// Same operator as the other kernels (page 1, "deform_conv.py": sample the
+// input bilinearly at (h - pad + i + dy, w - pad + j + dx), corners outside
+// count as zero, times the mask, contract over (tap, channel) with the
+// weight, + bias).  This kernel serves fp32 problems with up to 64 output
+// channels -- the BiRefNet-decoder-like 64 -> 64, 7x7 shape.
+//
+// A workgroup is 4 waves = 64 consecutive output pixels x 64 output
+// channels; every k-block is one tap x 64 input channels.  Wave (h, c) owns
+// pixels [32h, 32h+32) and channels [32c, 32c+32) of each block:
+//   * its corner loads are 8 lanes x 16 B = one 128-byte line per pixel
+//     corner (as cheap for the texture-address unit as a full 256-byte
+//     vector, half the cost of the 64-byte runs a 16-channel split needs);
+//   * its column tile, coefficient table and weight fragments (loaded from
+//     memory straight into registers in MFMA order) are private, so the
+//     main loop has no workgroup barrier;
+//   * it accumulates 32 x 64 partial outputs over its channel half; the two
+//     halves are summed through LDS once at the end.
+// The choice keeps the per-MFMA instruction mix small: on gfx950 every VALU
+// op or LDS read issued beside the MFMAs costs matrix-pipe time, and this
+// split needs 4 LDS fragment reads and 8 weight loads per 64 MFMAs.
+//
+// Software pipeline (single column buffer, two 16-row groups): step s runs
+// the MFMAs of block s rows 0-15 while blending block s rows 16-31 (passes
+// 2, 3), then rows 16-31 while blending block s+1 rows 0-15 (passes 0, 1).
+// Each blended pass frees its corner registers, which immediately take the
+// same pass of the next block (one full step before they are needed).
+
+#include <type_traits>
+
+#include "dcn_device.h"
+#include "dcn_launch.h"
+
+namespace dcn {
+
+template <bool NHWC, bool FULLC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+fused_quad_kernel(FusedArgs a) {
+  constexpr int M = 64;           // output pixels per workgroup
+  constexpr int NO = 64;          // output channels per workgroup
+  constexpr int CB = 64;          // channels per k-block
+  constexpr int PW = 32;          // pixels per wave
+  constexpr int NT = NO / 16;     // 16-column MFMA tiles
+  constexpr int AST = 36;         // column-tile row stride (32 channels + pad)
+  constexpr int NSLOT = 3;        // coefficient ring
+  constexpr int A_FLOATS = PW * AST;
+  constexpr int MAIN_BYTES = 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 32;
+  constexpr int RST = PW + 4;
+  constexpr int RED_BYTES = 4 * NO * RST * 4;
+  constexpr int SMEM = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
+
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wh = wave >> 1;  // pixel half
+  const int wc = wave & 1;   // channel half
+
+  float* const Aw = reinterpret_cast<float*>(smem) + wave * A_FLOATS;
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * A_FLOATS * 4) + wave * NSLOT * PW;
+  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 16) +
+                    wave * NSLOT * PW;
+  float* const red = reinterpret_cast<float*>(smem);  // [wave][NO][RST]
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int otile = logical % a.n_otiles;
+  const int t2 = logical / a.n_otiles;
+  const int tile = t2 % a.tiles_per_img;
+  const int b = t2 / a.tiles_per_img;
+  const int hw0 = tile * M + wh * PW;  // first pixel of this wave
+  const int NKB = a.K * a.nchunk;
+  auto clampb = [&](int kb) { return kb < NKB ? kb : NKB - 1; };
+  auto clampt = [&](int kt) { return kt < a.K ? kt : a.K - 1; };
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const bool has_mask = a.mask != nullptr;
+  const __amdgpu_buffer_rsrc_t offr = make_rsrc(a.offset, a.offset_bytes);
+  const __amdgpu_buffer_rsrc_t mskr =
+      make_rsrc(has_mask ? a.mask : a.offset, has_mask ? a.mask_bytes : 0u);
+  const float* wblocks = static_cast<const float*>(a.wpack) +
+                         (size_t)otile * a.K * a.nchunk * (CB * NO);
+  const uint32_t row_bytes = (uint32_t)a.C * 4;
+
+  // ---- (a) coefficients: lane l -> pixel l & 31, corners 2(l>>5), 2(l>>5)+1
+  const int c_px = lane & 31;
+  const int c_pair = lane >> 5;
+  const int c_hw = hw0 + c_px;
+  const bool c_in = c_hw < a.HoWo;
+  const int c_ho = c_hw / a.Wo;
+  const int c_wo = c_hw - c_ho * a.Wo;
+  float c_dy[2], c_dx[2], c_mk[2];
+  auto coef_load = [&](int kt, float& dy, float& dx, float& mk) {
+    const uint32_t ob = ((uint32_t)(b * 2 * a.K + 2 * kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
+    const uint32_t mb = ((uint32_t)(b * a.K + kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
+    dy = load_scalar<float>(offr, ob);
+    dx = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
+    mk = load_scalar<float>(mskr, mb);
+  };
+  auto coef_finish = [&](int kt, float dy, float dx, float mkr) {
+    const int slot = kt % NSLOT;
+    const int i = kt / a.kw;
+    const int j = kt - i * a.kw;
+    const TapPoint t = tap_point(dy, dx, c_ho - a.ph + i, c_wo - a.pw + j, a.H, a.W);
+    const float mk = has_mask ? mkr : 1.0f;
+    // corners (a, 0) and (a, 1) with a = c_pair
+    const float wy = c_pair ? t.ly : 1.0f - t.ly;
+    const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
+    const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
+    const uint32_t base = (uint32_t)((b * a.H + y0 + c_pair) * a.W + x0) * row_bytes;
+    const bool ok0 = c_in && ((t.valid >> (2 * c_pair)) & 1u);
+    const bool ok1 = c_in && ((t.valid >> (2 * c_pair + 1)) & 1u);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 w2 = {ok0 ? wy * (1.0f - t.lx) * mk : 0.0f, ok1 ? wy * t.lx * mk : 0.0f};
+    const u32x2 o2 = {ok0 ? base : kNoCorner, ok1 ? base + row_bytes : kNoCorner};
+    *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(&Cw[slot * PW + c_px]) + 2 * c_pair) = w2;
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&Co[slot * PW + c_px]) + 2 * c_pair) = o2;
+  };
+
+  // ---- (b) corners: lane = (pixel pp of an 8-pixel pass, 16-byte slice sl
+  // of the wave's 32 channels); pass p covers the wave's pixels 8p .. 8p+7.
+  const int pp = lane >> 3;
+  const int sl = lane & 7;
+  u32x4 gv[4][4];
+  auto chan = [&](int kb, uint32_t& cbyte) {
+    const int kt = kb / a.nchunk;
+    const int ch = (kb - kt * a.nchunk) * CB + wc * 32 + sl * 4;
+    cbyte = (uint32_t)ch * 4;
+    return FULLC || ch < a.C;
+  };
+  auto slot_of = [&](int kb) { return (kb / a.nchunk) % NSLOT; };
+
+  // ---- (c) MFMA: k-slot g (lane / 16) owns the wave's channels 8g .. 8g+7;
+  // fragment read q holds channels 8g + 4q + [0, 4), i.e. k-steps 4q .. 4q+3.
+  // Weight block layout [half][nt][q][g][col][e] (channel 32*half + 8g + 4q + e,
+  // output 16*nt + col): the wave's 8 pieces are 1 KB coalesced runs.
+  const int rl = lane & 15;
+  const int g = lane >> 4;
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 af[2][2];      // [row group][q]
+  f32x4 bw[2][NT * 2];  // [set][nt * 2 + q]
+  auto b_src = [&](int kb) {
+    return wblocks + (size_t)kb * (CB * NO) + (size_t)wc * (NT * 2 * 256) + (g * 16 + rl) * 4;
+  };
+  auto a_frag = [&](int mt, int q) {
+    return *reinterpret_cast<const f32x4*>(&Aw[(mt * 16 + rl) * AST + g * 8 + q * 4]);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // ---- prologue
+  {
+    float dy, dx, mk;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      coef_load(clampt(t), dy, dx, mk);
+      coef_finish(clampt(t), dy, dx, mk);
+    }
+  }
+  coef_load(clampt(3 / a.nchunk), c_dy[0], c_dx[0], c_mk[0]);
+  coef_load(clampt(4 / a.nchunk), c_dy[1], c_dx[1], c_mk[1]);
+  {
+    const float* src = b_src(0);
+#pragma unroll
+    for (int k = 0; k < NT * 2; ++k) bw[0][k] = *reinterpret_cast<const f32x4*>(src + k * 256);
+  }
+  {
+    uint32_t cb0, cb1;
+    const bool ok0 = chan(0, cb0);
+    const bool ok1 = chan(clampb(1), cb1);
+    const int s0 = slot_of(0), s1 = slot_of(clampb(1));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x4 off = Co[s0 * PW + p * 8 + pp];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok0 ? off[c] + cb0 : kNoCorner);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const u32x4 r = Ops<float>::blend(Cw[s0 * PW + p * 8 + pp], gv[p][0], gv[p][1], gv[p][2],
+                                        gv[p][3]);
+      *reinterpret_cast<u32x4*>(&Aw[(p * 8 + pp) * AST + sl * 4]) = r;
+      const u32x4 off = Co[s1 * PW + p * 8 + pp];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok1 ? off[c] + cb1 : kNoCorner);
+    }
+    af[0][0] = a_frag(0, 0);
+    af[0][1] = a_frag(0, 1);
+  }
+
+  // ---- one step s: two groups of 32 MFMAs with the other work pinned
+  // between them (one action per MFMA slot, in this order).
+  // Group 0 (rows 0-15 of block s): blend of block s passes 2, 3 (rows
+  // 16-31) and their corner loads for block s+1; fragments of rows 16-31;
+  // weight fragments of block s+1.
+  // Group 1 (rows 16-31): blend of block s+1 passes 0, 1 (rows 0-15) and
+  // their corner loads for block s+2; fragments of rows 0-15 of block s+1;
+  // the coefficient table of tap (s+3)/nchunk from offsets loaded two steps
+  // ago, then the offsets of tap (s+5)/nchunk.
+  // Per pass pair: 4 table reads, then per pass 4 blend terms, the tile
+  // write and 4 corner loads (22 actions).
+  constexpr int NMF = 8 * NT;  // MFMAs per group
+  constexpr int NPA = 22;
+  auto step = [&](int s, auto par) {
+    constexpr int P = decltype(par)::value;  // s & 1
+    const int n1 = clampb(s + 1), n2 = clampb(s + 2);
+    const int sl_s = slot_of(s), sl_1 = slot_of(n1), sl_2 = slot_of(n2);
+    uint32_t cb1, cb2;
+    const bool ok1 = chan(n1, cb1);
+    const bool ok2 = chan(n2, cb2);
+    const float* bsrc = b_src(n1);
+    const int tc = (s + 3) / a.nchunk;
+    const bool coef_due = tc * a.nchunk == s + 3 && tc < a.K;
+    const int tl = clampt((s + 5) / a.nchunk);
+    static_for<2>([&](auto MT) {
+      constexpr int mt = decltype(MT)::value;
+      constexpr int pa = mt == 0 ? 2 : 0;  // passes blended under this group
+      constexpr int NACT = NPA + 2 + (mt == 0 ? NT * 2 : 2);
+      // group 0: blend block s, load block s+1; group 1: blend s+1, load s+2
+      const int slw = mt == 0 ? sl_s : sl_1;
+      const int slo = mt == 0 ? sl_1 : sl_2;
+      const bool okn = mt == 0 ? ok1 : ok2;
+      const uint32_t cbn = mt == 0 ? cb1 : cb2;
+      f32x4 w[2];
+      u32x4 off[2];
+      f32x4 r;
+      auto act = [&](auto X) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x < 4) {
+          constexpr int pi = x >> 1;
+          if constexpr ((x & 1) == 0) w[pi] = Cw[slw * PW + (pa + pi) * 8 + pp];
+          else off[pi] = Co[slo * PW + (pa + pi) * 8 + pp];
+        } else if constexpr (x < NPA) {
+          constexpr int pi = (x - 4) / 9, y = (x - 4) % 9, p = pa + pi;
+          if constexpr (y < 4) {
+            const f32x4 v = __builtin_bit_cast(f32x4, gv[p][y]);
+            if constexpr (y == 0) {
+              r = v * w[pi][0];
+            } else {
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk) r[kk] = __builtin_fmaf(w[pi][y], v[kk], r[kk]);
+            }
+          } else if constexpr (y == 4) {
+            *reinterpret_cast<f32x4*>(&Aw[(p * 8 + pp) * AST + sl * 4]) = r;
+          } else {
+            constexpr int c = y - 5;
+            gv[p][c] = load16(xr, okn ? off[pi][c] + cbn : kNoCorner);
+          }
+        } else if constexpr (x < NPA + 2) {
+          // rows 16-31 of block s (group 0) / rows 0-15 of block s+1 (group 1)
+          af[mt ^ 1][x - NPA] = a_frag(mt ^ 1, x - NPA);
+        } else if constexpr (mt == 0) {
+          bw[P ^ 1][x - NPA - 2] = *reinterpret_cast<const f32x4*>(bsrc + (x - NPA - 2) * 256);
+        } else if constexpr (x == NPA + 2) {
+          if (coef_due) coef_finish(tc, c_dy[P], c_dx[P], c_mk[P]);
+        } else {
+          coef_load(tl, c_dy[P], c_dx[P], c_mk[P]);
+        }
+      };
+      static_for<NMF>([&](auto J) {
+        constexpr int jj = decltype(J)::value;
+        constexpr int k = jj / NT, nt = jj % NT;  // k-step 0..7, tile
+        constexpr int q = k / 4, e = k % 4;
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][q][e], bw[P][nt * 2 + q][e],
+                                                           acc[mt][nt], 0, 0, 0);
+        static_for<NACT>([&](auto X) {
+          constexpr int x = decltype(X)::value;
+          if constexpr (x * NMF / NACT == jj) act(X);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+  int s = 0;
+  for (; s + 1 < NKB; s += 2) {
+    step(s, S0{});
+    step(s + 1, S1{});
+  }
+  if (s < NKB) step(s, S0{});
+
+  // ---- epilogue: sum the two channel halves of each pixel half, + bias, store
+  __syncthreads();  // every wave is done with its column tile and tables
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(&red[(wave * NO + nt * 16 + rl) * RST + mt * 16 + g * 4]) =
+          acc[mt][nt];
+  __syncthreads();
+  const float* biasp = static_cast<const float*>(a.bias);
+  const int base_hw = tile * M;
+  if constexpr (!NHWC) {
+    // thread -> (pixel half, output channel, run of 4 pixels)
+    for (int e = tid; e < 2 * NO * (PW / 4); e += 256) {
+      const int h = e / (NO * (PW / 4));
+      const int rem = e - h * NO * (PW / 4);
+      const int col = rem / (PW / 4);
+      const int r4 = rem - col * (PW / 4);
+      const int o = otile * NO + col;
+      if (o >= a.O) continue;
+      const int w0 = h * 2;  // waves (h, 0) and (h, 1)
+      f32x4 v = *reinterpret_cast<const f32x4*>(&red[(w0 * NO + col) * RST + r4 * 4]);
+      v += *reinterpret_cast<const f32x4*>(&red[((w0 + 1) * NO + col) * RST + r4 * 4]);
+      v += biasp ? biasp[o] : 0.0f;
+      const int hw = base_hw + h * PW + r4 * 4;
+      float* dst = a.out + ((size_t)b * a.O + o) * a.HoWo + hw;
+      if (a.vec_store && hw + 3 < a.HoWo) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (hw + rr < a.HoWo) dst[rr] = v[rr];
+      }
+    }
+  } else {
+    for (int e = tid; e < M * NO; e += 256) {
+      const int col = e % NO;
+      const int px = e / NO;
+      const int h = px / PW, row = px - h * PW;
+      const int o = otile * NO + col;
+      const int hw = base_hw + px;
+      if (o >= a.O || hw >= a.HoWo) continue;
+      const float v = red[(2 * h * NO + col) * RST + row] + red[((2 * h + 1) * NO + col) * RST + row] +
+                      (biasp ? biasp[o] : 0.0f);
+      a.out[((size_t)b * a.HoWo + hw) * a.O + o] = v;
+    }
+  }
+}
+
+bool quad_supported(const KernelConfig& kc) {
+  return !kc.bf16 && kc.CB == 64 && kc.NO == 64 && kc.M == 64;
+}
+
+hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * kc.n_otiles;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
+  const bool fullc = a.C % 64 == 0;
+  const dim3 grid((unsigned)nblk), block(256);
+  if (kc.nhwc) {
+    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_quad_kernel<true, false>), grid, block, 0, s, a);
+  } else {
+    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_quad_kernel<false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dcn

@@ -20,6 +20,7 @@ W = synth.WORKLOADS
 # Full-output comparisons: sizes the oracle finishes in seconds that still
 # span several 64-pixel tiles, ragged tails, several channel chunks and
 # output-channel tiles.
+E = W["edge_stress_fp32"]
 FULL_CASES = {
     "tiny_fp32": W["tiny_fp32"],
     "birefnet512_fp32": W["birefnet512_fp32"],
@@ -34,6 +35,17 @@ FULL_CASES = {
                                                      ph=1, pw=1),
     "bf16_c40_o20": W["detection_bf16"].scaled(B=1, C=40, O=20, H=9, W=23, kh=5, kw=3, ph=2,
                                                pw=0),
+    # fp32 tiles of at most 64 output channels (32 x 32 per wave): a 32-channel
+    # input leaves one channel half empty; 96 = one full and one half chunk;
+    # 192 = three chunks (coefficient ring reuse); K = 1; odd Ho*Wo; B = 2
+    "q_c32_o48": E.scaled(B=2, C=32, O=48, H=11, W=13, kh=3, kw=3, ph=1, pw=1),
+    "q_c96_o64": E.scaled(B=1, C=96, O=64, H=12, W=12, kh=5, kw=5, ph=2, pw=2),
+    "q_c192_o64": E.scaled(B=1, C=192, O=64, H=9, W=10, kh=3, kw=3, ph=1, pw=1),
+    "q_c36_o17_k1": E.scaled(B=2, C=36, O=17, H=7, W=9, kh=1, kw=1, ph=0, pw=0),
+    "q_c128_o64": E.scaled(B=2, C=128, O=64, H=20, W=19, kh=3, kw=3, ph=1, pw=1),
+    # fp32 tiles of 65..128 output channels (k split over waves)
+    "w_c32_o100": E.scaled(B=2, C=32, O=100, H=10, W=11, kh=3, kw=3, ph=1, pw=1),
+    "w_c96_o128": E.scaled(B=1, C=96, O=128, H=9, W=15, kh=3, kw=5, ph=1, pw=2),
 }
 
 
