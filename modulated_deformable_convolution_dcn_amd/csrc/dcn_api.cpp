@@ -62,6 +62,13 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
     kc.CB = 64;
     kc.NO = 64;
     kc.M = 64;
+  } else if (kc.bf16 && O > 128 && C >= 32) {
+    // bf16, wide outputs: 128 pixels x 256 output channels per workgroup,
+    // one workgroup per CU (dcn_bf16.hip)
+    kc.kind = 3;
+    kc.CB = C <= 64 ? 64 : C <= 128 ? 128 : 256;
+    kc.NO = 256;
+    kc.M = 128;
   } else if (!kc.bf16 && O > 16 && O <= 128 && C >= 32) {
     // fp32 with a small output tile: k split over the four waves, no
     // workgroup barrier in the main loop (dcn_wsk.hip)

@@ -323,7 +323,10 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 //            B fragments for a block are one contiguous run per nt;
 //   layout 2 (32 x 32 per wave, CB = 64, VEC = 4): [half][NO/16][q][g][16][4]
 //            = channel 32*half + 8g + 4q + e, output 16*nt + col -- one
-//            1 KB run per (nt, q) for the wave owning that channel half.
+//            1 KB run per (nt, q) for the wave owning that channel half;
+//   layout 3 (bf16 16x16x32 fragments, VEC = 8): [CB/32][NO/16][g][16][8]
+//            = channel 32q + 8g + e, output 16*nt + col -- fragment (q, nt)
+//            is one 1 KB run in lane order.
 template <class T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* __restrict__ wp,
                                                    int O, int C, int kh, int kw, int CB, int NO,
@@ -347,6 +350,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* _
       const int e = ib & 3, col = (ib >> 2) & 15, g = (ib >> 6) & 3;
       const int nt = (ib >> 8) % (NO / 16), wv = (ib >> 8) / (NO / 16);
       c_in = 16 * wv + 4 * g + e;
+      o_in = 16 * nt + col;
+    } else if (layout == 3) {
+      const int e = ib & 7, col = (ib >> 3) & 15, g = (ib >> 7) & 3;
+      const int nt = (ib >> 9) % (NO / 16), q = (ib >> 9) / (NO / 16);
+      c_in = 32 * q + 8 * g + e;
       o_in = 16 * nt + col;
     } else {
       const int e = ib & 3, col = (ib >> 2) & 15, g = (ib >> 6) & 3, q = (ib >> 8) & 1;
@@ -475,6 +483,7 @@ unsigned grid_for(int64_t total) {
 bool config_supported(const KernelConfig& kc) {
   if (kc.kind == 1) return wsk_supported(kc);
   if (kc.kind == 2) return quad_supported(kc);
+  if (kc.kind == 3) return bf16w_supported(kc);
   if (kc.M != 64) return false;
   if (kc.NO != 16 && kc.NO != 64 && kc.NO != 128 && kc.NO != 256) return false;
   if (kc.bf16) return kc.CB == 32 || kc.CB == 64;
@@ -492,7 +501,7 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
   if (kc.bf16) {
     hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s,
                        static_cast<const __bf16*>(weight), static_cast<__bf16*>(wpack), O, C,
-                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, 0, total);
+                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, kc.kind == 3 ? 3 : 0, total);
   } else {
     hipLaunchKernelGGL(pack_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
                        static_cast<const float*>(weight), static_cast<float*>(wpack), O, C, kh,
@@ -504,6 +513,7 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
 hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
   if (kc.kind == 1) return launch_fused_wsk(kc, a, s);
   if (kc.kind == 2) return launch_fused_quad(kc, a, s);
+  if (kc.kind == 3) return launch_fused_bf16w(kc, a, s);
   if (kc.bf16) {
     return kc.nhwc ? launch_cb<__bf16, true>(kc, a, s) : launch_cb<__bf16, false>(kc, a, s);
   }

@@ -10,7 +10,8 @@ namespace dcn {
 // Tile configuration chosen once per plan.
 struct KernelConfig {
   int kind;       // 0: shared column tile (dcn_kernels.hip), 1: k split over waves
-                  // (dcn_wsk.hip), 2: 32 pixels x 32 channels per wave (dcn_quad.hip)
+                  // (dcn_wsk.hip), 2: 32 pixels x 32 channels per wave (dcn_quad.hip),
+                  // 3: bf16, 128 pixels x 256 outputs per workgroup (dcn_bf16.hip)
   int bf16;       // 0: fp32 operands, 1: bf16 operands
   int M;          // output pixels per workgroup
   int CB;         // channels per k-block (one tap, one channel chunk)
@@ -55,6 +56,10 @@ hipError_t launch_fused_wsk(const KernelConfig& kc, const FusedArgs& a, hipStrea
 // The 32-pixel x 32-channel-per-wave kernel (fp32, 64-wide output tiles).
 bool quad_supported(const KernelConfig& kc);
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+
+// The wide bf16 kernel (128 pixels x 256 output channels per workgroup).
+bool bf16w_supported(const KernelConfig& kc);
+hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
 
 hipError_t launch_coords(int bf16, const void* offset, int32_t* y0x0, uint8_t* valid4, int B,
                          int K, int kw, int Ho, int Wo, int ph, int pw, int H, int W,

@@ -21,6 +21,7 @@ W = synth.WORKLOADS
 # span several 64-pixel tiles, ragged tails, several channel chunks and
 # output-channel tiles.
 E = W["edge_stress_fp32"]
+D = W["detection_bf16"]
 FULL_CASES = {
     "tiny_fp32": W["tiny_fp32"],
     "birefnet512_fp32": W["birefnet512_fp32"],
@@ -43,6 +44,12 @@ FULL_CASES = {
     "q_c192_o64": E.scaled(B=1, C=192, O=64, H=9, W=10, kh=3, kw=3, ph=1, pw=1),
     "q_c36_o17_k1": E.scaled(B=2, C=36, O=17, H=7, W=9, kh=1, kw=1, ph=0, pw=0),
     "q_c128_o64": E.scaled(B=2, C=128, O=64, H=20, W=19, kh=3, kw=3, ph=1, pw=1),
+    # bf16 with more than 128 output channels (128 pixels x 256 outputs per
+    # workgroup): ragged channel chunk, two output tiles, odd Ho*Wo, K = 1
+    "b_c72_o200": D.scaled(B=3, C=72, O=200, H=9, W=13, kh=3, kw=3, ph=1, pw=1),
+    "b_c128_o300": D.scaled(B=1, C=128, O=300, H=11, W=12, kh=3, kw=2, ph=1, pw=0),
+    "b_c256_o256_k1": D.scaled(B=2, C=256, O=256, H=7, W=9, kh=1, kw=1, ph=0, pw=0),
+    "b_c32_o129": D.scaled(B=1, C=32, O=129, H=17, W=16, kh=5, kw=5, ph=2, pw=2),
     # fp32 tiles of 65..128 output channels (k split over waves)
     "w_c32_o100": E.scaled(B=2, C=32, O=100, H=10, W=11, kh=3, kw=3, ph=1, pw=1),
     "w_c96_o128": E.scaled(B=1, C=96, O=128, H=9, W=15, kh=3, kw=5, ph=1, pw=2),
