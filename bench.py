@@ -56,6 +56,61 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def summarize_traffic(pmc_dir: str, workload: str, copy_mib: int) -> dict:
+    """Per-launch HBM bytes of the fused kernel from four rocprofv3 --pmc runs
+    under pmc_dir: <workload>_FETCH_SIZE, <workload>_WRITE_SIZE (this script on
+    the workload) and copy_FETCH_SIZE, copy_WRITE_SIZE (this script with
+    --copy-calibration-mib copy_mib).  Each counter is scaled by the bytes a
+    plain device copy of known size moves per unit of the same counter."""
+    import csv
+
+    def mean(run, pick):
+        vals = []
+        with open(os.path.join(pmc_dir, run, "p_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                if pick(r["Kernel_Name"]):
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit("no matching dispatch in %s" % run)
+        return sum(vals) / len(vals), len(vals)
+
+    fused = lambda k: "fused" in k
+    copy = lambda k: "copyBuffer" in k
+    fk, n = mean("%s_FETCH_SIZE" % workload, fused)
+    wk, _ = mean("%s_WRITE_SIZE" % workload, fused)
+    cf, _ = mean("copy_FETCH_SIZE", copy)
+    cw, _ = mean("copy_WRITE_SIZE", copy)
+    copy_bytes = copy_mib * (1 << 20)
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    cmd = ("rocprofv3 --pmc %s --output-format csv -d " + pmc_dir + "/%s -o p -- python bench.py ")
+    return {
+        "workload": workload,
+        "commands": [cmd % (c, "%s_%s" % (workload, c)) +
+                     "--steps 5 --warmup 2 --no-cpu-baseline --workload " + workload
+                     for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                    [cmd % (c, "copy_" + c) + "--copy-calibration-mib %d --steps 3" % copy_mib
+                     for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        "dispatches": n,
+        "fused_fetch_kib_per_dispatch": round(fk, 1),
+        "fused_write_kib_per_dispatch": round(wk, 1),
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": round(cf, 1),
+        "copy_write_kib": round(cw, 1),
+        "fetch_scale": round(fs, 4),
+        "write_scale": round(ws, 4),
+        "traffic_read_bytes_per_launch": round(fk * 1024 * fs),
+        "traffic_write_bytes_per_launch": round(wk * 1024 * ws),
+        "traffic_bytes_per_launch": round(fk * 1024 * fs + wk * 1024 * ws),
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+
+
+def percentiles(xs):
+    ys = sorted(xs)
+    pick = lambda f: ys[min(len(ys) - 1, int(round(f * (len(ys) - 1))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
 def cpu_baseline(spec, d, seconds: float):
     """The oracle (as it stands) on evenly spaced output pixels of the workload."""
     import numpy as np
@@ -105,7 +160,21 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scratch buffer before every timed step "
+                         "(inputs no longer cache-resident); not the default")
+    ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
+                    help="write profiles/fused_kernel_<workload>_traffic.json from "
+                         "rocprofv3 --pmc runs under PMC_DIR and exit")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        rec = summarize_traffic(args.summarize_traffic, args.workload, 256)
+        path = os.path.join(ROOT, "profiles", "fused_kernel_%s_traffic.json" % args.workload)
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -151,16 +220,24 @@ def main() -> int:
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    scratch = torch.empty(512 << 18, device="cuda") if args.cold else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(float(i))
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    pack_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    fused_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    ms_per_step = elapsed * 1e3 / args.steps
+    pack_list = [e[0].elapsed_time(e[1]) for e in events]
+    fused_list = [e[1].elapsed_time(e[2]) for e in events]
+    pack_ms = sum(pack_list) / args.steps
+    fused_ms = sum(fused_list) / args.steps
+    # with --cold the scratch writes sit inside the wall-clock window: the
+    # step time then comes from the events alone
+    ms_per_step = (sum(e[0].elapsed_time(e[2]) for e in events) / args.steps if args.cold
+                   else elapsed * 1e3 / args.steps)
     P = spec.pixels
     flops = spec.gemm_flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -189,6 +266,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
                      "traffic": measured_traffic(spec.name)},
         "kernels_us": {"fused": fused_ms * 1e3, "pack": pack_ms * 1e3},
+        "fused_us_percentiles": {k: v * 1e3 for k, v in percentiles(fused_list).items()},
+        "inputs": "cold (512 MiB written before each step)" if args.cold else "warm (resident)",
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(spec, d, args.cpu_seconds)
