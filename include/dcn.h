@@ -131,6 +131,33 @@ dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const v
                        const void* weight, const void* bias, void* out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* A band of output rows (page 1, deform_conv2d_gather's row0 argument: the
+ * offsets and mask of a call may cover a horizontal strip of the output
+ * only, while x is always the whole input map).  Computes output rows
+ * [row0, row0 + rows) of the plan's operator from an already packed weight:
+ *   offset [B, 2K, rows, Wo], mask [B, K, rows, Wo] or NULL  -- the band's
+ *          rows only (row r of the band is output row row0 + r)
+ *   out    [B, O, rows, Wo] (NCHW) or [B, rows, Wo, O] (NHWC), fp32
+ *   x, packed_weight, bias exactly as for dcn_forward_packed.
+ * Sampling points use the absolute output row, so the bands of a partition
+ * of [0, Ho) reproduce dcn_forward_packed's output row for row.
+ * DCN_E_SHAPE unless 0 <= row0, 0 <= rows and row0 + rows <= Ho; rows == 0
+ * is a no-op.  One fused kernel launch on `stream`. */
+dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const void* x,
+                            const void* offset, const void* mask, const void* packed_weight,
+                            size_t workspace_bytes, const void* bias, void* out,
+                            void* stream);
+
+/* Layout conversion for callers holding NCHW input (page 5's torchvision
+ * drop-in takes torchvision's argument order and NCHW layout): writes
+ * dst[b, y, x, c] = src[b, c, y, x] for a [batch, channels, height, width]
+ * tensor of `dtype` (DCN_F32 or DCN_BF16).  src and dst are device buffers of
+ * batch*channels*height*width elements, 16-byte aligned, not overlapping.
+ * One LDS-tiled transpose kernel on `stream`; a zero-sized tensor is a
+ * no-op; DCN_E_SHAPE for negative sizes or more than 2^31 - 1 elements. */
+dcn_status dcn_nchw_to_nhwc(const void* src, void* dst, int32_t batch, int32_t channels,
+                            int32_t height, int32_t width, int32_t dtype, void* stream);
+
 /* Test hook, not on the timed path: the sampling-corner stage alone, from
  * the same device function the fused kernel uses.  For every (b, k, ho, wo)
  * it writes y0x0[2e], y0x0[2e+1] = floor of the fp32 sampling row / column

@@ -19,7 +19,7 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import DcnError  # noqa: F401
 
-__all__ = ["Plan", "deform_conv2d_nhwc", "DcnError"]
+__all__ = ["Plan", "deform_conv2d", "deform_conv2d_nhwc", "nchw_to_nhwc", "DcnError"]
 
 _DTYPES = {"f32": _lib.DCN_F32, "bf16": _lib.DCN_BF16}
 _LAYOUTS = {"nchw": _lib.DCN_OUT_NCHW, "nhwc": _lib.DCN_OUT_NHWC}
@@ -168,6 +168,26 @@ class Plan:
             _ptr(ws), ws.numel(), ctypes.c_void_p(_stream_handle(stream))), "dcn_forward")
         return out
 
+    def forward_rows(self, row0, x, offset, mask, packed, bias=None, out=None, stream=None):
+        """``dcn_forward_rows``: output rows [row0, row0 + rows) where rows is
+        offset.shape[2]; offset/mask/out cover those rows only, x is whole."""
+        d = self.desc
+        rows = offset.shape[2] if offset is not None and offset.dim() == 4 else -1
+        self._check("x", x, (d.batch, d.height, d.width, d.in_ch))
+        self._check("offset", offset, (d.batch, 2 * self.K, rows, self.Wo))
+        self._check("mask", mask, (d.batch, self.K, rows, self.Wo), optional=True)
+        self._check("bias", bias, (d.out_ch,), optional=True)
+        shape = ((d.batch, d.out_ch, rows, self.Wo) if d.out_layout == "nchw"
+                 else (d.batch, rows, self.Wo, d.out_ch))
+        if out is None:
+            out = _torch().empty(shape, dtype=_torch().float32, device="cuda")
+        self._check("out", out, shape, dtype=_torch().float32)
+        _lib.check(_lib.load().dcn_forward_rows(
+            self._h, int(row0), int(rows), _ptr(x), _ptr(offset), _ptr(mask), _ptr(packed),
+            packed.numel(), _ptr(bias), _ptr(out), ctypes.c_void_p(_stream_handle(stream))),
+            "dcn_forward_rows")
+        return out
+
     def debug_coords(self, offset, stream=None):
         """``dcn_debug_coords``: (y0x0 [B,K,Ho,Wo,2] int32, valid4 [B,K,Ho,Wo] uint8)."""
         torch = _torch()
@@ -211,3 +231,32 @@ def deform_conv2d_nhwc(x, offset, weight, bias=None, padding=0, mask=None, out_l
         raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
     plan = plan_for(Desc(B, C, H, W, O, kh, kw, ph, pw, dtype, out_layout))
     return plan.forward(x, offset, mask, weight, bias)
+
+
+def nchw_to_nhwc(x, out=None, stream=None):
+    """``dcn_nchw_to_nhwc``: [B,C,H,W] -> [B,H,W,C] on the GPU (float32 or bfloat16)."""
+    torch = _torch()
+    dtype = {torch.float32: _lib.DCN_F32, torch.bfloat16: _lib.DCN_BF16}.get(x.dtype)
+    if dtype is None:
+        raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 4-d device tensor")
+    B, C, H, W = x.shape
+    if out is None:
+        out = torch.empty((B, H, W, C), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (B, H, W, C) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,H,W,C] tensor of x's dtype")
+    _lib.check(_lib.load().dcn_nchw_to_nhwc(_ptr(x), _ptr(out), B, C, H, W, dtype,
+                                            ctypes.c_void_p(_stream_handle(stream))),
+               "dcn_nchw_to_nhwc")
+    return out
+
+
+def deform_conv2d(input, offset, weight, bias=None, padding=0, mask=None, out_layout="nchw"):
+    """torchvision-order drop-in (page 5's torchvision integration): NCHW
+    ``input`` [B,C,H,W], offset [B,2*kh*kw,Ho,Wo], weight [O,C,kh,kw], bias
+    [O] or None, mask [B,kh*kw,Ho,Wo] or None; stride 1, dilation 1.  The input
+    is moved to NHWC by the library's transpose kernel, then the fused forward
+    runs.  Returns fp32 [B,O,Ho,Wo] (or [B,Ho,Wo,O] with ``out_layout="nhwc"``)."""
+    return deform_conv2d_nhwc(nchw_to_nhwc(input), offset, weight, bias, padding, mask,
+                              out_layout)

@@ -101,7 +101,7 @@ dcn_status hip_fail(hipError_t e, const char* what) {
 
 extern "C" {
 
-int32_t dcn_version(void) { return 10000; }
+int32_t dcn_version(void) { return 10100; }
 
 const char* dcn_status_string(dcn_status s) {
   switch (s) {
@@ -229,14 +229,24 @@ dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
   }
 }
 
-dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, const void* mask,
-                              const void* packed_weight, size_t workspace_bytes,
-                              const void* bias, void* out, void* stream) {
+namespace {
+
+// Output rows [row0, row0 + rows) from a packed weight.  The band is the
+// plan's operator with the sampling grid shifted down by row0: the kernels
+// form grid row = ho - pad_h + i, so a band launches with pad_h - row0 and
+// rows output rows (the offsets, mask and output cover the band only).
+dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
+                        const void* x, const void* offset, const void* mask,
+                        const void* packed_weight, size_t workspace_bytes, const void* bias,
+                        void* out, void* stream) {
   try {
-    if (!plan) return fail(DCN_E_NULL, "dcn_forward_packed: plan is NULL");
+    if (!plan) return fail(DCN_E_NULL, "%s: plan is NULL", who);
     const dcn_desc& d = plan->d;
-    if (d.batch == 0) return ok();  // empty batch: nothing to read or write
-    if (!x || !offset || !out) return fail(DCN_E_NULL, "x, offset and out are required");
+    if (row0 < 0 || rows < 0 || (int64_t)row0 + rows > plan->Ho)
+      return fail(DCN_E_SHAPE, "%s: rows [%d, %d + %d) outside the output's %d rows", who, row0,
+                  row0, rows, plan->Ho);
+    if (d.batch == 0 || rows == 0) return ok();  // nothing to read or write
+    if (!x || !offset || !out) return fail(DCN_E_NULL, "%s: x, offset and out are required", who);
     if (!packed_weight || workspace_bytes < plan->ws_bytes)
       return fail(DCN_E_WORKSPACE, "packed weight needs %zu bytes, got %zu at %p",
                   plan->ws_bytes, workspace_bytes, packed_weight);
@@ -260,23 +270,64 @@ dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, 
     a.kh = d.kernel_h;
     a.kw = d.kernel_w;
     a.K = plan->K;
-    a.ph = d.pad_h;
+    a.ph = d.pad_h - row0;
     a.pw = d.pad_w;
-    a.Ho = plan->Ho;
+    a.Ho = rows;
     a.Wo = plan->Wo;
-    a.HoWo = plan->Ho * plan->Wo;
-    a.nchunk = plan->kc.nchunk;
-    a.n_otiles = plan->kc.n_otiles;
-    a.tiles_per_img = plan->kc.tiles_per_img;
+    a.HoWo = rows * plan->Wo;
+    dcn::KernelConfig kc = plan->kc;
+    kc.tiles_per_img = (int)ceil_div(a.HoWo, kc.M);
+    a.nchunk = kc.nchunk;
+    a.n_otiles = kc.n_otiles;
+    a.tiles_per_img = kc.tiles_per_img;
     a.x_bytes = plan->x_bytes;
     a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
     a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
     a.vec_store = (a.HoWo % 4) == 0;
-    hipError_t e = dcn::launch_fused(plan->kc, a, static_cast<hipStream_t>(stream));
+    hipError_t e = dcn::launch_fused(kc, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused forward launch");
     return ok();
   } catch (...) {
-    return fail(DCN_E_INTERNAL, "dcn_forward_packed: unexpected exception");
+    return fail(DCN_E_INTERNAL, "%s: unexpected exception", who);
+  }
+}
+
+}  // namespace
+
+dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                              const void* packed_weight, size_t workspace_bytes,
+                              const void* bias, void* out, void* stream) {
+  return forward_band("dcn_forward_packed", plan, 0, plan ? plan->Ho : 0, x, offset, mask,
+                      packed_weight, workspace_bytes, bias, out, stream);
+}
+
+dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const void* x,
+                            const void* offset, const void* mask, const void* packed_weight,
+                            size_t workspace_bytes, const void* bias, void* out,
+                            void* stream) {
+  return forward_band("dcn_forward_rows", plan, row0, rows, x, offset, mask, packed_weight,
+                      workspace_bytes, bias, out, stream);
+}
+
+dcn_status dcn_nchw_to_nhwc(const void* src, void* dst, int32_t batch, int32_t channels,
+                            int32_t height, int32_t width, int32_t dtype, void* stream) {
+  try {
+    if (dtype != DCN_F32 && dtype != DCN_BF16)
+      return fail(DCN_E_DTYPE, "dcn_nchw_to_nhwc: dtype %d", dtype);
+    if (batch < 0 || channels < 0 || height < 0 || width < 0)
+      return fail(DCN_E_SHAPE, "dcn_nchw_to_nhwc: negative size");
+    const int64_t n = (int64_t)batch * channels * height * width;
+    if (n >= kLimit31) return fail(DCN_E_SHAPE, "dcn_nchw_to_nhwc: %lld elements", (long long)n);
+    if (n == 0) return ok();
+    if (!src || !dst) return fail(DCN_E_NULL, "dcn_nchw_to_nhwc: src and dst are required");
+    if (!aligned(src, 16) || !aligned(dst, 16))
+      return fail(DCN_E_ALIGN, "dcn_nchw_to_nhwc: src and dst must be 16-byte aligned");
+    hipError_t e = dcn::launch_nchw_to_nhwc(dtype == DCN_BF16, src, dst, batch, channels,
+                                            height * width, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_nchw_to_nhwc: unexpected exception");
   }
 }
 

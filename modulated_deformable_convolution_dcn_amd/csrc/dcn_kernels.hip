@@ -371,6 +371,78 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* _
   }
 }
 
+// ---------------------------------------------------------------- layout
+// NCHW -> NHWC for callers that hold torchvision-layout input (page 5's
+// drop-in takes NCHW).  One workgroup moves a 64-channel x 64-pixel tile
+// through LDS.  Interior tiles (whole tile inside, pixel and channel counts
+// multiples of the 16-byte vector) use 16-byte accesses on both sides:
+// each thread reads VEC consecutive pixels of one channel and writes VEC
+// consecutive channels of one pixel; edge tiles take the element-wise path.
+// Element-exact: a pure copy.
+template <class T>
+__global__ __launch_bounds__(256) void nchw_to_nhwc_kernel(const T* __restrict__ src,
+                                                           T* __restrict__ dst, int C, int HW,
+                                                           int c_tiles, int p_tiles) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PITCH = 64 + VEC;  // row pitch (elements): rows start 16 B apart in the banks
+  __shared__ __attribute__((aligned(16))) T tile[64 * PITCH];
+  const int t = blockIdx.x;
+  const int pt = t % p_tiles;
+  const int ct = (t / p_tiles) % c_tiles;
+  const int b = t / (p_tiles * c_tiles);
+  const int c0 = ct * 64, p0 = pt * 64;
+  const T* s = src + (size_t)b * C * HW;
+  T* d = dst + (size_t)b * HW * C;
+  const int tid = threadIdx.x;
+  const bool vec = c0 + 64 <= C && p0 + 64 <= HW && C % VEC == 0 && HW % VEC == 0;
+  if (vec) {
+    constexpr int LPR = 64 / VEC;      // lanes per 64-element row
+    constexpr int RPP = 256 / LPR;     // rows per pass
+    const int li = tid % LPR, r0 = tid / LPR;
+#pragma unroll
+    for (int r = r0; r < 64; r += RPP)
+      *reinterpret_cast<u32x4*>(&tile[r * PITCH + li * VEC]) =
+          *reinterpret_cast<const u32x4*>(s + (size_t)(c0 + r) * HW + p0 + li * VEC);
+    __syncthreads();
+#pragma unroll
+    for (int r = r0; r < 64; r += RPP) {  // r: pixel, li: channel group
+      T v[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = tile[(li * VEC + e) * PITCH + r];
+      *reinterpret_cast<u32x4*>(d + (size_t)(p0 + r) * C + c0 + li * VEC) =
+          *reinterpret_cast<const u32x4*>(v);
+    }
+    return;
+  }
+  const int lane = tid & 63, row = tid >> 6;
+  for (int r = row; r < 64; r += 4) {
+    const int c = c0 + r, p = p0 + lane;
+    if (c < C && p < HW) tile[r * PITCH + lane] = s[(size_t)c * HW + p];
+  }
+  __syncthreads();
+  for (int r = row; r < 64; r += 4) {
+    const int p = p0 + r, c = c0 + lane;
+    if (c < C && p < HW) d[(size_t)p * C + c] = tile[lane * PITCH + r];
+  }
+}
+
+hipError_t launch_nchw_to_nhwc(int bf16, const void* src, void* dst, int B, int C, int HW,
+                               hipStream_t s) {
+  const int c_tiles = (C + 63) / 64, p_tiles = (HW + 63) / 64;
+  const int64_t nblk = (int64_t)B * c_tiles * p_tiles;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (bf16)
+    hipLaunchKernelGGL(nchw_to_nhwc_kernel<__bf16>, dim3((unsigned)nblk), dim3(256), 0, s,
+                       static_cast<const __bf16*>(src), static_cast<__bf16*>(dst), C, HW, c_tiles,
+                       p_tiles);
+  else
+    hipLaunchKernelGGL(nchw_to_nhwc_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, s,
+                       static_cast<const float*>(src), static_cast<float*>(dst), C, HW, c_tiles,
+                       p_tiles);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- corners
 template <class T>
 __global__ __launch_bounds__(256) void coords_kernel(const T* __restrict__ offset,

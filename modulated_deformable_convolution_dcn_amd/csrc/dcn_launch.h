@@ -61,6 +61,10 @@ hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStre
 bool bf16w_supported(const KernelConfig& kc);
 hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
 
+// dst[b, p, c] = src[b, c, p] for p over height*width pixels.
+hipError_t launch_nchw_to_nhwc(int bf16, const void* src, void* dst, int B, int C, int HW,
+                               hipStream_t stream);
+
 hipError_t launch_coords(int bf16, const void* offset, int32_t* y0x0, uint8_t* valid4, int B,
                          int K, int kw, int Ho, int Wo, int ph, int pw, int H, int W,
                          hipStream_t stream);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.dcn_version() == 10000
+    assert lib.dcn_version() == 10100
 
 
 def test_status_strings():
@@ -145,3 +145,36 @@ def test_python_binding_rejects_bad_tensors():
                   torch.zeros(4, 4, 3, 3))  # CPU tensors are refused
     with pytest.raises(DcnError):
         Plan(Desc(1, 3, 8, 8, 4, 3, 3, 1, 1))
+
+
+def test_row_band_checks_fire_before_any_launch():
+    """dcn_forward_rows: row range, NULL and workspace errors without touching the GPU."""
+    lib = _lib.load()
+    p = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1))  # Ho = 16
+    h = p._h
+    fake = ctypes.c_void_p(0x10000)
+    ws = p.workspace_bytes
+    call = lambda r0, n, x=fake, pk=fake, w=ws: lib.dcn_forward_rows(  # noqa: E731
+        h, r0, n, x, fake, None, pk, w, None, fake, None)
+    assert call(-1, 4) == 2
+    assert call(0, -1) == 2
+    assert call(13, 4) == 2          # 13 + 4 > 16
+    assert call(16, 1) == 2
+    assert "outside the output" in lib.dcn_last_error().decode()
+    assert call(16, 0) == 0          # empty band at the end: no-op
+    assert call(3, 0, x=None) == 0   # empty band: nothing is read
+    assert call(3, 4, x=None) == 1
+    assert call(3, 4, pk=None) == 8
+    assert call(3, 4, w=ws - 1) == 8
+    assert lib.dcn_forward_rows(None, 0, 1, fake, fake, None, fake, ws, None, fake, None) == 1
+
+
+def test_transpose_checks_fire_before_any_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.dcn_nchw_to_nhwc(fake, fake, 1, 4, 4, 4, 7, None) == 3      # dtype
+    assert lib.dcn_nchw_to_nhwc(fake, fake, 1, -4, 4, 4, 0, None) == 2     # negative size
+    assert lib.dcn_nchw_to_nhwc(fake, fake, 1 << 16, 1 << 16, 1, 1, 0, None) == 2  # > 2^31 - 1
+    assert lib.dcn_nchw_to_nhwc(None, None, 0, 4, 4, 4, 0, None) == 0      # empty: no-op
+    assert lib.dcn_nchw_to_nhwc(None, fake, 1, 4, 4, 4, 0, None) == 1
+    assert lib.dcn_nchw_to_nhwc(ctypes.c_void_p(0x10004), fake, 1, 4, 4, 4, 1, None) == 5

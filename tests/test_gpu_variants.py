@@ -1,0 +1,112 @@
+"""GPU tests of the call variants on the same kernels: row bands (page 1's
+row0: offsets and mask of an output-row strip, whole input map) and the
+NCHW-input torchvision-order entry (page 5's torchvision drop-in), which
+moves the input to NHWC with the library's transpose kernel.
+
+Bands are checked two ways: against the oracle's full-map output rows (the
+bar of every parity test) and bit for bit against the full-map GPU output
+(a band runs the same per-element arithmetic; only the tiling moves).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dcn_testlib import compare, device_inputs, oracle_shape, pixel_major
+from modulated_deformable_convolution_dcn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+E = W["edge_stress_fp32"]
+D = W["detection_bf16"]
+
+# one case per kernel variant (see the dispatch table of the C ABI)
+BAND_CASES = {
+    "quad_c64_o64": W["birefnet512_fp32"].scaled(H=37, W=29),
+    "wsk_c128_o128": E.scaled(B=1, H=23, W=19),
+    "bf16_c256_o256": D.scaled(B=2, H=21, W=17),
+    "general_c4_o4": W["tiny_fp32"].scaled(H=19, W=11),
+}
+
+
+def _bands(ho):
+    # ragged partition, a single-row band, the whole map
+    cuts = sorted({0, 1, 7, ho // 2, ho - 1, ho})
+    return [(a, b - a) for a, b in zip(cuts[:-1], cuts[1:])] + [(0, ho)]
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+@pytest.mark.parametrize("name", sorted(BAND_CASES))
+def test_row_bands(name, layout):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan
+    spec = BAND_CASES[name]
+    d = synth.make_inputs(spec)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                               d["bias"])
+    ref = ref.reshape(spec.B, spec.Ho, spec.Wo, spec.O)
+    norm = norm.reshape(spec.B, spec.Ho, spec.Wo, spec.O)
+    dev = device_inputs(spec, d)
+    plan = Plan(Desc(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw,
+                     spec.dtype, layout))
+    packed = plan.pack_weight(dev["weight"])
+    full = plan.forward_packed(dev["x"], dev["offset"], dev["mask"], packed, dev["bias"])
+    torch.cuda.synchronize()
+    full = full.cpu().numpy()
+    print("case", name, layout, spec, flush=True)
+    for row0, rows in _bands(spec.Ho):
+        off = dev["offset"][:, :, row0:row0 + rows].contiguous()
+        msk = dev["mask"][:, :, row0:row0 + rows].contiguous()
+        got = plan.forward_rows(row0, dev["x"], off, msk, packed, dev["bias"])
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        want_gpu = full[:, :, row0:row0 + rows] if layout == "nchw" else full[:, row0:row0 + rows]
+        assert np.array_equal(got, want_gpu), "band [%d, +%d) differs from the full map" % (row0,
+                                                                                             rows)
+        compare(pixel_major(got, layout), ref[:, row0:row0 + rows].reshape(-1, spec.O),
+                norm[:, row0:row0 + rows].reshape(-1, spec.O), d["bias"], spec.dtype,
+                "%s band [%d, +%d)" % (name, row0, rows))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 64, 16, 16), (2, 72, 37, 13), (1, 4, 3, 5), (3, 130, 9, 70),
+                                   (2, 136, 24, 24), (1, 256, 64, 64)])
+def test_nchw_to_nhwc_is_an_exact_copy(shape, dtype):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import nchw_to_nhwc
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal(shape).astype(np.float32)
+    if dtype == "f32":
+        t = torch.from_numpy(a).cuda()
+    else:
+        t = torch.from_numpy(synth.round_bf16(a)[1].astype(np.int16)).cuda().view(torch.bfloat16)
+    print("transpose", shape, dtype, flush=True)
+    got = nchw_to_nhwc(t)
+    torch.cuda.synchronize()
+    want = t.cpu().permute(0, 2, 3, 1).contiguous()
+    assert torch.equal(got.cpu().view(torch.int16 if dtype == "bf16" else torch.int32),
+                       want.view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+@pytest.mark.parametrize("name", ["birefnet512_small", "edge_small", "bf16_small", "tiny"])
+def test_torchvision_order_nchw_input(name):
+    """deform_conv2d(input NCHW, offset, weight, bias, padding, mask) == the oracle."""
+    import torch
+    from modulated_deformable_convolution_dcn_amd import deform_conv2d
+    spec = {"birefnet512_small": W["birefnet512_fp32"].scaled(H=24, W=31),
+            "edge_small": E.scaled(B=1, H=17, W=22),
+            "bf16_small": D.scaled(B=1, H=12, W=14),
+            "tiny": W["tiny_fp32"]}[name]
+    d = synth.make_inputs(spec)
+    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                               d["bias"])
+    dev = device_inputs(spec, d)
+    x_nchw = dev["x"].permute(0, 3, 1, 2).contiguous()
+    print("case", name, spec, flush=True)
+    out = deform_conv2d(x_nchw, dev["offset"], dev["weight"], dev["bias"],
+                        padding=(spec.ph, spec.pw), mask=dev["mask"])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (spec.B, spec.O, spec.Ho, spec.Wo)
+    compare(pixel_major(out.cpu().numpy(), "nchw"), ref, norm, d["bias"], spec.dtype, name)
