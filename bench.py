@@ -161,6 +161,11 @@ def main() -> int:
     ap.add_argument("--input-layout", default="nhwc", choices=["nhwc", "nchw"],
                     help="nchw: x is held NCHW and every step first runs the library's "
                          "NCHW->NHWC transpose (the torchvision-order entry)")
+    ap.add_argument("--branches", type=int, default=1,
+                    help="run this many branches of the workload (own offsets/mask/weight/"
+                         "bias, shared input) per step with one multi-branch call")
+    ap.add_argument("--sequential", action="store_true",
+                    help="with --branches: one forward call per branch instead")
     ap.add_argument("--bands", type=int, default=1,
                     help="run the forward as this many output-row bands (row0 calls), "
                          "back to back on one stream")
@@ -226,6 +231,20 @@ def main() -> int:
               band_out(r1 - r0))
              for r0, r1 in zip(cuts[:-1], cuts[1:])]
 
+    from modulated_deformable_convolution_dcn_amd import forward_multi
+    nbr = max(1, args.branches)
+    extra = []  # branches 1.. : own offsets/mask/weight/bias (seeds spec.seed + i), shared x
+    for i in range(1, nbr):
+        di = synth.make_inputs(spec.scaled(seed=spec.seed + 1000 * i))
+        e = {}
+        for k in ("offset", "mask", "weight", "bias"):
+            v = di[k]
+            e[k] = (None if v is None else torch.from_numpy(v).cuda() if spec.dtype == "f32"
+                    else torch.from_numpy(di["bits"][k].astype("int16")).cuda().view(torch.bfloat16))
+        e["ws"] = plan.new_workspace()
+        e["out"] = plan.new_output()
+        extra.append(e)
+
     def step(ev=None):
         # events: [0] start, [1] after transpose + pack, [2] after the fused forward
         if ev is not None:
@@ -233,9 +252,20 @@ def main() -> int:
         if x_nchw is not None:
             nchw_to_nhwc(x_nchw, x_nhwc)
         plan.pack_weight(dev["weight"], ws)
+        for e in extra:
+            plan.pack_weight(e["weight"], e["ws"])
         if ev is not None:
             ev[1].record()
-        if nb == 1:
+        if extra and not args.sequential:
+            forward_multi([plan] * nbr, x_nhwc, [dev["offset"]] + [e["offset"] for e in extra],
+                          [dev["mask"]] + [e["mask"] for e in extra],
+                          [ws] + [e["ws"] for e in extra], [dev["bias"]] + [e["bias"] for e in extra],
+                          [out] + [e["out"] for e in extra])
+        elif extra:
+            plan.forward_packed(x_nhwc, dev["offset"], dev["mask"], ws, dev["bias"], out)
+            for e in extra:
+                plan.forward_packed(x_nhwc, e["offset"], e["mask"], e["ws"], e["bias"], e["out"])
+        elif nb == 1:
             plan.forward_packed(x_nhwc, dev["offset"], dev["mask"], ws, dev["bias"], out)
         else:
             for r0, off, msk, bo in bands:
@@ -266,8 +296,8 @@ def main() -> int:
     # step time then comes from the events alone
     ms_per_step = (sum(e[0].elapsed_time(e[2]) for e in events) / args.steps if args.cold
                    else elapsed * 1e3 / args.steps)
-    P = spec.pixels
-    flops = spec.gemm_flops
+    P = spec.pixels * nbr
+    flops = spec.gemm_flops * nbr
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[spec.dtype]
     fused_tflops = flops / (fused_ms * 1e-3) / 1e12
@@ -287,7 +317,9 @@ def main() -> int:
         "config": {"workload": spec.name, "B": spec.B, "C": spec.C, "O": spec.O, "H": spec.H,
                    "W": spec.W, "kernel": "%dx%d" % (spec.kh, spec.kw),
                    "pad": [spec.ph, spec.pw], "out_layout": args.layout,
-                   "input_layout": args.input_layout, "row_bands": nb},
+                   "input_layout": args.input_layout, "row_bands": nb,
+                   "branches": nbr, "branch_launch": ("one per branch" if args.sequential
+                                                      else "one for all") if nbr > 1 else None},
         "tflops": tflops,
         "pct_roofline": 100.0 * tflops / peak,
         "roofline": {"bound": "mfma", "achieved": fused_tflops, "peak": peak,

@@ -148,6 +148,23 @@ dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const voi
                             size_t workspace_bytes, const void* bias, void* out,
                             void* stream);
 
+/* Several deformable convolutions on ONE input map in one call (page 2: the
+ * BiRefNet decoder's deformable ASPP blocks run four branches on the same
+ * map).  Branch i is plans[i]'s operator with its own offsets[i], masks[i]
+ * (or NULL), packed_weights[i] (from dcn_pack_weight with plans[i],
+ * workspace_bytes[i] bytes), biases[i] (or NULL) and outs[i]; x is shared.
+ * `masks` and `biases` may themselves be NULL (no branch has one).  All
+ * plans must read the same input (batch, in_ch, height, width, in_dtype:
+ * else DCN_E_SHAPE); kernel size, padding, out_ch and out_layout may
+ * differ.  Branches that run the same kernel variant share ONE launch (the
+ * workgroups of all of them in one grid); 1 <= n <= 8 (n == 0 is a no-op,
+ * more is DCN_E_UNSUPPORTED).  Per-branch pointer rules and errors as for
+ * dcn_forward_packed; nothing is launched unless every branch validates. */
+dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
+                             const void* const* offsets, const void* const* masks,
+                             const void* const* packed_weights, const size_t* workspace_bytes,
+                             const void* const* biases, void* const* outs, void* stream);
+
 /* Layout conversion for callers holding NCHW input (page 5's torchvision
  * drop-in takes torchvision's argument order and NCHW layout): writes
  * dst[b, y, x, c] = src[b, c, y, x] for a [batch, channels, height, width]

@@ -19,7 +19,8 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import DcnError  # noqa: F401
 
-__all__ = ["Plan", "deform_conv2d", "deform_conv2d_nhwc", "nchw_to_nhwc", "DcnError"]
+__all__ = ["Plan", "deform_conv2d", "deform_conv2d_nhwc", "forward_multi", "nchw_to_nhwc",
+           "DcnError"]
 
 _DTYPES = {"f32": _lib.DCN_F32, "bf16": _lib.DCN_BF16}
 _LAYOUTS = {"nchw": _lib.DCN_OUT_NCHW, "nhwc": _lib.DCN_OUT_NHWC}
@@ -260,3 +261,27 @@ def deform_conv2d(input, offset, weight, bias=None, padding=0, mask=None, out_la
     runs.  Returns fp32 [B,O,Ho,Wo] (or [B,Ho,Wo,O] with ``out_layout="nhwc"``)."""
     return deform_conv2d_nhwc(nchw_to_nhwc(input), offset, weight, bias, padding, mask,
                               out_layout)
+
+
+def forward_multi(plans, x, offsets, masks, packeds, biases=None, outs=None, stream=None):
+    """``dcn_forward_multi``: branch i = plans[i] on the shared NHWC ``x`` with
+    offsets[i], masks[i] (or None), packed weight packeds[i] (from
+    plans[i].pack_weight), biases[i] (or None); returns the list of outputs.
+    Branches that run the same kernel variant share one launch."""
+    n = len(plans)
+    masks = masks if masks is not None else [None] * n
+    biases = biases if biases is not None else [None] * n
+    outs = outs if outs is not None else [p.new_output() for p in plans]
+    if not (len(offsets) == len(masks) == len(packeds) == len(biases) == len(outs) == n):
+        raise ValueError("one offset, mask, packed weight, bias and output per plan")
+    for p, off, m, b, o in zip(plans, offsets, masks, biases, outs):
+        p._check_inputs(x, off, m, b)
+        p._check("out", o, p.out_shape(), dtype=_torch().float32)
+    arr = lambda items: (ctypes.c_void_p * n)(*[None if t is None else t.data_ptr()  # noqa: E731
+                                                for t in items])
+    handles = (ctypes.c_void_p * n)(*[p._h.value for p in plans])
+    sizes = (ctypes.c_size_t * n)(*[w.numel() for w in packeds])
+    _lib.check(_lib.load().dcn_forward_multi(
+        n, handles, _ptr(x), arr(offsets), arr(masks), arr(packeds), sizes, arr(biases),
+        arr(outs), ctypes.c_void_p(_stream_handle(stream))), "dcn_forward_multi")
+    return outs

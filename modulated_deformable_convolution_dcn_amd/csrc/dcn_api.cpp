@@ -231,65 +231,89 @@ dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
 
 namespace {
 
-// Output rows [row0, row0 + rows) from a packed weight.  The band is the
-// plan's operator with the sampling grid shifted down by row0: the kernels
-// form grid row = ho - pad_h + i, so a band launches with pad_h - row0 and
-// rows output rows (the offsets, mask and output cover the band only).
+// Validated kernel arguments for output rows [row0, row0 + rows) from a
+// packed weight.  The band is the plan's operator with the sampling grid
+// shifted down by row0: the kernels form grid row = ho - pad_h + i, so a band
+// launches with pad_h - row0 and rows output rows (the offsets, mask and
+// output cover the band only).  *empty is set when there is nothing to read
+// or write (empty batch or band).
+dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows, const void* x,
+                     const void* offset, const void* mask, const void* packed_weight,
+                     size_t workspace_bytes, const void* bias, void* out, dcn::FusedArgs& a,
+                     dcn::KernelConfig& kc, bool& empty) {
+  empty = false;
+  if (!plan) return fail(DCN_E_NULL, "%s: plan is NULL", who);
+  const dcn_desc& d = plan->d;
+  if (row0 < 0 || rows < 0 || (int64_t)row0 + rows > plan->Ho)
+    return fail(DCN_E_SHAPE, "%s: rows [%d, %d + %d) outside the output's %d rows", who, row0,
+                row0, rows, plan->Ho);
+  if (d.batch == 0 || rows == 0) {
+    empty = true;
+    return ok();
+  }
+  if (!x || !offset || !out) return fail(DCN_E_NULL, "%s: x, offset and out are required", who);
+  if (!packed_weight || workspace_bytes < plan->ws_bytes)
+    return fail(DCN_E_WORKSPACE, "%s: packed weight needs %zu bytes, got %zu at %p", who,
+                plan->ws_bytes, workspace_bytes, packed_weight);
+  const size_t E = plan->kc.bf16 ? 2 : 4;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(packed_weight, 16))
+    return fail(DCN_E_ALIGN, "%s: x, out and the packed weight must be 16-byte aligned", who);
+  if (!aligned(offset, E) || (mask && !aligned(mask, E)) || (bias && !aligned(bias, E)))
+    return fail(DCN_E_ALIGN, "%s: offset, mask and bias must be %zu-byte aligned", who, E);
+  a = dcn::FusedArgs{};
+  a.x = x;
+  a.offset = offset;
+  a.mask = mask;
+  a.wpack = packed_weight;
+  a.bias = bias;
+  a.out = static_cast<float*>(out);
+  a.B = d.batch;
+  a.C = d.in_ch;
+  a.H = d.height;
+  a.W = d.width;
+  a.O = d.out_ch;
+  a.kh = d.kernel_h;
+  a.kw = d.kernel_w;
+  a.K = plan->K;
+  a.ph = d.pad_h - row0;
+  a.pw = d.pad_w;
+  a.Ho = rows;
+  a.Wo = plan->Wo;
+  a.HoWo = rows * plan->Wo;
+  kc = plan->kc;
+  kc.tiles_per_img = (int)ceil_div(a.HoWo, kc.M);
+  a.nchunk = kc.nchunk;
+  a.n_otiles = kc.n_otiles;
+  a.tiles_per_img = kc.tiles_per_img;
+  a.x_bytes = plan->x_bytes;
+  a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
+  a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
+  a.vec_store = (a.HoWo % 4) == 0;
+  return ok();
+}
+
 dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
                         const void* x, const void* offset, const void* mask,
                         const void* packed_weight, size_t workspace_bytes, const void* bias,
                         void* out, void* stream) {
   try {
-    if (!plan) return fail(DCN_E_NULL, "%s: plan is NULL", who);
-    const dcn_desc& d = plan->d;
-    if (row0 < 0 || rows < 0 || (int64_t)row0 + rows > plan->Ho)
-      return fail(DCN_E_SHAPE, "%s: rows [%d, %d + %d) outside the output's %d rows", who, row0,
-                  row0, rows, plan->Ho);
-    if (d.batch == 0 || rows == 0) return ok();  // nothing to read or write
-    if (!x || !offset || !out) return fail(DCN_E_NULL, "%s: x, offset and out are required", who);
-    if (!packed_weight || workspace_bytes < plan->ws_bytes)
-      return fail(DCN_E_WORKSPACE, "packed weight needs %zu bytes, got %zu at %p",
-                  plan->ws_bytes, workspace_bytes, packed_weight);
-    const size_t E = plan->kc.bf16 ? 2 : 4;
-    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(packed_weight, 16))
-      return fail(DCN_E_ALIGN, "x, out and the packed weight must be 16-byte aligned");
-    if (!aligned(offset, E) || (mask && !aligned(mask, E)) || (bias && !aligned(bias, E)))
-      return fail(DCN_E_ALIGN, "offset, mask and bias must be %zu-byte aligned", E);
-    dcn::FusedArgs a{};
-    a.x = x;
-    a.offset = offset;
-    a.mask = mask;
-    a.wpack = packed_weight;
-    a.bias = bias;
-    a.out = static_cast<float*>(out);
-    a.B = d.batch;
-    a.C = d.in_ch;
-    a.H = d.height;
-    a.W = d.width;
-    a.O = d.out_ch;
-    a.kh = d.kernel_h;
-    a.kw = d.kernel_w;
-    a.K = plan->K;
-    a.ph = d.pad_h - row0;
-    a.pw = d.pad_w;
-    a.Ho = rows;
-    a.Wo = plan->Wo;
-    a.HoWo = rows * plan->Wo;
-    dcn::KernelConfig kc = plan->kc;
-    kc.tiles_per_img = (int)ceil_div(a.HoWo, kc.M);
-    a.nchunk = kc.nchunk;
-    a.n_otiles = kc.n_otiles;
-    a.tiles_per_img = kc.tiles_per_img;
-    a.x_bytes = plan->x_bytes;
-    a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
-    a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
-    a.vec_store = (a.HoWo % 4) == 0;
+    dcn::FusedArgs a;
+    dcn::KernelConfig kc;
+    bool empty;
+    dcn_status st = make_args(who, plan, row0, rows, x, offset, mask, packed_weight,
+                              workspace_bytes, bias, out, a, kc, empty);
+    if (st != DCN_OK || empty) return st;
     hipError_t e = dcn::launch_fused(kc, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fused forward launch");
     return ok();
   } catch (...) {
     return fail(DCN_E_INTERNAL, "%s: unexpected exception", who);
   }
+}
+
+bool same_kernel(const dcn::KernelConfig& p, const dcn::KernelConfig& q) {
+  return p.kind == q.kind && p.bf16 == q.bf16 && p.M == q.M && p.CB == q.CB && p.NO == q.NO &&
+         p.nhwc == q.nhwc;
 }
 
 }  // namespace
@@ -307,6 +331,74 @@ dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const voi
                             void* stream) {
   return forward_band("dcn_forward_rows", plan, row0, rows, x, offset, mask, packed_weight,
                       workspace_bytes, bias, out, stream);
+}
+
+dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
+                             const void* const* offsets, const void* const* masks,
+                             const void* const* packed_weights, const size_t* workspace_bytes,
+                             const void* const* biases, void* const* outs, void* stream) {
+  try {
+    if (n == 0) return ok();
+    if (n < 0) return fail(DCN_E_SHAPE, "dcn_forward_multi: %d branches", n);
+    if (n > dcn::kMaxBranches)
+      return fail(DCN_E_UNSUPPORTED, "dcn_forward_multi: %d branches (1..%d supported)", n,
+                  dcn::kMaxBranches);
+    if (!plans || !offsets || !packed_weights || !workspace_bytes || !outs)
+      return fail(DCN_E_NULL, "dcn_forward_multi: plans, offsets, packed_weights, "
+                              "workspace_bytes and outs are required arrays");
+    for (int i = 0; i < n; ++i) {
+      if (!plans[i]) return fail(DCN_E_NULL, "dcn_forward_multi: plan %d is NULL", i);
+      const dcn_desc& p = plans[i]->d;
+      const dcn_desc& q = plans[0]->d;
+      if (p.batch != q.batch || p.in_ch != q.in_ch || p.height != q.height ||
+          p.width != q.width || p.in_dtype != q.in_dtype)
+        return fail(DCN_E_SHAPE, "dcn_forward_multi: branch %d reads a different input than "
+                                 "branch 0 (batch, channels, size and dtype must match)", i);
+    }
+    dcn::FusedArgs args[dcn::kMaxBranches];
+    dcn::KernelConfig cfg[dcn::kMaxBranches];
+    bool live[dcn::kMaxBranches];
+    for (int i = 0; i < n; ++i) {
+      bool empty;
+      dcn_status st = make_args("dcn_forward_multi", plans[i], 0, plans[i]->Ho, x, offsets[i],
+                                masks ? masks[i] : nullptr, packed_weights[i],
+                                workspace_bytes[i], biases ? biases[i] : nullptr, outs[i],
+                                args[i], cfg[i], empty);
+      if (st != DCN_OK) return st;
+      live[i] = !empty;
+    }
+    // one launch per group of branches that run the same kernel variant; the
+    // general kernel takes its branches one launch each
+    bool done[dcn::kMaxBranches] = {};
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < n; ++i) {
+      if (!live[i] || done[i]) continue;
+      if (cfg[i].kind == 0) {
+        hipError_t e = dcn::launch_fused(cfg[i], args[i], hs);
+        if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+        done[i] = true;
+        continue;
+      }
+      dcn::MultiArgs m{};
+      int64_t total = 0;
+      for (int j = i; j < n; ++j) {
+        if (!live[j] || done[j] || !same_kernel(cfg[i], cfg[j])) continue;
+        m.start[m.n] = (int)total;
+        m.a[m.n] = args[j];
+        ++m.n;
+        total += (int64_t)args[j].B * cfg[j].tiles_per_img * cfg[j].n_otiles;
+        done[j] = true;
+      }
+      if (total >= kLimit31)
+        return fail(DCN_E_UNSUPPORTED, "dcn_forward_multi: %lld workgroups", (long long)total);
+      m.start[m.n] = (int)total;
+      hipError_t e = dcn::launch_fused_multi(cfg[i], m, hs);
+      if (e != hipSuccess) return hip_fail(e, "multi-branch forward launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_forward_multi: unexpected exception");
+  }
 }
 
 dcn_status dcn_nchw_to_nhwc(const void* src, void* dst, int32_t batch, int32_t channels,

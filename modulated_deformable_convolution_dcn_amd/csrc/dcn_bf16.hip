@@ -38,9 +38,11 @@
 
 namespace dcn {
 
-template <int CB, bool NHWC, bool FULLC>
+template <int CB, bool NHWC, bool FULLC, class Src>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-fused_bf16_kernel(FusedArgs a) {
+fused_bf16_kernel(Src src) {
+  int logical;
+  const FusedArgs& a = resolve_args(src, logical);
   constexpr int M = 128;              // output pixels per workgroup
   constexpr int NO = 256;             // output channels per workgroup
   constexpr int NQ = CB / 32;         // MFMA k-steps per block
@@ -65,7 +67,6 @@ fused_bf16_kernel(FusedArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int otile = logical % a.n_otiles;
   const int t2 = logical / a.n_otiles;
   const int tile = t2 % a.tiles_per_img;
@@ -355,31 +356,40 @@ bool bf16w_supported(const KernelConfig& kc) {
 }
 
 namespace {
-template <int CB>
-hipError_t launch_cb_bf16w(const FusedArgs& a, bool nhwc, dim3 grid, hipStream_t s) {
-  const bool fullc = a.C % CB == 0;
+template <int CB, class Src>
+hipError_t launch_cb_bf16w(const Src& src, int C, bool nhwc, dim3 grid, hipStream_t s) {
+  const bool fullc = C % CB == 0;
   const dim3 block(256);
   if (nhwc) {
-    if (fullc) hipLaunchKernelGGL((fused_bf16_kernel<CB, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fused_bf16_kernel<CB, true, false>), grid, block, 0, s, a);
+    if (fullc) hipLaunchKernelGGL((fused_bf16_kernel<CB, true, true, Src>), grid, block, 0, s, src);
+    else hipLaunchKernelGGL((fused_bf16_kernel<CB, true, false, Src>), grid, block, 0, s, src);
   } else {
-    if (fullc) hipLaunchKernelGGL((fused_bf16_kernel<CB, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fused_bf16_kernel<CB, false, false>), grid, block, 0, s, a);
+    if (fullc) hipLaunchKernelGGL((fused_bf16_kernel<CB, false, true, Src>), grid, block, 0, s, src);
+    else hipLaunchKernelGGL((fused_bf16_kernel<CB, false, false, Src>), grid, block, 0, s, src);
   }
   return hipGetLastError();
 }
-}  // namespace
 
-hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * kc.n_otiles;
+template <class Src>
+hipError_t launch_bf16w_src(const KernelConfig& kc, const Src& src, int C, int64_t nblk,
+                            hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff || !bf16w_supported(kc)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nblk);
   switch (kc.CB) {
-    case 64: return launch_cb_bf16w<64>(a, kc.nhwc, grid, s);
-    case 128: return launch_cb_bf16w<128>(a, kc.nhwc, grid, s);
-    default: return launch_cb_bf16w<256>(a, kc.nhwc, grid, s);
+    case 64: return launch_cb_bf16w<64>(src, C, kc.nhwc, grid, s);
+    case 128: return launch_cb_bf16w<128>(src, C, kc.nhwc, grid, s);
+    default: return launch_cb_bf16w<256>(src, C, kc.nhwc, grid, s);
   }
+}
+}  // namespace
+
+hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  return launch_bf16w_src(kc, a, a.C, (int64_t)a.B * kc.tiles_per_img * kc.n_otiles, s);
+}
+
+hipError_t launch_fused_bf16w_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
+  return launch_bf16w_src(kc, m, m.a[0].C, m.start[m.n], s);
 }
 
 }  // namespace dcn

@@ -11,6 +11,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "dcn_launch.h"
+
 namespace dcn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -178,6 +180,24 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
   if (bid >= full) return bid;
   const int per_xcd = full / 8;
   return (bid % 8) * per_xcd + bid / 8;
+}
+
+// Kernel-argument source: a kernel runs either one problem (FusedArgs) or a
+// table of branches (MultiArgs) in one launch.  Both give the workgroup's
+// problem and its logical tile index within that problem; logical indices
+// are XCD-remapped before the branch is found, so each XCD walks one
+// contiguous run of tiles across the branches.
+__device__ __forceinline__ const FusedArgs& resolve_args(const FusedArgs& a, int& logical) {
+  logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  return a;
+}
+__device__ __forceinline__ const FusedArgs& resolve_args(const MultiArgs& m, int& logical) {
+  const int g = xcd_logical_block(blockIdx.x, gridDim.x);
+  int br = 0;
+  for (int i = 1; i < m.n; ++i)
+    if (g >= m.start[i]) br = i;
+  logical = g - m.start[br];
+  return m.a[br];
 }
 
 }  // namespace dcn

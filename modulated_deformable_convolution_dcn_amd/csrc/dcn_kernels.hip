@@ -592,6 +592,14 @@ hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t 
   return kc.nhwc ? launch_cb<float, true>(kc, a, s) : launch_cb<float, false>(kc, a, s);
 }
 
+hipError_t launch_fused_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
+  if (m.n < 1 || m.n > kMaxBranches) return hipErrorInvalidValue;
+  if (kc.kind == 1) return launch_fused_wsk_multi(kc, m, s);
+  if (kc.kind == 2) return launch_fused_quad_multi(kc, m, s);
+  if (kc.kind == 3) return launch_fused_bf16w_multi(kc, m, s);
+  return hipErrorInvalidConfiguration;
+}
+
 hipError_t launch_coords(int bf16, const void* offset, int32_t* y0x0, uint8_t* valid4, int B,
                          int K, int kw, int Ho, int Wo, int ph, int pw, int H, int W,
                          hipStream_t s) {

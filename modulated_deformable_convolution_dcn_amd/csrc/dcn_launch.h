@@ -38,6 +38,16 @@ struct FusedArgs {
   int vec_store;       // NCHW: Ho*Wo % 4 == 0, so 4 consecutive pixels store as one 16-B write
 };
 
+// Several branches (same input map, own offsets/mask/weight/bias/output and
+// kernel size) in one launch: branch i owns the logical workgroups
+// [start[i], start[i+1]).
+constexpr int kMaxBranches = 8;
+struct MultiArgs {
+  int n;
+  int start[kMaxBranches + 1];
+  FusedArgs a[kMaxBranches];
+};
+
 // Kernel variants compiled into the library; false if none matches.
 bool config_supported(const KernelConfig& kc);
 
@@ -49,17 +59,25 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
 
 hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
 
+// One launch over all branches of `m` (kinds 1..3; every branch's config must
+// match `kc` up to tiles_per_img / n_otiles, which `m.start` accounts for).
+// hipErrorInvalidConfiguration for the general kernel (kind 0).
+hipError_t launch_fused_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
+
 // The k-split-over-waves kernel (fp32, 64- or 128-wide output tiles).
 bool wsk_supported(const KernelConfig& kc);
 hipError_t launch_fused_wsk(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+hipError_t launch_fused_wsk_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
 
 // The 32-pixel x 32-channel-per-wave kernel (fp32, 64-wide output tiles).
 bool quad_supported(const KernelConfig& kc);
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
 
 // The wide bf16 kernel (128 pixels x 256 output channels per workgroup).
 bool bf16w_supported(const KernelConfig& kc);
 hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+hipError_t launch_fused_bf16w_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
 
 // dst[b, p, c] = src[b, c, p] for p over height*width pixels.
 hipError_t launch_nchw_to_nhwc(int bf16, const void* src, void* dst, int B, int C, int HW,

@@ -35,9 +35,11 @@
 
 namespace dcn {
 
-template <bool NHWC, bool FULLC>
+template <bool NHWC, bool FULLC, class Src>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-fused_quad_kernel(FusedArgs a) {
+fused_quad_kernel(Src src) {
+  int logical;
+  const FusedArgs& a = resolve_args(src, logical);
   constexpr int M = 64;           // output pixels per workgroup
   constexpr int NO = 64;          // output channels per workgroup
   constexpr int CB = 64;          // channels per k-block
@@ -65,7 +67,6 @@ fused_quad_kernel(FusedArgs a) {
                     wave * NSLOT * PW;
   float* const red = reinterpret_cast<float*>(smem);  // [wave][NO][RST]
 
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int otile = logical % a.n_otiles;
   const int t2 = logical / a.n_otiles;
   const int tile = t2 % a.tiles_per_img;
@@ -339,20 +340,31 @@ bool quad_supported(const KernelConfig& kc) {
   return !kc.bf16 && kc.CB == 64 && kc.NO == 64 && kc.M == 64;
 }
 
-hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * kc.n_otiles;
+namespace {
+template <class Src>
+hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, int64_t nblk,
+                           hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
-  const bool fullc = a.C % 64 == 0;
+  const bool fullc = C % 64 == 0;
   const dim3 grid((unsigned)nblk), block(256);
   if (kc.nhwc) {
-    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fused_quad_kernel<true, false>), grid, block, 0, s, a);
+    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<true, true, Src>), grid, block, 0, s, src);
+    else hipLaunchKernelGGL((fused_quad_kernel<true, false, Src>), grid, block, 0, s, src);
   } else {
-    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fused_quad_kernel<false, false>), grid, block, 0, s, a);
+    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<false, true, Src>), grid, block, 0, s, src);
+    else hipLaunchKernelGGL((fused_quad_kernel<false, false, Src>), grid, block, 0, s, src);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
+  return launch_quad_src(kc, a, a.C, (int64_t)a.B * kc.tiles_per_img * kc.n_otiles, s);
+}
+
+hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
+  return launch_quad_src(kc, m, m.a[0].C, m.start[m.n], s);
 }
 
 }  // namespace dcn

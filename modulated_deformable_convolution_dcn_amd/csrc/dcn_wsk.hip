@@ -33,9 +33,11 @@
 
 namespace dcn {
 
-template <int M, int NO, bool NHWC>
+template <int M, int NO, bool NHWC, class Src>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-fused_wsk_kernel(FusedArgs a) {
+fused_wsk_kernel(Src src) {
+  int logical;
+  const FusedArgs& a = resolve_args(src, logical);
   constexpr int CB = 64;          // channels per k-block
   constexpr int MT = M / 16;      // row groups = gather passes (16 pixels x 4 quads each)
   constexpr int NT = NO / 16;
@@ -58,7 +60,6 @@ fused_wsk_kernel(FusedArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int otile = logical % a.n_otiles;
   const int t2 = logical / a.n_otiles;
   const int tile = t2 % a.tiles_per_img;
@@ -343,13 +344,24 @@ fused_wsk_kernel(FusedArgs a) {
 }
 
 namespace {
-template <int M, int NO, bool NHWC>
-hipError_t launch_wsk_variant(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * kc.n_otiles;
+template <int M, int NO, bool NHWC, class Src>
+hipError_t launch_wsk_variant(const Src& src, int64_t nblk, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fused_wsk_kernel<M, NO, NHWC>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fused_wsk_kernel<M, NO, NHWC, Src>), dim3((unsigned)nblk), dim3(256), 0, s,
+                     src);
   return hipGetLastError();
+}
+
+template <class Src>
+hipError_t launch_wsk_src(const KernelConfig& kc, const Src& src, int64_t nblk, hipStream_t s) {
+  if (kc.NO == 64 && kc.M == 64)
+    return kc.nhwc ? launch_wsk_variant<64, 64, true>(src, nblk, s)
+                   : launch_wsk_variant<64, 64, false>(src, nblk, s);
+  if (kc.NO == 128 && kc.M == 32)
+    return kc.nhwc ? launch_wsk_variant<32, 128, true>(src, nblk, s)
+                   : launch_wsk_variant<32, 128, false>(src, nblk, s);
+  return hipErrorInvalidValue;
 }
 }  // namespace
 
@@ -358,13 +370,11 @@ bool wsk_supported(const KernelConfig& kc) {
 }
 
 hipError_t launch_fused_wsk(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  if (kc.NO == 64 && kc.M == 64)
-    return kc.nhwc ? launch_wsk_variant<64, 64, true>(kc, a, s)
-                   : launch_wsk_variant<64, 64, false>(kc, a, s);
-  if (kc.NO == 128 && kc.M == 32)
-    return kc.nhwc ? launch_wsk_variant<32, 128, true>(kc, a, s)
-                   : launch_wsk_variant<32, 128, false>(kc, a, s);
-  return hipErrorInvalidValue;
+  return launch_wsk_src(kc, a, (int64_t)a.B * kc.tiles_per_img * kc.n_otiles, s);
+}
+
+hipError_t launch_fused_wsk_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
+  return launch_wsk_src(kc, m, m.start[m.n], s);
 }
 
 }  // namespace dcn

@@ -178,3 +178,35 @@ def test_transpose_checks_fire_before_any_launch():
     assert lib.dcn_nchw_to_nhwc(None, None, 0, 4, 4, 4, 0, None) == 0      # empty: no-op
     assert lib.dcn_nchw_to_nhwc(None, fake, 1, 4, 4, 4, 0, None) == 1
     assert lib.dcn_nchw_to_nhwc(ctypes.c_void_p(0x10004), fake, 1, 4, 4, 4, 1, None) == 5
+
+
+def test_multi_branch_checks_fire_before_any_launch():
+    lib = _lib.load()
+    a = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1))
+    b = Plan(Desc(1, 64, 16, 16, 32, 1, 1, 0, 0))
+    c = Plan(Desc(1, 64, 16, 15, 64, 3, 3, 1, 1))   # different input width
+    fake = 0x10000
+    V = ctypes.c_void_p
+    arr = lambda *xs: (V * len(xs))(*xs)  # noqa: E731
+    sizes = lambda *ps: (ctypes.c_size_t * len(ps))(*[p.workspace_bytes for p in ps])  # noqa: E731
+
+    def call(plans, n=None, x=fake, offs=None, outs=None, packs=None, ws=None):
+        n = len(plans) if n is None else n
+        offs = offs if offs is not None else arr(*[fake] * len(plans))
+        outs = outs if outs is not None else arr(*[fake] * len(plans))
+        packs = packs if packs is not None else arr(*[fake] * len(plans))
+        ws = ws if ws is not None else sizes(*plans)
+        return lib.dcn_forward_multi(n, arr(*[p._h.value for p in plans]), V(x), offs, None,
+                                     packs, ws, None, outs, None)
+
+    assert call([a, b], n=0) == 0
+    assert call([a, b], n=-1) == 2
+    assert call([a] * 9) == 4
+    assert call([a, c]) == 2                             # branches read different inputs
+    assert "different input" in lib.dcn_last_error().decode()
+    assert call([a, b], outs=arr(fake, None)) == 1       # branch 1 has no output
+    assert call([a, b], packs=arr(fake, None)) == 8
+    short = (ctypes.c_size_t * 2)(a.workspace_bytes, b.workspace_bytes - 1)
+    assert call([a, b], ws=short) == 8                   # branch 1's workspace too small
+    assert call([a, b], x=0) == 1                        # shared input missing
+    assert lib.dcn_forward_multi(1, None, V(fake), None, None, None, None, None, None, None) == 1

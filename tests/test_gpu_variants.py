@@ -110,3 +110,63 @@ def test_torchvision_order_nchw_input(name):
     torch.cuda.synchronize()
     assert tuple(out.shape) == (spec.B, spec.O, spec.Ho, spec.Wo)
     compare(pixel_major(out.cpu().numpy(), "nchw"), ref, norm, d["bias"], spec.dtype, name)
+
+
+# Multi-branch launches: several deformable convolutions on one input map
+# (page 2: four ASPP branches per BiRefNet decoder block).  Each branch is
+# checked against the oracle and bit for bit against its own single launch.
+MULTI_CASES = {
+    # all four on the 32x32-per-wave kernel: one launch
+    "aspp4_quad": [W["birefnet512_fp32"].scaled(H=30, W=26, kh=k, kw=k, ph=k // 2, pw=k // 2,
+                                                 seed=40 + k) for k in (1, 3, 5, 7)],
+    # mixed variants: quad (NCHW and NHWC outputs: two groups), k-split, general
+    "mixed_fp32": [W["birefnet512_fp32"].scaled(H=21, W=23, seed=51),
+                   W["birefnet512_fp32"].scaled(H=21, W=23, O=40, kh=3, kw=3, ph=1, pw=1,
+                                                seed=52),
+                   W["birefnet512_fp32"].scaled(H=21, W=23, O=100, kh=3, kw=5, ph=1, pw=2,
+                                                seed=53),
+                   W["birefnet512_fp32"].scaled(H=21, W=23, O=16, kh=1, kw=1, ph=0, pw=0,
+                                                seed=54)],
+    "bf16_wide": [D.scaled(B=2, H=13, W=15, seed=61),
+                  D.scaled(B=2, H=13, W=15, O=200, kh=1, kw=1, ph=0, pw=0, seed=62)],
+}
+MULTI_LAYOUTS = {"mixed_fp32": ["nchw", "nhwc", "nchw", "nchw"]}
+
+
+@pytest.mark.parametrize("optional", [True, False])
+@pytest.mark.parametrize("name", sorted(MULTI_CASES))
+def test_multi_branch(name, optional):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import Desc, Plan, forward_multi
+    specs = MULTI_CASES[name]
+    layouts = MULTI_LAYOUTS.get(name, ["nchw"] * len(specs))
+    ds = [synth.make_inputs(sp) for sp in specs]
+    for d in ds[1:]:            # one shared input map
+        d["x"] = ds[0]["x"]
+        if "bits" in d:
+            d["bits"]["x"] = ds[0]["bits"]["x"]
+    if not optional:            # branch 1 without mask, branch 0 without bias
+        ds[1]["mask"] = None
+        ds[0]["bias"] = None
+    print("case", name, "optional" if optional else "partial", flush=True)
+    plans, offs, msks, packs, biases, devs = [], [], [], [], [], []
+    for sp, d, lay in zip(specs, ds, layouts):
+        dev = device_inputs(sp, d)
+        plan = Plan(Desc(sp.B, sp.C, sp.H, sp.W, sp.O, sp.kh, sp.kw, sp.ph, sp.pw, sp.dtype, lay))
+        plans.append(plan)
+        offs.append(dev["offset"])
+        msks.append(dev["mask"])
+        packs.append(plan.pack_weight(dev["weight"]))
+        biases.append(dev["bias"])
+        devs.append(dev)
+    x = devs[0]["x"]
+    outs = forward_multi(plans, x, offs, msks, packs, biases)
+    singles = [p.forward_packed(x, o, m, w, b) for p, o, m, w, b in
+               zip(plans, offs, msks, packs, biases)]
+    torch.cuda.synchronize()
+    for i, (sp, d, lay) in enumerate(zip(specs, ds, layouts)):
+        got = outs[i].cpu().numpy()
+        assert np.array_equal(got, singles[i].cpu().numpy()), "branch %d differs from its own launch" % i
+        ref, norm = oracle.forward(oracle_shape(sp), d["x"], d["offset"], d["mask"], d["weight"],
+                                   d["bias"])
+        compare(pixel_major(got, lay), ref, norm, d["bias"], sp.dtype, "%s branch %d" % (name, i))
