@@ -327,47 +327,57 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 //   layout 3 (bf16 16x16x32 fragments, VEC = 8): [CB/32][NO/16][g][16][8]
 //            = channel 32q + 8g + e, output 16*nt + col -- fragment (q, nt)
 //            is one 1 KB run in lane order.
+// Index of (channel c_in, output o_in) inside one packed block.
+__device__ __forceinline__ int packed_index(int c_in, int o_in, int layout, int NO, int VEC) {
+  const int nt = o_in >> 4, col = o_in & 15;
+  switch (layout) {
+    case 0: return ((c_in / VEC) * NO + o_in) * VEC + c_in % VEC;
+    case 1: {
+      const int wv = c_in >> 4, g = (c_in >> 2) & 3, e = c_in & 3;
+      return (((wv * (NO / 16) + nt) * 4 + g) * 16 + col) * 4 + e;
+    }
+    case 2: {
+      const int half = c_in >> 5, g = (c_in >> 3) & 3, q = (c_in >> 2) & 1, e = c_in & 3;
+      return ((((half * (NO / 16) + nt) * 2 + q) * 4 + g) * 16 + col) * 4 + e;
+    }
+    default: {
+      const int q = c_in >> 5, g = (c_in >> 3) & 3, e = c_in & 7;
+      return (((q * (NO / 16) + nt) * 4 + g) * 16 + col) * 8 + e;
+    }
+  }
+}
+
+// Pass 1: every weight element, read in its own order [O][C][kh][kw]
+// (coalesced), written to its packed place.
 template <class T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* __restrict__ wp,
-                                                   int O, int C, int kh, int kw, int CB, int NO,
-                                                   int VEC, int nchunk, int layout, int64_t total) {
-  const int K = kh * kw;
+                                                   int O, int C, int K, int CB, int NO, int VEC,
+                                                   int nchunk, int layout) {
+  const int64_t total = (int64_t)O * C * K;
+  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < total;
+       s += (int64_t)gridDim.x * 256) {
+    const int tap = (int)(s % K);
+    const int64_t oc = s / K;
+    const int c = (int)(oc % C), o = (int)(oc / C);
+    const int otile = o / NO, chunk = c / CB;
+    const int64_t block = ((int64_t)otile * K + tap) * nchunk + chunk;
+    wp[block * CB * NO + packed_index(c - chunk * CB, o - otile * NO, layout, NO, VEC)] = w[s];
+  }
+}
+
+// Before pass 1, only when C or O is not a multiple of the block: zero every
+// block that holds padding (pass 1 then overwrites its real entries).
+template <class T>
+__global__ __launch_bounds__(256) void pack_pad_kernel(T* __restrict__ wp, int O, int C, int K,
+                                                       int CB, int NO, int nchunk,
+                                                       int64_t total) {
   const int blk = CB * NO;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
-    const int ib = (int)(idx % blk);
-    int64_t r = idx / blk;
-    const int chunk = (int)(r % nchunk);
-    r /= nchunk;
-    const int tap = (int)(r % K);
-    const int otile = (int)(r / K);
-    int c_in, o_in;
-    if (layout == 0) {
-      const int v = ib % VEC;
-      o_in = (ib / VEC) % NO;
-      c_in = (ib / (VEC * NO)) * VEC + v;
-    } else if (layout == 1) {
-      const int e = ib & 3, col = (ib >> 2) & 15, g = (ib >> 6) & 3;
-      const int nt = (ib >> 8) % (NO / 16), wv = (ib >> 8) / (NO / 16);
-      c_in = 16 * wv + 4 * g + e;
-      o_in = 16 * nt + col;
-    } else if (layout == 3) {
-      const int e = ib & 7, col = (ib >> 3) & 15, g = (ib >> 7) & 3;
-      const int nt = (ib >> 9) % (NO / 16), q = (ib >> 9) / (NO / 16);
-      c_in = 32 * q + 8 * g + e;
-      o_in = 16 * nt + col;
-    } else {
-      const int e = ib & 3, col = (ib >> 2) & 15, g = (ib >> 6) & 3, q = (ib >> 8) & 1;
-      const int nt = (ib >> 9) % (NO / 16), half = (ib >> 9) / (NO / 16);
-      c_in = 32 * half + 8 * g + 4 * q + e;
-      o_in = 16 * nt + col;
-    }
-    const int o = otile * NO + o_in;
-    const int c = chunk * CB + c_in;
-    const int i = tap / kw, j = tap % kw;
-    T val = static_cast<T>(0.0f);
-    if (o < O && c < C) val = w[(((int64_t)o * C + c) * kh + i) * kw + j];
-    wp[idx] = val;
+    const int64_t block = idx / blk;  // [otile][tap][chunk]
+    const int chunk = (int)(block % nchunk);
+    const int otile = (int)(block / ((int64_t)nchunk * K));
+    if ((chunk + 1) * CB > C || (otile + 1) * NO > O) wp[idx] = static_cast<T>(0.0f);
   }
 }
 
@@ -570,14 +580,26 @@ int64_t packed_weight_elems(const KernelConfig& kc, int K) {
 hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, int O, int C,
                        int kh, int kw, hipStream_t s) {
   const int64_t total = packed_weight_elems(kc, kh * kw);
+  const int K = kh * kw;
+  const bool padded = C % kc.CB != 0 || O % kc.NO != 0;
+  const int layout = kc.bf16 ? (kc.kind == 3 ? 3 : 0) : kc.kind;
+  const unsigned g_src = grid_for((int64_t)O * C * K);
   if (kc.bf16) {
-    hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s,
-                       static_cast<const __bf16*>(weight), static_cast<__bf16*>(wpack), O, C,
-                       kh, kw, kc.CB, kc.NO, 8, kc.nchunk, kc.kind == 3 ? 3 : 0, total);
+    __bf16* wp = static_cast<__bf16*>(wpack);
+    if (padded)
+      hipLaunchKernelGGL(pack_pad_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s, wp, O, C,
+                         K, kc.CB, kc.NO, kc.nchunk, total);
+    hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(g_src), dim3(256), 0, s,
+                       static_cast<const __bf16*>(weight), wp, O, C, K, kc.CB, kc.NO, 8,
+                       kc.nchunk, layout);
   } else {
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s,
-                       static_cast<const float*>(weight), static_cast<float*>(wpack), O, C, kh,
-                       kw, kc.CB, kc.NO, 4, kc.nchunk, kc.kind, total);
+    float* wp = static_cast<float*>(wpack);
+    if (padded)
+      hipLaunchKernelGGL(pack_pad_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s, wp, O, C,
+                         K, kc.CB, kc.NO, kc.nchunk, total);
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(g_src), dim3(256), 0, s,
+                       static_cast<const float*>(weight), wp, O, C, K, kc.CB, kc.NO, 4, kc.nchunk,
+                       layout);
   }
   return hipGetLastError();
 }

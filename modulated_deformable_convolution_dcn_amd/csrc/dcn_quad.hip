@@ -45,7 +45,7 @@ fused_quad_kernel(Src src) {
   constexpr int CB = 64;          // channels per k-block
   constexpr int PW = 32;          // pixels per wave
   constexpr int NT = NO / 16;     // 16-column MFMA tiles
-  constexpr int AST = 36;         // column-tile row stride (32 channels + pad)
+  constexpr int AST = 32;         // column-tile row: 32 channels, 16-byte chunks XOR-swizzled
   constexpr int NSLOT = 3;        // coefficient ring
   constexpr int A_FLOATS = PW * AST;
   constexpr int MAIN_BYTES = 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 32;
@@ -66,6 +66,10 @@ fused_quad_kernel(Src src) {
   u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 16) +
                     wave * NSLOT * PW;
   float* const red = reinterpret_cast<float*>(smem);  // [wave][NO][RST]
+  // Column tile: row r (pixel), 16-byte chunk k (channels 4k .. 4k+3) at
+  // float r * 32 + 4 * (k ^ ((r >> 1) & 7)): the eight-lane row writes of two
+  // rows and the sixteen-row fragment reads both cover all banks.
+  auto a_at = [](int r, int k) { return r * AST + 4 * (k ^ ((r >> 1) & 7)); };
 
   const int otile = logical % a.n_otiles;
   const int t2 = logical / a.n_otiles;
@@ -151,7 +155,7 @@ fused_quad_kernel(Src src) {
     return wblocks + (size_t)kb * (CB * NO) + (size_t)wc * (NT * 2 * 256) + (g * 16 + rl) * 4;
   };
   auto a_frag = [&](int mt, int q) {
-    return *reinterpret_cast<const f32x4*>(&Aw[(mt * 16 + rl) * AST + g * 8 + q * 4]);
+    return *reinterpret_cast<const f32x4*>(&Aw[a_at(mt * 16 + rl, 2 * g + q)]);
   };
 
   using S0 = std::integral_constant<int, 0>;
@@ -188,7 +192,7 @@ fused_quad_kernel(Src src) {
     for (int p = 0; p < 2; ++p) {
       const u32x4 r = Ops<float>::blend(Cw[s0 * PW + p * 8 + pp], gv[p][0], gv[p][1], gv[p][2],
                                         gv[p][3]);
-      *reinterpret_cast<u32x4*>(&Aw[(p * 8 + pp) * AST + sl * 4]) = r;
+      *reinterpret_cast<u32x4*>(&Aw[a_at(p * 8 + pp, sl)]) = r;
       const u32x4 off = Co[s1 * PW + p * 8 + pp];
 #pragma unroll
       for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok1 ? off[c] + cb1 : kNoCorner);
@@ -250,7 +254,7 @@ fused_quad_kernel(Src src) {
               for (int kk = 0; kk < 4; ++kk) r[kk] = __builtin_fmaf(w[pi][y], v[kk], r[kk]);
             }
           } else if constexpr (y == 4) {
-            *reinterpret_cast<f32x4*>(&Aw[(p * 8 + pp) * AST + sl * 4]) = r;
+            *reinterpret_cast<f32x4*>(&Aw[a_at(p * 8 + pp, sl)]) = r;
           } else {
             constexpr int c = y - 5;
             gv[p][c] = load16(xr, okn ? off[pi][c] + cbn : kNoCorner);
