@@ -58,6 +58,8 @@ def _load():
         lib.dcn_oracle_forward.restype = ctypes.c_int
         lib.dcn_oracle_coords.argtypes = [ctypes.POINTER(_Shape), vp, vp, vp, ctypes.c_int]
         lib.dcn_oracle_coords.restype = ctypes.c_int
+        lib.dcn_oracle_backward.argtypes = [ctypes.POINTER(_Shape)] + [vp] * 15 + [ctypes.c_int]
+        lib.dcn_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -156,3 +158,34 @@ def coords(shape: Shape, offset, nthreads: int = 0):
     if rc != 0:
         raise ValueError("dcn_oracle_coords failed with code %d" % rc)
     return y0x0, valid4
+
+
+def backward(shape: Shape, x, offset, mask, weight, grad_out, nthreads: int = 0):
+    """Oracle backward: the exact derivative of ``forward`` (see dcn_oracle.h).
+
+    ``grad_out`` is dL/dout in the forward's NCHW layout [B, O, Ho, Wo].
+    Returns ``(grads, norms)``: dicts with keys ``x`` [B,H,W,C], ``offset``
+    [B,2K,Ho,Wo], ``mask`` [B,K,Ho,Wo], ``weight`` [O,C,kh,kw], ``bias`` [O],
+    float64; ``norms`` holds each element's absolute-term sum (the parity
+    normaliser).
+    """
+    s = shape
+    x, offset, mask, weight, grad_out = (_f32(a) for a in (x, offset, mask, weight, grad_out))
+    assert x.shape == (s.B, s.H, s.W, s.C), x.shape
+    assert offset.shape == (s.B, 2 * s.K, s.Ho, s.Wo), offset.shape
+    assert mask is None or mask.shape == (s.B, s.K, s.Ho, s.Wo), mask.shape
+    assert weight.shape == (s.O, s.C, s.kh, s.kw), weight.shape
+    assert grad_out.shape == (s.B, s.O, s.Ho, s.Wo), grad_out.shape
+    shapes = {"x": (s.B, s.H, s.W, s.C), "offset": (s.B, 2 * s.K, s.Ho, s.Wo),
+              "mask": (s.B, s.K, s.Ho, s.Wo), "weight": (s.O, s.C, s.kh, s.kw), "bias": (s.O,)}
+    g = {k: np.empty(v, dtype=np.float64) for k, v in shapes.items()}
+    n = {k: np.empty(v, dtype=np.float64) for k, v in shapes.items()}
+    order = ("x", "offset", "mask", "weight", "bias")
+    cs = s._c()
+    rc = _load().dcn_oracle_backward(ctypes.byref(cs), _ptr(x), _ptr(offset), _ptr(mask),
+                                     _ptr(weight), _ptr(grad_out),
+                                     *[_ptr(g[k]) for k in order], *[_ptr(n[k]) for k in order],
+                                     int(nthreads))
+    if rc != 0:
+        raise ValueError("dcn_oracle_backward failed with code %d" % rc)
+    return g, n

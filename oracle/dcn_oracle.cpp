@@ -217,3 +217,161 @@ extern "C" int dcn_oracle_coords(const dcn_oracle_shape* s, const float* offset,
   for (auto& th : pool) th.join();
   return 0;
 }
+
+// ---------------------------------------------------------------- backward
+// The forward, differentiated term by term.  For output pixel (b, ho, wo),
+// tap k with sampling point p in floor cell (y0, x0), fractions (ly, lx):
+//   su[c]  = sum_valid w_ab x_ab[c]           (unmodulated sample)
+//   s[c]   = m su[c]                          (the column-matrix entry)
+//   out[o] = bias[o] + sum_{k,c} W[o,c,k] s[c]
+// so with g[o] = dL/dout[o] and gs[c] = sum_o g[o] W[o,c,k]:
+//   dL/dW[o,c,k]   += g[o] s[c]               dL/dbias[o] += g[o]
+//   dL/dx_ab[c]    += gs[c] m w_ab            (valid corners)
+//   dL/dm          += sum_c gs[c] su[c]
+//   dL/ddy         += m sum_c gs[c] sum_valid (d w_ab / d ly) x_ab[c]
+//   dL/ddx         += m sum_c gs[c] sum_valid (d w_ab / d lx) x_ab[c]
+// with d w / d ly = {-(1-lx), -lx, (1-lx), lx} and d w / d lx =
+// {-(1-ly), (1-ly), -ly, ly} for corners (0,0), (0,1), (1,0), (1,1).
+namespace {
+
+struct BwdAcc {
+  std::vector<double> gx, ngx, gw, ngw, gb, ngb;
+};
+
+void backward_pixel(const Dims& d, const float* x, const float* offset, const float* mask,
+                    const float* weight, const float* grad_out, int64_t p, BwdAcc& acc,
+                    double* goff, double* gmask, double* ngoff, double* ngmask,
+                    std::vector<double>& gs, std::vector<double>& gsa) {
+  const int64_t hw = d.Ho * d.Wo;
+  const int64_t b = p / hw;
+  const int64_t ho = (p % hw) / d.Wo;
+  const int64_t wo = p % d.Wo;
+  auto g_at = [&](int64_t o) {
+    return static_cast<double>(grad_out[((b * d.O + o) * d.Ho + ho) * d.Wo + wo]);
+  };
+  for (int64_t o = 0; o < d.O; ++o) {
+    acc.gb[o] += g_at(o);
+    acc.ngb[o] += std::fabs(g_at(o));
+  }
+  for (int64_t k = 0; k < d.K; ++k) {
+    const int64_t i = k / d.kw, j = k % d.kw;
+    const int64_t oy = ((b * 2 * d.K + 2 * k) * d.Ho + ho) * d.Wo + wo;
+    const int64_t ox = ((b * 2 * d.K + 2 * k + 1) * d.Ho + ho) * d.Wo + wo;
+    const int64_t om = ((b * d.K + k) * d.Ho + ho) * d.Wo + wo;
+    const double m = mask ? static_cast<double>(mask[om]) : 1.0;
+    const Coord cd = tap_coord(d, ho, wo, i, j, offset[oy], offset[ox]);
+    const double ly = cd.ly, lx = cd.lx;
+    const double wgt[4] = {(1.0 - ly) * (1.0 - lx), (1.0 - ly) * lx, ly * (1.0 - lx), ly * lx};
+    const double dwy[4] = {-(1.0 - lx), -lx, 1.0 - lx, lx};
+    const double dwx[4] = {-(1.0 - ly), 1.0 - ly, -ly, ly};
+    const float* v[4] = {nullptr, nullptr, nullptr, nullptr};
+    int64_t at[4] = {0, 0, 0, 0};
+    for (int a = 0; a < 2; ++a)
+      for (int bb = 0; bb < 2; ++bb) {
+        if (!corner_valid(d, cd.y0, cd.x0, a, bb)) continue;
+        const int64_t yy = static_cast<int64_t>(cd.y0) + a;
+        const int64_t xx = static_cast<int64_t>(cd.x0) + bb;
+        at[2 * a + bb] = ((b * d.H + yy) * d.W + xx) * d.C;
+        v[2 * a + bb] = &x[at[2 * a + bb]];
+      }
+    // gs[c] = sum_o g[o] W[o, c, k] and its absolute-term bound
+    for (int64_t c = 0; c < d.C; ++c) {
+      double t = 0.0, ta = 0.0;
+      for (int64_t o = 0; o < d.O; ++o) {
+        const double w = weight[((o * d.C + c) * d.kh + i) * d.kw + j];
+        t += g_at(o) * w;
+        ta += std::fabs(g_at(o)) * std::fabs(w);
+      }
+      gs[c] = t;
+      gsa[c] = ta;
+    }
+    double sm = 0.0, nsm = 0.0, sdy = 0.0, nsdy = 0.0, sdx = 0.0, nsdx = 0.0;
+    for (int64_t c = 0; c < d.C; ++c) {
+      double su = 0.0, sua = 0.0, ty = 0.0, tya = 0.0, tx = 0.0, txa = 0.0;
+      for (int q = 0; q < 4; ++q) {
+        if (!v[q]) continue;
+        const double xv = v[q][c];
+        su += wgt[q] * xv;
+        sua += wgt[q] * std::fabs(xv);
+        ty += dwy[q] * xv;
+        tya += std::fabs(dwy[q] * xv);
+        tx += dwx[q] * xv;
+        txa += std::fabs(dwx[q] * xv);
+        acc.gx[at[q] + c] += gs[c] * m * wgt[q];
+        acc.ngx[at[q] + c] += gsa[c] * std::fabs(m) * wgt[q];
+      }
+      sm += gs[c] * su;
+      nsm += gsa[c] * sua;
+      sdy += gs[c] * ty;
+      nsdy += gsa[c] * tya;
+      sdx += gs[c] * tx;
+      nsdx += gsa[c] * txa;
+      for (int64_t o = 0; o < d.O; ++o) {
+        const int64_t wi = ((o * d.C + c) * d.kh + i) * d.kw + j;
+        acc.gw[wi] += g_at(o) * m * su;
+        acc.ngw[wi] += std::fabs(g_at(o)) * std::fabs(m) * sua;
+      }
+    }
+    if (gmask) gmask[om] = sm;
+    if (ngmask) ngmask[om] = nsm;
+    if (goff) {
+      goff[oy] = m * sdy;
+      goff[ox] = m * sdx;
+    }
+    if (ngoff) {
+      ngoff[oy] = std::fabs(m) * nsdy;
+      ngoff[ox] = std::fabs(m) * nsdx;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int dcn_oracle_backward(const dcn_oracle_shape* s, const float* x,
+                                   const float* offset, const float* mask, const float* weight,
+                                   const float* grad_out, double* gx, double* goff,
+                                   double* gmask, double* gw, double* gb, double* ngx,
+                                   double* ngoff, double* ngmask, double* ngw, double* ngb,
+                                   int nthreads) {
+  if (!s || !x || !offset || !weight || !grad_out) return 1;
+  Dims d;
+  if (!make_dims(s, &d)) return 2;
+  const int64_t npix = d.B * d.Ho * d.Wo;
+  const int64_t nx = d.B * d.H * d.W * d.C, nw = d.O * d.C * d.K;
+  const int nt = resolve_threads(nthreads, npix);
+  std::vector<BwdAcc> accs(static_cast<size_t>(nt));
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t) {
+    pool.emplace_back([&, t]() {
+      BwdAcc& a = accs[t];
+      a.gx.assign(nx, 0.0);
+      a.ngx.assign(nx, 0.0);
+      a.gw.assign(nw, 0.0);
+      a.ngw.assign(nw, 0.0);
+      a.gb.assign(d.O, 0.0);
+      a.ngb.assign(d.O, 0.0);
+      std::vector<double> gsv(static_cast<size_t>(d.C)), gsa(static_cast<size_t>(d.C));
+      // contiguous pixel ranges: the per-thread sums run in pixel order
+      const int64_t lo = npix * t / nt, hi = npix * (t + 1) / nt;
+      for (int64_t p = lo; p < hi; ++p)
+        backward_pixel(d, x, offset, mask, weight, grad_out, p, a, goff, gmask, ngoff, ngmask,
+                       gsv, gsa);
+    });
+  }
+  for (auto& th : pool) th.join();
+  auto reduce = [&](double* dst, std::vector<double> BwdAcc::*field, int64_t n) {
+    if (!dst) return;
+    for (int64_t e = 0; e < n; ++e) dst[e] = 0.0;
+    for (int t = 0; t < nt; ++t) {
+      const std::vector<double>& v = accs[t].*field;
+      for (int64_t e = 0; e < n; ++e) dst[e] += v[e];
+    }
+  };
+  reduce(gx, &BwdAcc::gx, nx);
+  reduce(ngx, &BwdAcc::ngx, nx);
+  reduce(gw, &BwdAcc::gw, nw);
+  reduce(ngw, &BwdAcc::ngw, nw);
+  reduce(gb, &BwdAcc::gb, d.O);
+  reduce(ngb, &BwdAcc::ngb, d.O);
+  return 0;
+}

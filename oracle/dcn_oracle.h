@@ -69,6 +69,34 @@ int dcn_oracle_forward(const dcn_oracle_shape* s, const float* x, const float* o
 int dcn_oracle_coords(const dcn_oracle_shape* s, const float* offset, int32_t* y0x0,
                       uint8_t* valid4, int nthreads);
 
+/*
+ * Backward: the gradients of a scalar loss L given g = dL/dout, obtained by
+ * differentiating the forward above term by term (the pages state the
+ * forward only; this is its exact derivative).  The sampling value is
+ * piecewise bilinear in the offsets; the offset gradient is its derivative
+ * inside the floor cell of the sampling point (d ly / d dy = d lx / d dx = 1,
+ * with floor and validity held fixed), corners outside the image contribute
+ * nothing.
+ *   grad_out [B, O, Ho, Wo] fp32 (the forward's NCHW layout)
+ * Outputs (fp64; any may be NULL; each non-NULL one is fully written):
+ *   gx    [B, H, W, C]      dL/dx
+ *   goff  [B, 2K, Ho, Wo]   dL/doffset (channel 2k: dy, 2k+1: dx)
+ *   gmask [B, K, Ho, Wo]    dL/dmask (also when mask is NULL, at mask = 1)
+ *   gw    [O, C, kh, kw]    dL/dweight
+ *   gb    [O]               dL/dbias
+ * and normalisers of the same shapes (any may be NULL): the sum of the
+ * absolute values of the terms of each gradient element, with the inner
+ * contraction sum_o g[o] * weight[o, c, k] expanded into absolute terms too.
+ * Gradients are sums over output pixels: each thread accumulates its own
+ * copy and the copies are added in thread order, so a given nthreads always
+ * gives the same bits (memory: one copy of gx and gw per thread).
+ */
+int dcn_oracle_backward(const dcn_oracle_shape* s, const float* x, const float* offset,
+                        const float* mask, const float* weight, const float* grad_out,
+                        double* gx, double* goff, double* gmask, double* gw, double* gb,
+                        double* ngx, double* ngoff, double* ngmask, double* ngw, double* ngb,
+                        int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
