@@ -166,6 +166,8 @@ def main() -> int:
                          "bias, shared input) per step with one multi-branch call")
     ap.add_argument("--sequential", action="store_true",
                     help="with --branches: one forward call per branch instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the fp32 backward (all five gradients) instead of the forward")
     ap.add_argument("--bands", type=int, default=1,
                     help="run the forward as this many output-row bands (row0 calls), "
                          "back to back on one stream")
@@ -273,6 +275,24 @@ def main() -> int:
         if ev is not None:
             ev[2].record()
 
+    if args.backward:
+        if spec.dtype != "f32":
+            print("bench.py: the backward is fp32 only", file=sys.stderr)
+            return 2
+        gout = torch.randn(plan.out_shape(), device="cuda")
+        bws = torch.empty(plan.backward_workspace_bytes(), dtype=torch.uint8, device="cuda")
+        grads = plan.backward(x_nhwc, dev["offset"], dev["mask"], dev["weight"], gout,
+                              workspace=bws)
+
+        def step(ev=None):  # noqa: F811 -- the backward step replaces the forward one
+            if ev is not None:
+                ev[0].record()
+                ev[1].record()
+            plan.backward(x_nhwc, dev["offset"], dev["mask"], dev["weight"], gout, grads=grads,
+                          workspace=bws)
+            if ev is not None:
+                ev[2].record()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -297,7 +317,8 @@ def main() -> int:
     ms_per_step = (sum(e[0].elapsed_time(e[2]) for e in events) / args.steps if args.cold
                    else elapsed * 1e3 / args.steps)
     P = spec.pixels * nbr
-    flops = spec.gemm_flops * nbr
+    # the backward runs two contractions of the forward's size (dL/dsample and dL/dW)
+    flops = spec.gemm_flops * nbr * (2 if args.backward else 1)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[spec.dtype]
     fused_tflops = flops / (fused_ms * 1e-3) / 1e12
@@ -318,6 +339,7 @@ def main() -> int:
                    "W": spec.W, "kernel": "%dx%d" % (spec.kh, spec.kw),
                    "pad": [spec.ph, spec.pw], "out_layout": args.layout,
                    "input_layout": args.input_layout, "row_bands": nb,
+                   "pass": "backward" if args.backward else "forward",
                    "branches": nbr, "branch_launch": ("one per branch" if args.sequential
                                                       else "one for all") if nbr > 1 else None},
         "tflops": tflops,

@@ -165,6 +165,32 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
                              const void* const* packed_weights, const size_t* workspace_bytes,
                              const void* const* biases, void* const* outs, void* stream);
 
+/* Backward of the forward (fp32 plans with out_ch <= 256; DCN_E_UNSUPPORTED
+ * otherwise): given grad_out = dL/dout in the plan's output layout (fp32),
+ * writes
+ *   grad_x      [B, H, W, C]       dL/dx (NHWC, like x)
+ *   grad_offset [B, 2K, Ho, Wo]    dL/doffset (channel 2k: dy, 2k+1: dx)
+ *   grad_mask   [B, K, Ho, Wo]     dL/dmask (with a NULL mask: at mask = 1)
+ *   grad_weight [O, C, kh, kw]     dL/dweight
+ *   grad_bias   [O]                dL/dbias
+ * Any gradient pointer may be NULL (not computed); every non-NULL one is
+ * fully overwritten.  The gradients are the exact derivative of the forward
+ * (the pages define the forward only): the sample is bilinear inside the
+ * floor cell of the sampling point, so the offset gradient is the derivative
+ * inside that cell with the floor and corner validity held fixed, and
+ * corners outside the image contribute nothing.  The input, offset and mask
+ * gradients are sums over many output pixels and taps accumulated with fp32
+ * atomic adds (page 5 names atomic adds into fp32 accumulators as the way
+ * these gradients are gathered), so they are not bitwise repeatable.
+ * workspace: >= dcn_backward_workspace_bytes (the weight re-packed for the
+ * input-gradient contraction), device, 16-byte aligned.  x, grad_x: 16-byte
+ * aligned; the rest 4-byte aligned.  Asynchronous on `stream`. */
+dcn_status dcn_backward_workspace_bytes(dcn_plan plan, size_t* bytes);
+dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                        const void* weight, const void* grad_out, void* grad_x,
+                        void* grad_offset, void* grad_mask, void* grad_weight, void* grad_bias,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Layout conversion for callers holding NCHW input (page 5's torchvision
  * drop-in takes torchvision's argument order and NCHW layout): writes
  * dst[b, y, x, c] = src[b, c, y, x] for a [batch, channels, height, width]

@@ -189,6 +189,44 @@ class Plan:
             "dcn_forward_rows")
         return out
 
+    def backward_workspace_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        _lib.check(_lib.load().dcn_backward_workspace_bytes(self._h, ctypes.byref(n)),
+                   "dcn_backward_workspace_bytes")
+        return n.value
+
+    def backward(self, x, offset, mask, weight, grad_out, want=("x", "offset", "mask", "weight",
+                                                                 "bias"),
+                 grads=None, workspace=None, stream=None):
+        """``dcn_backward``: returns {name: gradient} for the names in ``want``
+        (x [B,H,W,C], offset, mask [B,K,Ho,Wo], weight, bias [O]; fp32)."""
+        torch = _torch()
+        d = self.desc
+        self._check_inputs(x, offset, mask, None)
+        self._check("weight", weight, (d.out_ch, d.in_ch, d.kernel_h, d.kernel_w))
+        self._check("grad_out", grad_out, self.out_shape(), dtype=torch.float32)
+        shapes = {"x": (d.batch, d.height, d.width, d.in_ch),
+                  "offset": (d.batch, 2 * self.K, self.Ho, self.Wo),
+                  "mask": (d.batch, self.K, self.Ho, self.Wo),
+                  "weight": (d.out_ch, d.in_ch, d.kernel_h, d.kernel_w), "bias": (d.out_ch,)}
+        grads = dict(grads or {})
+        for k in want:
+            if k not in shapes:
+                raise ValueError("unknown gradient %r" % k)
+            if k not in grads:
+                grads[k] = torch.empty(shapes[k], dtype=torch.float32, device="cuda")
+            self._check("grad_" + k, grads[k], shapes[k], dtype=torch.float32)
+        ws = workspace
+        if ws is None:
+            ws = torch.empty(max(self.backward_workspace_bytes(), 16), dtype=torch.uint8,
+                             device="cuda")
+        g = lambda k: _ptr(grads.get(k)) if k in want else None  # noqa: E731
+        _lib.check(_lib.load().dcn_backward(
+            self._h, _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(grad_out),
+            g("x"), g("offset"), g("mask"), g("weight"), g("bias"), _ptr(ws), ws.numel(),
+            ctypes.c_void_p(_stream_handle(stream))), "dcn_backward")
+        return {k: grads[k] for k in want}
+
     def debug_coords(self, offset, stream=None):
         """``dcn_debug_coords``: (y0x0 [B,K,Ho,Wo,2] int32, valid4 [B,K,Ho,Wo] uint8)."""
         torch = _torch()

@@ -23,7 +23,8 @@ DCN_OUT_NCHW, DCN_OUT_NHWC = 0, 1
 # every symbol include/dcn.h declares
 EXPORTS = ("dcn_create", "dcn_destroy", "dcn_output_size", "dcn_workspace_bytes",
            "dcn_pack_weight", "dcn_forward_packed", "dcn_forward", "dcn_forward_rows",
-           "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_debug_coords", "dcn_status_string", "dcn_last_error",
+           "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_backward_workspace_bytes",
+           "dcn_backward", "dcn_debug_coords", "dcn_status_string", "dcn_last_error",
            "dcn_version")
 
 
@@ -64,6 +65,8 @@ def load():
         "dcn_forward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dcn_forward_rows": (st, [vp, i32, i32, vp, vp, vp, vp, sz, vp, vp, vp]),
         "dcn_nchw_to_nhwc": (st, [vp, vp, i32, i32, i32, i32, i32, vp]),
+        "dcn_backward_workspace_bytes": (st, [vp, ctypes.POINTER(sz)]),
+        "dcn_backward": (st, [vp] * 12 + [sz, vp]),
         "dcn_forward_multi": (st, [i32, ctypes.POINTER(vp), vp, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(sz),
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),

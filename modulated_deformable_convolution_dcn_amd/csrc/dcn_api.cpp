@@ -401,6 +401,76 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
   }
 }
 
+dcn_status dcn_backward_workspace_bytes(dcn_plan plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(DCN_E_NULL, "dcn_backward_workspace_bytes: NULL argument");
+  const dcn_desc& d = plan->d;
+  *bytes = (size_t)dcn::bwd_workspace_floats(d.out_ch, d.in_ch, plan->K) * 4;
+  return ok();
+}
+
+dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                        const void* weight, const void* grad_out, void* grad_x,
+                        void* grad_offset, void* grad_mask, void* grad_weight, void* grad_bias,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_backward: plan is NULL");
+    const dcn_desc& d = plan->d;
+    if (d.in_dtype != DCN_F32)
+      return fail(DCN_E_UNSUPPORTED, "dcn_backward: fp32 operands only in this build");
+    if (d.out_ch > 256)
+      return fail(DCN_E_UNSUPPORTED, "dcn_backward: out_ch %d > 256", d.out_ch);
+    size_t need = 0;
+    dcn_backward_workspace_bytes(plan, &need);
+    if (d.batch == 0) return ok();
+    if (!x || !offset || !weight || !grad_out)
+      return fail(DCN_E_NULL, "dcn_backward: x, offset, weight and grad_out are required");
+    if (!workspace || workspace_bytes < need)
+      return fail(DCN_E_WORKSPACE, "dcn_backward: workspace needs %zu bytes, got %zu at %p",
+                  need, workspace_bytes, workspace);
+    if (!aligned(x, 16) || !aligned(workspace, 16) || (grad_x && !aligned(grad_x, 16)))
+      return fail(DCN_E_ALIGN, "dcn_backward: x, grad_x and the workspace must be 16-byte "
+                               "aligned");
+    const void* rest[] = {offset, mask, weight, grad_out, grad_offset, grad_mask, grad_weight,
+                          grad_bias};
+    for (const void* q : rest)
+      if (q && !aligned(q, 4)) return fail(DCN_E_ALIGN, "dcn_backward: misaligned pointer");
+    dcn::BwdArgs a{};
+    a.x = static_cast<const float*>(x);
+    a.offset = static_cast<const float*>(offset);
+    a.mask = static_cast<const float*>(mask);
+    a.gout = static_cast<const float*>(grad_out);
+    a.gx = static_cast<float*>(grad_x);
+    a.goff = static_cast<float*>(grad_offset);
+    a.gmask = static_cast<float*>(grad_mask);
+    a.gw = static_cast<float*>(grad_weight);
+    a.gb = static_cast<float*>(grad_bias);
+    a.B = d.batch;
+    a.C = d.in_ch;
+    a.H = d.height;
+    a.W = d.width;
+    a.O = d.out_ch;
+    a.kh = d.kernel_h;
+    a.kw = d.kernel_w;
+    a.K = plan->K;
+    a.ph = d.pad_h;
+    a.pw = d.pad_w;
+    a.Ho = plan->Ho;
+    a.Wo = plan->Wo;
+    a.HoWo = plan->Ho * plan->Wo;
+    a.nchunk = (int)ceil_div(d.in_ch, 64);
+    a.tiles_per_img = (int)ceil_div(a.HoWo, 64);
+    a.nhwc_g = d.out_layout == DCN_OUT_NHWC;
+    a.x_bytes = plan->x_bytes;
+    hipError_t e = dcn::launch_backward(a, static_cast<const float*>(weight),
+                                        static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_backward: unexpected exception");
+  }
+}
+
 dcn_status dcn_nchw_to_nhwc(const void* src, void* dst, int32_t batch, int32_t channels,
                             int32_t height, int32_t width, int32_t dtype, void* stream) {
   try {

@@ -38,6 +38,31 @@ struct FusedArgs {
   int vec_store;       // NCHW: Ho*Wo % 4 == 0, so 4 consecutive pixels store as one 16-B write
 };
 
+// Arguments of the fp32 backward kernels (dcn_backward.hip).
+struct BwdArgs {
+  const float* x;       // [B,H,W,C]
+  const float* offset;  // [B,2K,Ho,Wo]
+  const float* mask;    // [B,K,Ho,Wo] or nullptr (ones)
+  const float* gout;    // dL/dout, [B,O,Ho,Wo] or [B,Ho,Wo,O] (nhwc_g)
+  const float* wt;      // weight re-packed for the data gradient (workspace)
+  float* gx;            // [B,H,W,C]    or nullptr: not wanted
+  float* goff;          // [B,2K,Ho,Wo] or nullptr
+  float* gmask;         // [B,K,Ho,Wo]  or nullptr
+  float* gw;            // [O,C,kh,kw]  or nullptr
+  float* gb;            // [O]          or nullptr
+  int B, C, H, W, O, kh, kw, K, ph, pw, Ho, Wo, HoWo;
+  int nchunk;           // ceil(C / 64)
+  int tiles_per_img;    // ceil(Ho*Wo / 64)
+  int nhwc_g;
+  uint32_t x_bytes;
+};
+
+// Floats of workspace the backward needs; the launch zero-fills the
+// gradients it writes, re-packs the weight and runs the three kernels.
+int64_t bwd_workspace_floats(int O, int C, int K);
+hipError_t launch_backward(const BwdArgs& a, const float* weight, float* workspace,
+                           hipStream_t stream);
+
 // Several branches (same input map, own offsets/mask/weight/bias/output and
 // kernel size) in one launch: branch i owns the logical workgroups
 // [start[i], start[i+1]).

@@ -210,3 +210,31 @@ def test_multi_branch_checks_fire_before_any_launch():
     assert call([a, b], ws=short) == 8                   # branch 1's workspace too small
     assert call([a, b], x=0) == 1                        # shared input missing
     assert lib.dcn_forward_multi(1, None, V(fake), None, None, None, None, None, None, None) == 1
+
+
+def test_backward_checks_fire_before_any_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x10000)
+    V = ctypes.c_void_p
+    p = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1))
+    n = ctypes.c_size_t()
+    assert lib.dcn_backward_workspace_bytes(p._h, ctypes.byref(n)) == 0
+    assert n.value == 9 * 1 * 64 * 64 * 4       # taps x chunks x 64 outputs x 64 channels
+    ws = n.value
+    args = lambda **kw: [kw.get(k, fake) for k in (  # noqa: E731
+        "x", "off", "mask", "w", "g", "gx", "goff", "gmask", "gw", "gb")]
+    call = lambda plan=p, wsp=fake, wsn=ws, **kw: lib.dcn_backward(  # noqa: E731
+        plan._h, *args(**kw), wsp, wsn, None)
+    assert call(x=None) == 1
+    assert call(g=None) == 1
+    assert call(wsp=None) == 8
+    assert call(wsn=ws - 1) == 8
+    assert call(x=V(0x10004)) == 5
+    assert call(gw=V(0x10002)) == 5
+    bf = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1, "bf16"))
+    assert call(plan=bf) == 4
+    wide = Plan(Desc(1, 64, 16, 16, 300, 3, 3, 1, 1))
+    assert call(plan=wide) == 4
+    assert "256" in lib.dcn_last_error().decode()
+    empty = Plan(Desc(0, 64, 16, 16, 64, 3, 3, 1, 1))
+    assert lib.dcn_backward(empty._h, *[None] * 10, None, 0, None) == 0
