@@ -15,11 +15,13 @@
 // adds into fp32 accumulators; the input gradient here is exactly that.
 //
 // Three kernels after zero-filling the outputs:
-//   bwd_data   one workgroup per 64 output pixels: the g tile stays in LDS,
-//              per (tap, 64-channel chunk) gs comes from MFMA against the
-//              re-packed weight, then each thread takes one pixel's 4-channel
-//              slice: corner loads, input-gradient atomics, and the
-//              mask / offset sums reduced over the 16 lanes of the pixel;
+//   bwd_data   one workgroup per 8 x 8 block of output pixels: the g tile
+//              stays in LDS, per (tap, 64-channel chunk) gs comes from MFMA
+//              against the re-packed weight, then each thread takes one
+//              pixel's 4-channel slice: corner loads, input-gradient adds
+//              (into an LDS window around the block, flushed once per chunk;
+//              far corners straight to memory), and the mask / offset sums
+//              reduced over the 16 lanes of the pixel;
 //   bwd_weight one workgroup per (tap, chunk, image, run of pixel tiles):
 //              the modulated column tile and the g tile go to LDS transposed
 //              and MFMA accumulates dW[c, o] over the run, then one atomic
@@ -44,6 +46,7 @@ __device__ __forceinline__ void atomic_add(float* p, float v) { unsafeAtomicAdd(
 struct TapTerms {
   float w[4], dwy[4], dwx[4];
   int pix[4];
+  int y0, x0;  // corner (0, 0), clamped to [-1, H] x [-1, W]
   bool ok[4];
 };
 
@@ -59,6 +62,8 @@ __device__ __forceinline__ TapTerms tap_terms(const BwdArgs& a, int b, int ho, i
   const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
   const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
   TapTerms r;
+  r.y0 = y0;
+  r.x0 = x0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     r.ok[q] = (t.valid >> q) & 1u;
@@ -78,103 +83,151 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 }  // namespace
 
 // ---------------------------------------------------------------- data grads
+// LDS budget of the input-gradient window, per padded output count.
+constexpr int bwd_window_floats(int OP) {
+  return OP <= 16 ? 32768 : OP <= 64 ? 29696 : OP <= 128 ? 25600 : 16896;
+}
+constexpr int WSTR = 68;  // floats per window position: 64 channels + 4 (bank spread)
+
+// One workgroup = an 8 x 8 block of output pixels of one image.  Its
+// sampling points cluster around the block, so the input gradient of the
+// window [wy0, wy0 + WH) x [wx0, wx0 + WW) (the block's footprint grown by R
+// on every side) is accumulated in LDS with LDS atomics and flushed to
+// memory once per 64-channel chunk; corners outside the window (far
+// offsets) go straight to memory.  R < 0: no window.
 template <int OP>  // padded output channels: 16, 64, 128 or 256
-__global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int tiles_x,
+                                                       int tiles_per_img) {
   constexpr int GST = OP + GPAD;     // g tile row stride
   constexpr int SST = 64 + GPAD;     // gs tile row stride
   __shared__ __attribute__((aligned(16))) float Gs[TILE * GST];
   __shared__ __attribute__((aligned(16))) float gsT[TILE * SST];
+  __shared__ __attribute__((aligned(16))) float win[bwd_window_floats(OP)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int tile = logical % a.tiles_per_img, b = logical / a.tiles_per_img;
-  const int hw0 = tile * TILE;
+  const int tile = logical % tiles_per_img, b = logical / tiles_per_img;
+  const int ty = tile / tiles_x, tx = tile - (tile / tiles_x) * tiles_x;
+  const bool use_win = R >= 0;
+  const int WH = 8 + a.kh + 2 * R, WW = 8 + a.kw + 2 * R;
+  const int wy0 = 8 * ty - a.ph - R, wx0 = 8 * tx - a.pw - R;
+  // pixel px of the block -> output (8ty + px / 8, 8tx + px % 8)
+  auto px_hw = [&](int px, int& hw) {
+    const int ho = 8 * ty + (px >> 3), wo = 8 * tx + (px & 7);
+    hw = ho * a.Wo + wo;
+    return ho < a.Ho && wo < a.Wo;
+  };
 
   // g tile [64 pixels][OP outputs], zero outside
   for (int e = tid; e < TILE * OP; e += 256) {
     const int o = e / TILE, px = e % TILE;
-    const int hw = hw0 + px;
-    Gs[px * GST + o] = (o < a.O && hw < a.HoWo) ? gout_at(a, b, o, hw) : 0.0f;
+    int hw;
+    const bool in = px_hw(px, hw);
+    Gs[px * GST + o] = (o < a.O && in) ? gout_at(a, b, o, hw) : 0.0f;
   }
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const int rl = lane & 15, g = lane >> 4;
   const int sl = tid & 15;  // 4-channel slice of the 64-channel chunk
-  for (int kb = 0; kb < a.K * a.nchunk; ++kb) {
-    const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
-    __syncthreads();  // g tile written / previous block's gs tile consumed
-    // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows 16w..
-    f32x4 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* wt = a.wt + (size_t)kb * OP * 64;
-#pragma unroll 4
-    for (int q = 0; q < OP / 16; ++q) {
-      const f32x4 af = *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + rl) * GST + 16 * q + 4 * g]);
-      f32x4 bf[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bf[nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[nt][e], acc[nt], 0, 0, 0);
-    }
-    // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r, column l % 16
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gsT[(16 * wave + 4 * g + r) * SST + 16 * nt + rl] = acc[nt][r];
-    __syncthreads();
-
-    // (2) per (pixel, 4-channel slice): corners, input-gradient atomics,
-    // mask / offset sums
+  const int nwin = use_win ? WH * WW : 0;
+  for (int chunk = 0; chunk < a.nchunk; ++chunk) {
+    for (int e = tid; e < nwin * WSTR; e += 256) win[e] = 0.0f;
     const int ch = chunk * 64 + 4 * sl;
     const bool chan_ok = ch < a.C;
+    for (int k = 0; k < a.K; ++k) {
+      const int kb = k * a.nchunk + chunk;
+      __syncthreads();  // g tile / window zeroed; previous gs tile consumed
+      // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows 16w..
+      f32x4 acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* wt = a.wt + (size_t)kb * OP * 64;
+#pragma unroll 4
+      for (int q = 0; q < OP / 16; ++q) {
+        const f32x4 af =
+            *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + rl) * GST + 16 * q + 4 * g]);
+        f32x4 bf[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          bf[nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[nt][e], acc[nt], 0, 0, 0);
+      }
+      // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r, column l % 16
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gsT[(16 * wave + 4 * g + r) * SST + 16 * nt + rl] = acc[nt][r];
+      __syncthreads();
+
+      // (2) per (pixel, 4-channel slice): corners, input-gradient adds,
+      // mask / offset sums
 #pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-      const int px = 16 * p + (tid >> 4);
-      const int hw = hw0 + px;
-      float sm = 0.f, sdy = 0.f, sdx = 0.f, m = 0.f;
-      if (hw < a.HoWo) {
-        const int ho = hw / a.Wo, wo = hw - (hw / a.Wo) * a.Wo;
-        const TapTerms t = tap_terms(a, b, ho, wo, k);
-        m = a.mask ? a.mask[((size_t)(b * a.K + k)) * a.HoWo + hw] : 1.0f;
-        const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
-        if (chan_ok) {
+      for (int p = 0; p < 4; ++p) {
+        const int px = 16 * p + (tid >> 4);
+        int hw;
+        const bool in = px_hw(px, hw);
+        float sm = 0.f, sdy = 0.f, sdx = 0.f, m = 0.f;
+        if (in) {
+          const TapTerms t = tap_terms(a, b, hw / a.Wo, hw - (hw / a.Wo) * a.Wo, k);
+          m = a.mask ? a.mask[((size_t)(b * a.K + k)) * a.HoWo + hw] : 1.0f;
+          const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
+          if (chan_ok) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (!t.ok[q]) continue;
-            const uint32_t off = ((uint32_t)t.pix[q] * (uint32_t)a.C + (uint32_t)ch) * 4u;
-            const f32x4 v = __builtin_bit_cast(f32x4, load16(xr, off));
-            float* dst = a.gx + (size_t)t.pix[q] * a.C + ch;
-            const float cw = m * t.w[q];
+            for (int q = 0; q < 4; ++q) {
+              if (!t.ok[q]) continue;
+              const uint32_t off = ((uint32_t)t.pix[q] * (uint32_t)a.C + (uint32_t)ch) * 4u;
+              const f32x4 v = __builtin_bit_cast(f32x4, load16(xr, off));
+              const float cw = m * t.w[q];
+              const int wy = t.y0 + (q >> 1) - wy0, wx = t.x0 + (q & 1) - wx0;
+              if (use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW) {
+                float* dst = &win[(wy * WW + wx) * WSTR + 4 * sl];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              atomic_add(dst + e, gs[e] * cw);
-              sm = __builtin_fmaf(gs[e] * t.w[q], v[e], sm);
-              sdy = __builtin_fmaf(gs[e] * t.dwy[q], v[e], sdy);
-              sdx = __builtin_fmaf(gs[e] * t.dwx[q], v[e], sdx);
+                for (int e = 0; e < 4; ++e) atomicAdd(dst + e, gs[e] * cw);
+              } else {
+                float* dst = a.gx + (size_t)t.pix[q] * a.C + ch;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) atomic_add(dst + e, gs[e] * cw);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                sm = __builtin_fmaf(gs[e] * t.w[q], v[e], sm);
+                sdy = __builtin_fmaf(gs[e] * t.dwy[q], v[e], sdy);
+                sdx = __builtin_fmaf(gs[e] * t.dwx[q], v[e], sdx);
+              }
             }
           }
         }
-      }
-      // sum over the 16 lanes of the pixel (lanes 16*(l/16) .. +15)
+        // sum over the 16 lanes of the pixel (lanes 16*(l/16) .. +15)
 #pragma unroll
-      for (int sh = 8; sh >= 1; sh >>= 1) {
-        sm += __shfl_xor(sm, sh, 16);
-        sdy += __shfl_xor(sdy, sh, 16);
-        sdx += __shfl_xor(sdx, sh, 16);
-      }
-      if (sl == 0 && hw < a.HoWo) {
-        if (a.gmask) atomic_add(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, sm);
-        if (a.goff) {
-          atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, m * sdy);
-          atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, m * sdx);
+        for (int sh = 8; sh >= 1; sh >>= 1) {
+          sm += __shfl_xor(sm, sh, 16);
+          sdy += __shfl_xor(sdy, sh, 16);
+          sdx += __shfl_xor(sdx, sh, 16);
+        }
+        if (sl == 0 && in) {
+          if (a.gmask) atomic_add(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, sm);
+          if (a.goff) {
+            atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, m * sdy);
+            atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, m * sdx);
+          }
         }
       }
     }
+    // (3) flush the window's input gradient of this chunk
+    __syncthreads();
+    for (int e = tid; e < nwin * 64; e += 256) {
+      const int pos = e >> 6, c = e & 63;
+      const int y = wy0 + pos / WW, xx = wx0 + pos % WW;
+      const float v = win[pos * WSTR + c];
+      if (v != 0.0f && y >= 0 && y < a.H && xx >= 0 && xx < a.W && chunk * 64 + c < a.C)
+        atomic_add(a.gx + ((size_t)(b * a.H + y) * a.W + xx) * a.C + chunk * 64 + c, v);
+    }
+    __syncthreads();  // flush done before the next chunk zeroes the window
   }
 }
 
@@ -337,15 +390,24 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
                      weight, ws, a.O, a.C, a.K, OP, a.nchunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.wt = ws;
-  const int64_t nblk = (int64_t)a.B * a.tiles_per_img;
-  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.gx || a.goff || a.gmask) {
+    // 8 x 8 output blocks; window radius R: the largest that fits the LDS
+    // budget (-1: none)
+    const int tiles_x = (a.Wo + 7) / 8, tiles_y = (a.Ho + 7) / 8;
+    const int tiles = tiles_x * tiles_y;
+    const int64_t nblk = (int64_t)a.B * tiles;
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int budget = OP <= 16 ? bwd_window_floats(16) : OP <= 64 ? bwd_window_floats(64)
+                       : OP <= 128 ? bwd_window_floats(128) : bwd_window_floats(256);
+    int R = -1;
+    for (int r = 0; r <= 8; ++r)
+      if ((int64_t)(8 + a.kh + 2 * r) * (8 + a.kw + 2 * r) * WSTR <= budget) R = r;
     const dim3 grid((unsigned)nblk), block(256);
     switch (OP) {
-      case 16: hipLaunchKernelGGL(bwd_data_kernel<16>, grid, block, 0, s, a); break;
-      case 64: hipLaunchKernelGGL(bwd_data_kernel<64>, grid, block, 0, s, a); break;
-      case 128: hipLaunchKernelGGL(bwd_data_kernel<128>, grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL(bwd_data_kernel<256>, grid, block, 0, s, a); break;
+      case 16: hipLaunchKernelGGL(bwd_data_kernel<16>, grid, block, 0, s, a, R, tiles_x, tiles); break;
+      case 64: hipLaunchKernelGGL(bwd_data_kernel<64>, grid, block, 0, s, a, R, tiles_x, tiles); break;
+      case 128: hipLaunchKernelGGL(bwd_data_kernel<128>, grid, block, 0, s, a, R, tiles_x, tiles); break;
+      default: hipLaunchKernelGGL(bwd_data_kernel<256>, grid, block, 0, s, a, R, tiles_x, tiles); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
