@@ -103,6 +103,10 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
   __shared__ __attribute__((aligned(16))) float Gs[TILE * GST];
   __shared__ __attribute__((aligned(16))) float gsT[TILE * SST];
   __shared__ __attribute__((aligned(16))) float win[bwd_window_floats(OP)];
+  // per-tap table of the block's 64 sampling points (written by wave 0):
+  // {y0, x0, validity bits, pixel inside the output} and {ly, lx, mask}
+  __shared__ int4 Ti[TILE];
+  __shared__ f32x4 Tf[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -130,13 +134,35 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
   const int rl = lane & 15, g = lane >> 4;
   const int sl = tid & 15;  // 4-channel slice of the 64-channel chunk
   const int nwin = use_win ? WH * WW : 0;
+  // wave 0: the offsets / mask of the next tap, loaded one tap ahead
+  int t_hw = 0;
+  const bool t_in = tid < TILE && px_hw(tid, t_hw);
+  float n_dy = 0.f, n_dx = 0.f, n_m = 1.f;
+  auto t_load = [&](int k) {
+    if (!t_in) return;
+    const size_t ob = (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + t_hw;
+    n_dy = a.offset[ob];
+    n_dx = a.offset[ob + a.HoWo];
+    n_m = a.mask ? a.mask[(size_t)(b * a.K + k) * a.HoWo + t_hw] : 1.0f;
+  };
+  if (tid < TILE) t_load(0);
   for (int chunk = 0; chunk < a.nchunk; ++chunk) {
     for (int e = tid; e < nwin * WSTR; e += 256) win[e] = 0.0f;
     const int ch = chunk * 64 + 4 * sl;
     const bool chan_ok = ch < a.C;
     for (int k = 0; k < a.K; ++k) {
       const int kb = k * a.nchunk + chunk;
-      __syncthreads();  // g tile / window zeroed; previous gs tile consumed
+      __syncthreads();  // g tile / window zeroed; previous gs tile and table consumed
+      if (tid < TILE) {  // (0) the table of tap k, then the loads of the next tap
+        const int ho = t_hw / a.Wo, wo = t_hw - (t_hw / a.Wo) * a.Wo;
+        const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+        const TapPoint tp = tap_point(n_dy, n_dx, ho - a.ph + i, wo - a.pw + j, a.H, a.W);
+        Ti[tid] = make_int4((int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H),
+                            (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W), (int)tp.valid,
+                            t_in ? 1 : 0);
+        Tf[tid] = f32x4{tp.ly, tp.lx, n_m, 0.0f};
+        t_load(k + 1 < a.K ? k + 1 : 0);
+      }
       // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows 16w..
       f32x4 acc[4];
 #pragma unroll
@@ -173,8 +199,26 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
         const bool in = px_hw(px, hw);
         float sm = 0.f, sdy = 0.f, sdx = 0.f, m = 0.f;
         if (in) {
-          const TapTerms t = tap_terms(a, b, hw / a.Wo, hw - (hw / a.Wo) * a.Wo, k);
-          m = a.mask ? a.mask[((size_t)(b * a.K + k)) * a.HoWo + hw] : 1.0f;
+          const int4 ti = Ti[px];
+          const f32x4 tf = Tf[px];
+          TapTerms t;
+          {
+            const float ly = tf[0], lx = tf[1], hy = 1.0f - ly, hx = 1.0f - lx;
+            const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
+            const float vy[4] = {-hx, -lx, hx, lx};
+            const float vx[4] = {-hy, hy, -ly, ly};
+            t.y0 = ti.x;
+            t.x0 = ti.y;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              t.ok[q] = (ti.z >> q) & 1;
+              t.w[q] = t.ok[q] ? wv[q] : 0.0f;
+              t.dwy[q] = t.ok[q] ? vy[q] : 0.0f;
+              t.dwx[q] = t.ok[q] ? vx[q] : 0.0f;
+              t.pix[q] = (b * a.H + ti.x + (q >> 1)) * a.W + ti.y + (q & 1);
+            }
+          }
+          m = tf[2];
           const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
           if (chan_ok) {
 #pragma unroll
