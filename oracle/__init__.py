@@ -60,6 +60,9 @@ def _load():
         lib.dcn_oracle_coords.restype = ctypes.c_int
         lib.dcn_oracle_backward.argtypes = [ctypes.POINTER(_Shape)] + [vp] * 15 + [ctypes.c_int]
         lib.dcn_oracle_backward.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.dcn_oracle_msda.argtypes = [i64] * 7 + [vp] * 4 + [ctypes.c_int, vp, vp, ctypes.c_int]
+        lib.dcn_oracle_msda.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -189,3 +192,26 @@ def backward(shape: Shape, x, offset, mask, weight, grad_out, nthreads: int = 0)
     if rc != 0:
         raise ValueError("dcn_oracle_backward failed with code %d" % rc)
     return g, n
+
+
+def msda(value, shapes, locations, weights, softmax: bool, nthreads: int = 0):
+    """Oracle multi-scale deformable attention sampling (see dcn_oracle.h).
+
+    value (B, S, G, D), shapes [(H, W), ...], locations (B, Q, G, L, K, 2)
+    with component 0 = x (column), 1 = y (row), weights (B, Q, G, L*K).
+    Returns ``(out, norm)``, float64 (B, Q, G, D).
+    """
+    value, locations, weights = (_f32(a) for a in (value, locations, weights))
+    B, S, G, D = value.shape
+    _, Q, _, L, K, _ = locations.shape
+    assert locations.shape == (B, Q, G, L, K, 2), locations.shape
+    assert weights.shape == (B, Q, G, L * K), weights.shape
+    sh = np.ascontiguousarray(np.asarray(shapes, dtype=np.int64).reshape(L, 2))
+    out = np.empty((B, Q, G, D), dtype=np.float64)
+    norm = np.empty((B, Q, G, D), dtype=np.float64)
+    rc = _load().dcn_oracle_msda(B, S, G, D, Q, L, K, _ptr(sh), _ptr(value), _ptr(locations),
+                                 _ptr(weights), int(bool(softmax)), _ptr(out), _ptr(norm),
+                                 int(nthreads))
+    if rc != 0:
+        raise ValueError("dcn_oracle_msda failed with code %d" % rc)
+    return out, norm

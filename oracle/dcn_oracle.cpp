@@ -375,3 +375,85 @@ extern "C" int dcn_oracle_backward(const dcn_oracle_shape* s, const float* x,
   reduce(ngb, &BwdAcc::ngb, d.O);
   return 0;
 }
+
+// ---------------------------------------------------------------- MSDA
+// Page 5, "Multi-scale deformable attention": sample each level's value map
+// bilinearly at the normalised location and sum with the attention weights.
+// The pixel coordinate of a normalised location follows the half-pixel
+// convention (pixel centres at (i + 0.5) / size), each step rounded to fp32.
+extern "C" int dcn_oracle_msda(int64_t B, int64_t S, int64_t G, int64_t D, int64_t Q,
+                               int64_t L, int64_t K, const int64_t* shapes, const float* value,
+                               const float* locations, const float* weights, int softmax,
+                               double* out, double* norm, int nthreads) {
+  if (!shapes || !value || !locations || !weights || !out) return 1;
+  if (B < 0 || S <= 0 || G <= 0 || D <= 0 || Q < 0 || L <= 0 || K <= 0) return 2;
+  std::vector<int64_t> start(static_cast<size_t>(L));
+  int64_t total = 0;
+  for (int64_t l = 0; l < L; ++l) {
+    if (shapes[2 * l] <= 0 || shapes[2 * l + 1] <= 0) return 2;
+    start[l] = total;
+    total += shapes[2 * l] * shapes[2 * l + 1];
+  }
+  if (total != S) return 2;
+  const int64_t pairs = B * Q * G;
+  const int nt = resolve_threads(nthreads, pairs);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t) {
+    pool.emplace_back([&, t]() {
+      std::vector<double> a(static_cast<size_t>(L * K));
+      for (int64_t n = t; n < pairs; n += nt) {
+        const int64_t g = n % G, bq = n / G, b = bq / Q;
+        const float* wrow = &weights[n * L * K];  // (b, q, g) row of (B, Q, G, L*K)
+        if (softmax) {
+          double mx = -INFINITY, sum = 0.0;
+          for (int64_t e = 0; e < L * K; ++e) mx = std::fmax(mx, (double)wrow[e]);
+          for (int64_t e = 0; e < L * K; ++e) sum += std::exp((double)wrow[e] - mx);
+          for (int64_t e = 0; e < L * K; ++e) a[e] = std::exp((double)wrow[e] - mx) / sum;
+        } else {
+          for (int64_t e = 0; e < L * K; ++e) a[e] = wrow[e];
+        }
+        double* orow = &out[n * D];
+        double* nrow = norm ? &norm[n * D] : nullptr;
+        for (int64_t c = 0; c < D; ++c) {
+          orow[c] = 0.0;
+          if (nrow) nrow[c] = 0.0;
+        }
+        for (int64_t l = 0; l < L; ++l) {
+          const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
+          for (int64_t k = 0; k < K; ++k) {
+            const float* loc = &locations[((n * L + l) * K + k) * 2];
+            volatile float sx = loc[0] * static_cast<float>(W);
+            volatile float sy = loc[1] * static_cast<float>(H);
+            volatile float px = sx - 0.5f;
+            volatile float py = sy - 0.5f;
+            const float x0 = std::floor(static_cast<float>(px));
+            const float y0 = std::floor(static_cast<float>(py));
+            volatile float fx = px - x0;
+            volatile float fy = py - y0;
+            const double lx = static_cast<float>(fx), ly = static_cast<float>(fy);
+            const double wgt[2][2] = {{(1.0 - ly) * (1.0 - lx), (1.0 - ly) * lx},
+                                      {ly * (1.0 - lx), ly * lx}};
+            const double ak = a[l * K + k];
+            for (int ca = 0; ca < 2; ++ca)
+              for (int cb = 0; cb < 2; ++cb) {
+                volatile float yy = y0 + static_cast<float>(ca);
+                volatile float xx = x0 + static_cast<float>(cb);
+                if (!(yy >= 0.0f && yy <= static_cast<float>(H - 1) && xx >= 0.0f &&
+                      xx <= static_cast<float>(W - 1)))
+                  continue;  // outside the level counts as zero
+                const int64_t pix = start[l] + static_cast<int64_t>(yy) * W +
+                                    static_cast<int64_t>(xx);
+                const float* v = &value[((b * S + pix) * G + g) * D];
+                for (int64_t c = 0; c < D; ++c) {
+                  orow[c] += ak * wgt[ca][cb] * static_cast<double>(v[c]);
+                  if (nrow) nrow[c] += std::fabs(ak) * wgt[ca][cb] * std::fabs((double)v[c]);
+                }
+              }
+          }
+        }
+      }
+    });
+  }
+  for (auto& th : pool) th.join();
+  return 0;
+}

@@ -97,6 +97,25 @@ int dcn_oracle_backward(const dcn_oracle_shape* s, const float* x, const float* 
                         double* ngx, double* ngoff, double* ngmask, double* ngw, double* ngb,
                         int nthreads);
 
+/*
+ * Multi-scale deformable attention sampling (page 5, deformops README,
+ * "Multi-scale deformable attention": value (B, sum H*W, G, D), per-level
+ * shapes and start offsets, locations (B, Q, G, L, K, 2) normalised to
+ * [0, 1], weights (B, Q, G, L*K) used as given or normalised by a softmax
+ * over levels and points).  For each (b, q, g):
+ *   out[b, q, g, :] = sum_{l, k} a[l, k] * bilinear(value level l, head g, at p)
+ * with p = (x * W_l - 0.5, y * H_l - 0.5) in pixels (location component 0 is
+ * x, the column; 1 is y, the row), each product and difference rounded to
+ * fp32 (no fused multiply-add); corners outside the level count as zero.
+ *   shapes  [L][2] (H_l, W_l); starts[l] = sum_{m < l} H_m W_m
+ *   out     [B, Q, G, D] fp64; norm (may be NULL) the absolute-term sum
+ *           sum a * w_corner * |value| with |a|.
+ * softmax != 0: a = softmax over the L*K logits of (b, q, g) (fp64).
+ */
+int dcn_oracle_msda(int64_t B, int64_t S, int64_t G, int64_t D, int64_t Q, int64_t L, int64_t K,
+                    const int64_t* shapes, const float* value, const float* locations,
+                    const float* weights, int softmax, double* out, double* norm, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
