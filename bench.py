@@ -105,6 +105,51 @@ def summarize_traffic(pmc_dir: str, workload: str, copy_mib: int) -> dict:
     }
 
 
+def bench_msda(args, torch, synth) -> int:
+    """Multi-scale deformable attention sampling: one launch per step."""
+    from modulated_deformable_convolution_dcn_amd import MsdaPlan
+    spec = synth.MSDA_WORKLOADS[args.msda]
+    d = synth.make_msda_inputs(spec)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
+    plan = MsdaPlan(spec.B, spec.Q, spec.G, spec.D, spec.shapes, spec.K, spec.softmax)
+    out = torch.empty((spec.B, spec.Q, spec.G * spec.D), device="cuda")
+    for _ in range(args.warmup):
+        plan.forward(dev["value"], dev["locations"], dev["weights"], out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        plan.forward(dev["value"], dev["locations"], dev["weights"], out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ks = [e[0].elapsed_time(e[1]) for e in ev]
+    kern_ms = sum(ks) / len(ks)
+    ms = elapsed * 1e3 / args.steps
+    pairs = spec.B * spec.Q * spec.G
+    points = pairs * spec.L * spec.K
+    # compulsory bytes: value read once, locations, weights, output
+    compulsory = 4 * (spec.B * spec.S * spec.G * spec.D + points * 2 + points + pairs * spec.D)
+    gathered = points * 4 * spec.D * 4  # four corner vectors per point
+    hbm = compulsory / (kern_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "msda sampling points/s", "value": points / (ms * 1e-3), "unit": "points/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "Q": spec.Q, "G": spec.G, "D": spec.D,
+                   "levels": [list(x) for x in spec.shapes], "K": spec.K,
+                   "softmax": spec.softmax},
+        "roofline": {"bound": "hbm", "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm / HBM_PEAK_GBS, "traffic": None},
+        "gather_gbs": gathered / (kern_ms * 1e-3) / 1e9,
+        "kernels_us": {"msda": kern_ms * 1e3},
+        "fused_us_percentiles": {k: v * 1e3 for k, v in percentiles(ks).items()},
+    }), flush=True)
+    return 0
+
+
 def percentiles(xs):
     ys = sorted(xs)
     pick = lambda f: ys[min(len(ys) - 1, int(round(f * (len(ys) - 1))))]
@@ -168,6 +213,9 @@ def main() -> int:
                     help="with --branches: one forward call per branch instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the fp32 backward (all five gradients) instead of the forward")
+    ap.add_argument("--msda", metavar="WORKLOAD", default=None,
+                    help="time multi-scale deformable attention sampling on this workload "
+                         "(msda_encoder_fp32, msda_decoder_fp32) instead")
     ap.add_argument("--bands", type=int, default=1,
                     help="run the forward as this many output-row bands (row0 calls), "
                          "back to back on one stream")
@@ -202,6 +250,8 @@ def main() -> int:
         return 0
 
     from modulated_deformable_convolution_dcn_amd import Desc, Plan, synth
+    if args.msda:
+        return bench_msda(args, torch, synth)
 
     spec = synth.WORKLOADS[args.workload]
     d = synth.make_inputs(spec)

@@ -191,6 +191,43 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
                         void* grad_offset, void* grad_mask, void* grad_weight, void* grad_bias,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Multi-scale deformable attention sampling (page 5, deformops README,
+ * "Multi-scale deformable attention"; the second operator on the same
+ * gather machinery).  Shapes: B batch, G heads, D channels per head, Q
+ * queries, L levels of sizes H_l x W_l, K points per level, S = sum H_l W_l.
+ *   value     [B, S, G, D]       the L feature maps, flattened row-major and
+ *                                concatenated (level l starts at
+ *                                sum_{m<l} H_m W_m)
+ *   locations [B, Q, G, L, K, 2] normalised (x, y): component 0 is the
+ *                                column, 1 the row, (0, 0) the top-left edge
+ *   weights   [B, Q, G, L*K]     attention weights, or logits when
+ *                                desc.softmax != 0 (then normalised over the
+ *                                L*K points of each (b, q, g) in the kernel)
+ *   out       [B, Q, G, D]       = [B, Q, G*D]
+ *   out[b,q,g,:] = sum_{l,k} a * bilinear(level l, head g, at
+ *                  (x * W_l - 0.5, y * H_l - 0.5) pixels)
+ * with each product / difference of the pixel coordinate rounded to fp32
+ * and corners outside the level counting as zero.  fp32 only; L <= 8,
+ * K <= 8, D a multiple of 4 (<= 1024).  level_hw is a HOST array [L][2] of
+ * (H_l, W_l) copied into the plan.  The value buffer must hold exactly S
+ * positions (dcn_msda_value_positions).
+ */
+typedef struct dcn_msda_plan_s* dcn_msda_plan;
+typedef struct {
+  int32_t batch, num_queries, num_heads, head_dim, num_levels, num_points;
+  int32_t dtype;    /* DCN_F32 */
+  int32_t softmax;  /* 0: weights as given; 1: softmax of logits */
+} dcn_msda_desc;
+dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
+                           dcn_msda_plan* plan);
+dcn_status dcn_msda_destroy(dcn_msda_plan plan);
+dcn_status dcn_msda_value_positions(dcn_msda_plan plan, int32_t* positions);
+/* One kernel launch on `stream`; value and out 16-byte aligned, locations
+ * 8-byte, weights 4-byte; no input may overlap out. */
+dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* locations,
+                            const void* weights, void* out, void* stream);
+
 /* Layout conversion for callers holding NCHW input (page 5's torchvision
  * drop-in takes torchvision's argument order and NCHW layout): writes
  * dst[b, y, x, c] = src[b, c, y, x] for a [batch, channels, height, width]

@@ -19,8 +19,8 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import DcnError  # noqa: F401
 
-__all__ = ["Plan", "deform_conv2d", "deform_conv2d_nhwc", "forward_multi", "nchw_to_nhwc",
-           "DcnError"]
+__all__ = ["Plan", "MsdaPlan", "deform_conv2d", "deform_conv2d_nhwc", "forward_multi", "msda",
+           "nchw_to_nhwc", "DcnError"]
 
 _DTYPES = {"f32": _lib.DCN_F32, "bf16": _lib.DCN_BF16}
 _LAYOUTS = {"nchw": _lib.DCN_OUT_NCHW, "nhwc": _lib.DCN_OUT_NHWC}
@@ -323,3 +323,75 @@ def forward_multi(plans, x, offsets, masks, packeds, biases=None, outs=None, str
         n, handles, _ptr(x), arr(offsets), arr(masks), arr(packeds), sizes, arr(biases),
         arr(outs), ctypes.c_void_p(_stream_handle(stream))), "dcn_forward_multi")
     return outs
+
+
+class MsdaPlan:
+    """``dcn_msda_create``: multi-scale deformable attention sampling of one size."""
+
+    def __init__(self, batch, num_queries, num_heads, head_dim, shapes, num_points,
+                 softmax=False):
+        lib = _lib.load()
+        shapes = [(int(h), int(w)) for h, w in shapes]
+        self.shapes = shapes
+        self.B, self.Q, self.G, self.D = batch, num_queries, num_heads, head_dim
+        self.L, self.K = len(shapes), num_points
+        self.softmax = bool(softmax)
+        d = _lib.MsdaDesc(batch, num_queries, num_heads, head_dim, len(shapes), num_points,
+                          _lib.DCN_F32, int(bool(softmax)))
+        hw = (ctypes.c_int32 * (2 * len(shapes)))(*[v for s in shapes for v in s])
+        h = ctypes.c_void_p()
+        _lib.check(lib.dcn_msda_create(ctypes.byref(d), hw, ctypes.byref(h)), "dcn_msda_create")
+        self._h = h
+        n = ctypes.c_int32()
+        _lib.check(lib.dcn_msda_value_positions(h, ctypes.byref(n)), "dcn_msda_value_positions")
+        self.S = n.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.load().dcn_msda_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    def forward(self, value, locations, weights, out=None, stream=None):
+        """value [B,S,G,D], locations [B,Q,G,L,K,2], weights [B,Q,G,L*K] (fp32 device
+        tensors) -> out [B,Q,G*D] fp32."""
+        torch = _torch()
+        shapes = {"value": (self.B, self.S, self.G, self.D),
+                  "locations": (self.B, self.Q, self.G, self.L, self.K, 2),
+                  "weights": (self.B, self.Q, self.G, self.L * self.K)}
+        for name, t in (("value", value), ("locations", locations), ("weights", weights)):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+                raise ValueError("%s must be a contiguous float32 device tensor" % name)
+            if tuple(t.shape) != shapes[name]:
+                raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
+                                                                    shapes[name]))
+        if out is None:
+            out = torch.empty((self.B, self.Q, self.G * self.D), dtype=torch.float32,
+                              device="cuda")
+        if tuple(out.shape) != (self.B, self.Q, self.G * self.D) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, Q, G*D] float32 tensor")
+        _lib.check(_lib.load().dcn_msda_forward(self._h, _ptr(value), _ptr(locations),
+                                                _ptr(weights), _ptr(out),
+                                                ctypes.c_void_p(_stream_handle(stream))),
+                   "dcn_msda_forward")
+        return out
+
+
+_MSDA_PLANS = {}
+
+
+def msda(value, shapes, locations, weights, softmax=False):
+    """Multi-scale deformable attention sampling (page 5's functional form):
+    value [B,S,G,D], shapes [(H, W), ...], locations [B,Q,G,L,K,2] normalised
+    (x, y), weights [B,Q,G,L*K] (logits when ``softmax``) -> [B,Q,G*D]."""
+    B, S, G, D = value.shape
+    _, Q, _, L, K, _ = locations.shape
+    key = (B, Q, G, D, tuple((int(h), int(w)) for h, w in shapes), K, bool(softmax))
+    p = _MSDA_PLANS.get(key)
+    if p is None:
+        p = MsdaPlan(B, Q, G, D, shapes, K, softmax)
+        _MSDA_PLANS[key] = p
+    return p.forward(value, locations, weights)

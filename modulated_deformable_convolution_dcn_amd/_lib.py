@@ -24,7 +24,8 @@ DCN_OUT_NCHW, DCN_OUT_NHWC = 0, 1
 EXPORTS = ("dcn_create", "dcn_destroy", "dcn_output_size", "dcn_workspace_bytes",
            "dcn_pack_weight", "dcn_forward_packed", "dcn_forward", "dcn_forward_rows",
            "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_backward_workspace_bytes",
-           "dcn_backward", "dcn_debug_coords", "dcn_status_string", "dcn_last_error",
+           "dcn_backward", "dcn_msda_create", "dcn_msda_destroy", "dcn_msda_value_positions",
+           "dcn_msda_forward", "dcn_debug_coords", "dcn_status_string", "dcn_last_error",
            "dcn_version")
 
 
@@ -32,6 +33,12 @@ class DcnDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "in_ch", "height", "width", "out_ch", "kernel_h", "kernel_w",
         "pad_h", "pad_w", "in_dtype", "out_dtype", "out_layout")]
+
+
+class MsdaDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_queries", "num_heads", "head_dim", "num_levels", "num_points", "dtype",
+        "softmax")]
 
 
 class DcnError(RuntimeError):
@@ -67,6 +74,11 @@ def load():
         "dcn_nchw_to_nhwc": (st, [vp, vp, i32, i32, i32, i32, i32, vp]),
         "dcn_backward_workspace_bytes": (st, [vp, ctypes.POINTER(sz)]),
         "dcn_backward": (st, [vp] * 12 + [sz, vp]),
+        "dcn_msda_create": (st, [ctypes.POINTER(MsdaDesc), ctypes.POINTER(i32),
+                                 ctypes.POINTER(vp)]),
+        "dcn_msda_destroy": (st, [vp]),
+        "dcn_msda_value_positions": (st, [vp, ctypes.POINTER(i32)]),
+        "dcn_msda_forward": (st, [vp, vp, vp, vp, vp, vp]),
         "dcn_forward_multi": (st, [i32, ctypes.POINTER(vp), vp, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(sz),
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),

@@ -14,9 +14,16 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <new>
 
 #include "dcn_launch.h"
+
+struct dcn_msda_plan_s {
+  dcn_msda_desc d;
+  int S;
+  int H[dcn::kMsdaMaxLevels], W[dcn::kMsdaMaxLevels], start[dcn::kMsdaMaxLevels];
+};
 
 struct dcn_plan_s {
   dcn_desc d;
@@ -468,6 +475,99 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
     return ok();
   } catch (...) {
     return fail(DCN_E_INTERNAL, "dcn_backward: unexpected exception");
+  }
+}
+
+dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
+                           dcn_msda_plan* plan) {
+  try {
+    if (plan) *plan = nullptr;
+    if (!desc || !level_hw || !plan) return fail(DCN_E_NULL, "dcn_msda_create: NULL argument");
+    const dcn_msda_desc& d = *desc;
+    if (d.batch < 0 || d.num_queries < 0 || d.num_heads <= 0 || d.head_dim <= 0 ||
+        d.num_levels <= 0 || d.num_points <= 0)
+      return fail(DCN_E_SHAPE, "dcn_msda_create: sizes must be positive (batch, queries >= 0)");
+    if (d.dtype != DCN_F32) return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: fp32 only");
+    if (d.num_levels > dcn::kMsdaMaxLevels || d.num_points > dcn::kMsdaMaxPoints)
+      return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: at most %d levels and %d points",
+                  dcn::kMsdaMaxLevels, dcn::kMsdaMaxPoints);
+    if (d.head_dim % 4 != 0 || d.head_dim > 1024)
+      return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: head_dim %d must be a multiple of 4, "
+                                     "at most 1024", d.head_dim);
+    std::unique_ptr<dcn_msda_plan_s> p(new dcn_msda_plan_s{});
+    p->d = d;
+    int64_t S = 0;
+    for (int l = 0; l < d.num_levels; ++l) {
+      const int32_t H = level_hw[2 * l], W = level_hw[2 * l + 1];
+      if (H <= 0 || W <= 0) return fail(DCN_E_SHAPE, "dcn_msda_create: level %d is %dx%d", l, H, W);
+      p->H[l] = H;
+      p->W[l] = W;
+      p->start[l] = (int)S;
+      S += (int64_t)H * W;
+      if (S >= kLimit31) return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: too many positions");
+    }
+    p->S = (int)S;
+    const int64_t vbytes = (int64_t)d.batch * S * d.num_heads * d.head_dim * 4;
+    const int64_t pairs = (int64_t)d.batch * d.num_queries * d.num_heads;
+    if (vbytes >= kLimit31 || pairs * d.head_dim >= kLimit31 ||
+        pairs * d.num_levels * d.num_points * 2 >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: tensors must stay below 2^31 elements "
+                                     "(value below 2^31 bytes)");
+    *plan = p.release();
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_msda_create: unexpected exception");
+  }
+}
+
+dcn_status dcn_msda_destroy(dcn_msda_plan plan) {
+  delete plan;
+  return ok();
+}
+
+dcn_status dcn_msda_value_positions(dcn_msda_plan plan, int32_t* positions) {
+  if (!plan || !positions) return fail(DCN_E_NULL, "dcn_msda_value_positions: NULL argument");
+  *positions = plan->S;
+  return ok();
+}
+
+dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* locations,
+                            const void* weights, void* out, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_msda_forward: plan is NULL");
+    const dcn_msda_desc& d = plan->d;
+    const int64_t pairs = (int64_t)d.batch * d.num_queries * d.num_heads;
+    if (pairs == 0) return ok();
+    if (!value || !locations || !weights || !out)
+      return fail(DCN_E_NULL, "dcn_msda_forward: value, locations, weights and out are required");
+    if (!aligned(value, 16) || !aligned(out, 16) || !aligned(locations, 8) || !aligned(weights, 4))
+      return fail(DCN_E_ALIGN, "dcn_msda_forward: value and out must be 16-byte aligned, "
+                               "locations 8-byte");
+    dcn::MsdaArgs a{};
+    a.value = static_cast<const float*>(value);
+    a.locations = static_cast<const float*>(locations);
+    a.weights = static_cast<const float*>(weights);
+    a.out = static_cast<float*>(out);
+    a.npairs = pairs;
+    a.B = d.batch;
+    a.S = plan->S;
+    a.G = d.num_heads;
+    a.D = d.head_dim;
+    a.Q = d.num_queries;
+    a.L = d.num_levels;
+    a.K = d.num_points;
+    a.softmax = d.softmax ? 1 : 0;
+    for (int l = 0; l < d.num_levels; ++l) {
+      a.H[l] = plan->H[l];
+      a.W[l] = plan->W[l];
+      a.start[l] = plan->start[l];
+    }
+    a.value_bytes = (uint32_t)((int64_t)d.batch * plan->S * d.num_heads * d.head_dim * 4);
+    hipError_t e = dcn::launch_msda(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "msda launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_msda_forward: unexpected exception");
   }
 }
 

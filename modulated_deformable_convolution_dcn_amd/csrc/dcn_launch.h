@@ -63,6 +63,21 @@ int64_t bwd_workspace_floats(int O, int C, int K);
 hipError_t launch_backward(const BwdArgs& a, const float* weight, float* workspace,
                            hipStream_t stream);
 
+// Multi-scale deformable attention sampling (dcn_msda.hip), fp32.
+constexpr int kMsdaMaxLevels = 8;
+constexpr int kMsdaMaxPoints = 8;
+struct MsdaArgs {
+  const float* value;      // [B, S, G, D]
+  const float* locations;  // [B, Q, G, L, K, 2] normalised (x, y)
+  const float* weights;    // [B, Q, G, L*K]
+  float* out;              // [B, Q, G, D]
+  int64_t npairs;          // B * Q * G
+  int B, S, G, D, Q, L, K, softmax;
+  int H[kMsdaMaxLevels], W[kMsdaMaxLevels], start[kMsdaMaxLevels];
+  uint32_t value_bytes;
+};
+hipError_t launch_msda(const MsdaArgs& a, hipStream_t stream);
+
 // Several branches (same input map, own offsets/mask/weight/bias/output and
 // kernel size) in one launch: branch i owns the logical workgroups
 // [start[i], start[i+1]).

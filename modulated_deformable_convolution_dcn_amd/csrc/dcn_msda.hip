@@ -1,0 +1,169 @@
+// dcn_msda.hip -- multi-scale deformable attention sampling (fp32).
+//
+// Page 5 (deformops README, "Multi-scale deformable attention"): value
+// (B, sum_l H_l W_l, G, D) holds L flattened feature maps, locations
+// (B, Q, G, L, K, 2) are normalised (x, y) in [0, 1], weights (B, Q, G, L*K)
+// are used as given or normalised by a softmax over levels and points; the
+// output (B, Q, G*D) is the attention-weighted sum of the bilinear samples.
+// This is the deformable convolution's gather (coordinate stage, corner
+// gather, weighted blend) without the dense contraction, so it is bound by
+// the corner traffic, not by matrix math.
+//
+// A normalised location maps to pixel coordinates with the half-pixel
+// convention, p = (x * W - 0.5, y * H - 0.5), each product and difference
+// rounded to fp32 (no fused multiply-add); corners outside the level count as
+// zero.
+//
+// One workgroup handles 32 (b, q, g) pairs:
+//   (a) coefficient stage: every (pair, point) gets its four corner weights
+//       (attention x bilinear x validity) and corner byte offsets in an LDS
+//       table (the softmax, when asked for, is reduced over the 8 threads of
+//       a pair first);
+//   (b) gather: D/4 lanes per pair each own 16 bytes of the head's D
+//       channels; per point they read the table entry (a broadcast), issue
+//       the four 16-byte corner loads (buffer loads: an outside corner reads
+//       zero) and accumulate; one 16-byte store per lane.
+
+#include "dcn_device.h"
+#include "dcn_launch.h"
+
+namespace dcn {
+
+namespace {
+constexpr int NPAIR = 32;   // (b, q, g) pairs per workgroup
+constexpr int TPP = 256 / NPAIR;  // coefficient threads per pair
+}  // namespace
+
+__global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
+  constexpr int MAXLK = kMsdaMaxLevels * kMsdaMaxPoints;
+  __shared__ f32x4 Cw[NPAIR * MAXLK];
+  __shared__ u32x4 Co[NPAIR * MAXLK];
+  __shared__ int lv[kMsdaMaxLevels][3];  // H, W, start
+
+  const int tid = threadIdx.x;
+  const int LK = a.L * a.K;
+  if (tid < a.L) {
+    lv[tid][0] = a.H[tid];
+    lv[tid][1] = a.W[tid];
+    lv[tid][2] = a.start[tid];
+  }
+  __syncthreads();
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t n0 = (int64_t)logical * NPAIR;
+
+  // ---- (a) coefficients: thread -> pair tid / TPP, points e = tid % TPP + TPP * r
+  {
+    const int pl = tid / TPP, sub = tid % TPP;
+    const int64_t n = n0 + pl;
+    const bool pin = n < a.npairs;
+    const int npt = (LK + TPP - 1) / TPP;  // points per thread (<= MAXLK / TPP)
+    float logit[MAXLK / TPP];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < MAXLK / TPP; ++r) {
+      const int e = sub + TPP * r;
+      logit[r] = (r < npt && e < LK && pin) ? a.weights[n * LK + e] : -INFINITY;
+      mx = fmaxf(mx, logit[r]);
+    }
+    float sum = 0.f;
+    if (a.softmax) {
+#pragma unroll
+      for (int sh = TPP / 2; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh, TPP));
+#pragma unroll
+      for (int r = 0; r < MAXLK / TPP; ++r)
+        if (logit[r] != -INFINITY) sum += expf(logit[r] - mx);
+#pragma unroll
+      for (int sh = TPP / 2; sh >= 1; sh >>= 1) sum += __shfl_xor(sum, sh, TPP);
+    }
+    const int64_t g = pin ? n % a.G : 0;
+    const int64_t b = pin ? n / ((int64_t)a.Q * a.G) : 0;
+#pragma unroll
+    for (int r = 0; r < MAXLK / TPP; ++r) {
+      const int e = sub + TPP * r;
+      if (r >= npt || e >= LK) continue;
+      const int l = e / a.K;
+      const int H = lv[l][0], W = lv[l][1], st = lv[l][2];
+      f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
+      u32x4 o4 = {kNoCorner, kNoCorner, kNoCorner, kNoCorner};
+      if (pin) {
+        const float att = a.softmax ? expf(logit[r] - mx) / sum : logit[r];
+        const float x = a.locations[(n * LK + e) * 2], y = a.locations[(n * LK + e) * 2 + 1];
+        const float px = __fsub_rn(__fmul_rn(x, (float)W), 0.5f);
+        const float py = __fsub_rn(__fmul_rn(y, (float)H), 0.5f);
+        const float x0 = floorf(px), y0 = floorf(py);
+        const float fx = __fsub_rn(px, x0), fy = __fsub_rn(py, y0);
+        const float wv[4] = {(1.f - fy) * (1.f - fx), (1.f - fy) * fx, fy * (1.f - fx), fy * fx};
+        const int ix = (int)fminf(fmaxf(x0, -1.0f), (float)W);
+        const int iy = (int)fminf(fmaxf(y0, -1.0f), (float)H);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float yy = __fadd_rn(y0, (float)(q >> 1)), xx = __fadd_rn(x0, (float)(q & 1));
+          const bool ok = yy >= 0.f && yy <= (float)(H - 1) && xx >= 0.f && xx <= (float)(W - 1);
+          if (ok) {
+            w4[q] = att * wv[q];
+            const int64_t pix = (int64_t)st + (int64_t)(iy + (q >> 1)) * W + ix + (q & 1);
+            o4[q] = (uint32_t)(((b * a.S + pix) * a.G + g) * a.D * 4);
+          }
+        }
+      }
+      Cw[pl * MAXLK + e] = w4;
+      Co[pl * MAXLK + e] = o4;
+    }
+  }
+  __syncthreads();
+
+  // ---- (b) gather: lanes per pair = D / 4
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.value, a.value_bytes);
+  const int lpp = a.D >> 2;
+  const int ppp = 256 / lpp;  // pairs per pass
+  const int pr = tid / lpp, sl = tid - (tid / lpp) * lpp;
+  for (int p0 = 0; p0 < NPAIR; p0 += ppp) {
+    const int pl = p0 + pr;
+    if (pr >= ppp || pl >= NPAIR) continue;
+    const int64_t n = n0 + pl;
+    if (n >= a.npairs) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t lb = (uint32_t)sl * 16u;
+    int e = 0;
+    for (; e + 4 <= LK; e += 4) {  // four points (16 loads) in flight
+      u32x4 v[4][4];
+      f32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 o = Co[pl * MAXLK + e + u];
+        w[u] = Cw[pl * MAXLK + e + u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[u][q] = load16(vr, o[q] + lb);  // kNoCorner + lb stays outside
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 f = __builtin_bit_cast(f32x4, v[u][q]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w[u][q], f[c], acc[c]);
+        }
+    }
+    for (; e < LK; ++e) {
+      const u32x4 o = Co[pl * MAXLK + e];
+      const f32x4 w = Cw[pl * MAXLK + e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 f = __builtin_bit_cast(f32x4, load16(vr, o[q] + lb));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w[q], f[c], acc[c]);
+      }
+    }
+    *reinterpret_cast<f32x4*>(a.out + n * a.D + 4 * sl) = acc;
+  }
+}
+
+hipError_t launch_msda(const MsdaArgs& a, hipStream_t s) {
+  const int64_t nblk = (a.npairs + NPAIR - 1) / NPAIR;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(msda_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dcn

@@ -177,3 +177,53 @@ def make_inputs(spec: Spec):
             out[k], bits[k] = round_bf16(v)
         out["bits"] = bits
     return out
+
+
+@dataclass(frozen=True)
+class MsdaSpec:
+    """A multi-scale deformable attention sampling workload (page 5)."""
+    name: str
+    B: int
+    Q: int
+    G: int
+    D: int
+    shapes: tuple
+    K: int
+    softmax: bool
+    seed: int
+    loc_lo: float = -0.05   # locations ~ U(loc_lo, loc_hi): a few points fall outside
+    loc_hi: float = 1.05
+
+    @property
+    def L(self) -> int:
+        return len(self.shapes)
+
+    @property
+    def S(self) -> int:
+        return sum(h * w for h, w in self.shapes)
+
+    def scaled(self, **kw) -> "MsdaSpec":
+        return replace(self, **kw)
+
+
+# Deformable-DETR-like encoder: every position of a 4-level pyramid
+# (64^2, 32^2, 16^2, 8^2 -- page 5's example shapes) queries 4 points per
+# level in each of 8 heads of 32 channels; softmax over the 16 logits.
+MSDA_WORKLOADS = {
+    "msda_encoder_fp32": MsdaSpec("msda_encoder_fp32", 4, 5440, 8, 32,
+                                  ((64, 64), (32, 32), (16, 16), (8, 8)), 4, True, 21),
+    "msda_decoder_fp32": MsdaSpec("msda_decoder_fp32", 8, 300, 8, 32,
+                                  ((64, 64), (32, 32), (16, 16), (8, 8)), 4, True, 22),
+}
+
+
+def make_msda_inputs(spec: MsdaSpec) -> dict:
+    """value ~ N(0,1) [B,S,G,D]; locations ~ U(loc_lo, loc_hi) [B,Q,G,L,K,2];
+    weights (logits) ~ N(0,1) [B,Q,G,L*K]; all float32, drawn in that order."""
+    rng = np.random.default_rng(spec.seed)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)  # noqa: E731
+    value = f32(rng.standard_normal((spec.B, spec.S, spec.G, spec.D)))
+    loc = f32(rng.uniform(spec.loc_lo, spec.loc_hi,
+                          size=(spec.B, spec.Q, spec.G, spec.L, spec.K, 2)))
+    w = f32(rng.standard_normal((spec.B, spec.Q, spec.G, spec.L * spec.K)))
+    return {"value": value, "locations": loc, "weights": w}

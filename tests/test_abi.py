@@ -238,3 +238,25 @@ def test_backward_checks_fire_before_any_launch():
     assert "256" in lib.dcn_last_error().decode()
     empty = Plan(Desc(0, 64, 16, 16, 64, 3, 3, 1, 1))
     assert lib.dcn_backward(empty._h, *[None] * 10, None, 0, None) == 0
+
+
+def test_msda_create_validates_and_checks_pointers():
+    from modulated_deformable_convolution_dcn_amd import MsdaPlan
+    lib = _lib.load()
+    p = MsdaPlan(2, 10, 8, 32, [(8, 8), (4, 4)], 4, softmax=True)
+    assert p.S == 80
+    bad = [dict(shapes=[(8, 8)] * 9), dict(K=9), dict(D=30), dict(D=2048), dict(shapes=[(0, 4)])]
+    want = [4, 4, 4, 4, 2]
+    for kw, st in zip(bad, want):
+        args = dict(B=1, Q=4, G=2, D=8, shapes=[(4, 4)], K=2)
+        args.update(kw)
+        with pytest.raises(_lib.DcnError) as e:
+            MsdaPlan(args["B"], args["Q"], args["G"], args["D"], args["shapes"], args["K"])
+        assert e.value.status == st, (kw, e.value.status)
+    fake = ctypes.c_void_p(0x10000)
+    h = p._h
+    assert lib.dcn_msda_forward(h, None, fake, fake, fake, None) == 1
+    assert lib.dcn_msda_forward(h, ctypes.c_void_p(0x10008), fake, fake, fake, None) == 5
+    assert lib.dcn_msda_forward(h, fake, ctypes.c_void_p(0x10004), fake, fake, None) == 5
+    empty = MsdaPlan(0, 10, 8, 32, [(8, 8)], 4)
+    assert lib.dcn_msda_forward(empty._h, None, None, None, None, None) == 0
