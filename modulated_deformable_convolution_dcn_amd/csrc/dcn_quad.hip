@@ -104,25 +104,56 @@ fused_quad_kernel(Src src) {
     dx = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
     mk = load_scalar<float>(mskr, mb);
   };
-  auto coef_finish = [&](int kt, float dy, float dx, float mkr) {
-    const int slot = kt % NSLOT;
-    const int i = kt / a.kw;
-    const int j = kt - i * a.kw;
-    const TapPoint t = tap_point(dy, dx, c_ho - a.ph + i, c_wo - a.pw + j, a.H, a.W);
-    const float mk = has_mask ? mkr : 1.0f;
-    // corners (a, 0) and (a, 1) with a = c_pair
-    const float wy = c_pair ? t.ly : 1.0f - t.ly;
-    const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
-    const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
-    const uint32_t base = (uint32_t)((b * a.H + y0 + c_pair) * a.W + x0) * row_bytes;
-    const bool ok0 = c_in && ((t.valid >> (2 * c_pair)) & 1u);
-    const bool ok1 = c_in && ((t.valid >> (2 * c_pair + 1)) & 1u);
+  // The table entry of one tap, in four stages so that the step can spread
+  // them over four MFMA slots (the sampling point of page 1: exact integer
+  // grid plus ONE fp32 add of the offset, floor, fp32 fractions; validity of
+  // corner row y0 + a and columns x0, x0 + 1 compared on the floor, whose
+  // clamp to [-2, H] x [-2, W] keeps every outside corner outside).
+  const float c_gyb = (float)(c_ho - a.ph);  // exact: |values| < 2^24
+  const float c_gxb = (float)(c_wo - a.pw);
+  const float c_s = c_pair ? 1.0f : -1.0f, c_t = c_pair ? 0.0f : 1.0f;  // row weight ly*s + t
+  const uint32_t c_img = (uint32_t)b * (uint32_t)a.H * (uint32_t)a.W;
+  struct CoefState {
+    float ly, lx, fy, fx, w0, w1;
+    int ry, ix;
+    bool ok0, ok1;
+  } cs;
+  auto coef_stage = [&](int stage, int kt, float dy, float dx, float mkr) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const f32x2 w2 = {ok0 ? wy * (1.0f - t.lx) * mk : 0.0f, ok1 ? wy * t.lx * mk : 0.0f};
-    const u32x2 o2 = {ok0 ? base : kNoCorner, ok1 ? base + row_bytes : kNoCorner};
-    *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(&Cw[slot * PW + c_px]) + 2 * c_pair) = w2;
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&Co[slot * PW + c_px]) + 2 * c_pair) = o2;
+    if (stage == 0) {
+      const int i = kt / a.kw, j = kt - (kt / a.kw) * a.kw;
+      const float py = __fadd_rn(c_gyb + (float)i, dy);
+      const float px = __fadd_rn(c_gxb + (float)j, dx);
+      cs.fy = floorf(py);
+      cs.fx = floorf(px);
+      cs.ly = __fsub_rn(py, cs.fy);
+      cs.lx = __fsub_rn(px, cs.fx);
+    } else if (stage == 1) {
+      const int iy = (int)fminf(fmaxf(cs.fy, -2.0f), (float)a.H);
+      cs.ix = (int)fminf(fmaxf(cs.fx, -2.0f), (float)a.W);
+      cs.ry = iy + c_pair;
+      const bool rok = c_in && (uint32_t)cs.ry < (uint32_t)a.H;
+      cs.ok0 = rok && (uint32_t)cs.ix < (uint32_t)a.W;
+      cs.ok1 = rok && (uint32_t)(cs.ix + 1) < (uint32_t)a.W;
+    } else if (stage == 2) {
+      const float wy = __builtin_fmaf(cs.ly, c_s, c_t);  // 1 - ly or ly, exactly rounded
+      const float wm = has_mask ? wy * mkr : wy;
+      cs.w0 = cs.ok0 ? wm * (1.0f - cs.lx) : 0.0f;
+      cs.w1 = cs.ok1 ? wm * cs.lx : 0.0f;
+    } else {
+      const int slot = kt % NSLOT;
+      const uint32_t base = (c_img + (uint32_t)(cs.ry * a.W + cs.ix)) * row_bytes;
+      const f32x2 w2 = {cs.w0, cs.w1};
+      const u32x2 o2 = {cs.ok0 ? base : kNoCorner, cs.ok1 ? base + row_bytes : kNoCorner};
+      *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(&Cw[slot * PW + c_px]) + 2 * c_pair) = w2;
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&Co[slot * PW + c_px]) + 2 * c_pair) =
+          o2;
+    }
+  };
+  auto coef_finish = [&](int kt, float dy, float dx, float mkr) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) coef_stage(st, kt, dy, dx, mkr);
   };
 
   // ---- (b) corners: lane = (pixel pp of an 8-pixel pass, 16-byte slice sl
@@ -208,7 +239,8 @@ fused_quad_kernel(Src src) {
   // weight fragments of block s+1.
   // Group 1 (rows 16-31): blend of block s+1 passes 0, 1 (rows 0-15) and
   // their corner loads for block s+2; fragments of rows 0-15 of block s+1;
-  // the coefficient table of tap (s+3)/nchunk from offsets loaded two steps
+  // the coefficient table of tap (s+3)/nchunk (four stages in four slots) from
+  // offsets loaded two steps
   // ago, then the offsets of tap (s+5)/nchunk.
   // Per pass pair: 4 table reads, then per pass 4 blend terms, the tile
   // write and 4 corner loads (22 actions).
@@ -228,7 +260,7 @@ fused_quad_kernel(Src src) {
     static_for<2>([&](auto MT) {
       constexpr int mt = decltype(MT)::value;
       constexpr int pa = mt == 0 ? 2 : 0;  // passes blended under this group
-      constexpr int NACT = NPA + 2 + (mt == 0 ? NT * 2 : 2);
+      constexpr int NACT = NPA + 2 + (mt == 0 ? NT * 2 : 5);
       // group 0: blend block s, load block s+1; group 1: blend s+1, load s+2
       const int slw = mt == 0 ? sl_s : sl_1;
       const int slo = mt == 0 ? sl_1 : sl_2;
@@ -264,8 +296,8 @@ fused_quad_kernel(Src src) {
           af[mt ^ 1][x - NPA] = a_frag(mt ^ 1, x - NPA);
         } else if constexpr (mt == 0) {
           bw[P ^ 1][x - NPA - 2] = *reinterpret_cast<const f32x4*>(bsrc + (x - NPA - 2) * 256);
-        } else if constexpr (x == NPA + 2) {
-          if (coef_due) coef_finish(tc, c_dy[P], c_dx[P], c_mk[P]);
+        } else if constexpr (x < NPA + 6) {
+          if (coef_due) coef_stage(x - NPA - 2, tc, c_dy[P], c_dx[P], c_mk[P]);
         } else {
           coef_load(tl, c_dy[P], c_dx[P], c_mk[P]);
         }
