@@ -367,6 +367,12 @@ def main() -> int:
     ms_per_step = (sum(e[0].elapsed_time(e[2]) for e in events) / args.steps if args.cold
                    else elapsed * 1e3 / args.steps)
     P = spec.pixels * nbr
+    # runs of the split tap sum (1: none): the scratch holds one fp32 partial
+    # output per run, element count rounded up to 64
+    n_out = spec.B * spec.O * spec.Ho * spec.Wo
+    tap_split = 1
+    if not extra and not args.backward and plan.workspace_bytes > plan.packed_weight_bytes:
+        tap_split = (plan.workspace_bytes - plan.packed_weight_bytes) // (-(-n_out // 64) * 64 * 4)
     # the backward runs two contractions of the forward's size (dL/dsample and dL/dW)
     flops = spec.gemm_flops * nbr * (2 if args.backward else 1)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -390,6 +396,7 @@ def main() -> int:
                    "pad": [spec.ph, spec.pw], "out_layout": args.layout,
                    "input_layout": args.input_layout, "row_bands": nb,
                    "pass": "backward" if args.backward else "forward",
+                   "tap_split": tap_split,
                    "branches": nbr, "branch_launch": ("one per branch" if args.sequential
                                                       else "one for all") if nbr > 1 else None},
         "tflops": tflops,
@@ -397,6 +404,8 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": fused_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
                      "traffic": measured_traffic(spec.name)},
+        # "fused" spans the whole forward call: with a tap split, the fused
+        # kernel and the reduce that adds the runs
         "kernels_us": {"fused": fused_ms * 1e3,
                        ("transpose+pack" if x_nchw is not None else "pack"): pack_ms * 1e3},
         "fused_us_percentiles": {k: v * 1e3 for k, v in percentiles(fused_list).items()},

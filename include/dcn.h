@@ -103,14 +103,24 @@ dcn_status dcn_destroy(dcn_plan plan);
 /* Output size of a plan: Ho, Wo (either pointer may be NULL). */
 dcn_status dcn_output_size(dcn_plan plan, int32_t* ho, int32_t* wo);
 
-/* Bytes of device workspace dcn_forward needs: the weight repacked as
- * [tap][channel block][out channel] tiles (page 1 reorders the weight to
- * rows (i, j, c), columns o before its one matmul), zero-padded to the
- * kernel's tile sizes. */
+/* Bytes of device workspace a forward call runs fastest with: the weight
+ * repacked as [tap][channel block][out channel] tiles (page 1 reorders the
+ * weight to rows (i, j, c), columns o before its one matmul), zero-padded to
+ * the kernel's tile sizes, then -- for plans whose grid would leave most of
+ * the GPU idle (fp32 with 17..64 output channels and few output tiles) --
+ * scratch for a split of the tap sum: the taps are divided into up to 4 runs
+ * computed side by side into fp32 partial outputs that a second kernel adds
+ * (in run order, deterministic) together with the bias. */
 dcn_status dcn_workspace_bytes(dcn_plan plan, size_t* bytes);
 
+/* Bytes of the packed weight at the start of the workspace (<= the
+ * dcn_workspace_bytes size).  dcn_pack_weight writes only these bytes; a
+ * forward call given a workspace of fewer than dcn_workspace_bytes bytes
+ * (but at least these) runs without the tap split. */
+dcn_status dcn_packed_weight_bytes(dcn_plan plan, size_t* bytes);
+
 /* Repack `weight` [O, C, kh, kw] into `workspace` (device, >= the size
- * dcn_workspace_bytes reports).  One kernel launch on `stream`.  Callers
+ * dcn_packed_weight_bytes reports).  One kernel launch on `stream`.  Callers
  * whose weight does not change may call this once and then reuse the
  * packed workspace with dcn_forward_packed. */
 dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
@@ -118,15 +128,22 @@ dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
 
 /* The forward from an already packed weight: one fused kernel launch on
  * `stream` (sampling point, bilinear gather and modulation into an on-chip
- * column tile, MFMA contraction, bias epilogue).  `mask` and `bias` may be
- * NULL.  `out` must not overlap any input. */
+ * column tile, MFMA contraction, bias epilogue); with the tap split (see
+ * dcn_workspace_bytes) the fused kernel writes partial sums into the
+ * workspace's scratch and a reduce kernel writes `out`.  `workspace` holds
+ * the packed weight (dcn_pack_weight) in its first dcn_packed_weight_bytes
+ * bytes, which are only read; `workspace_bytes` (>= dcn_packed_weight_bytes,
+ * else DCN_E_WORKSPACE) is its size, and bytes beyond the packed weight are
+ * overwritten when the call splits its taps: calls that may overlap in time
+ * (different streams) then need workspaces of their own.  `mask` and `bias`
+ * may be NULL.  `out` must not overlap any input or the workspace. */
 dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset,
-                              const void* mask, const void* packed_weight,
-                              size_t workspace_bytes, const void* bias, void* out,
-                              void* stream);
+                              const void* mask, void* workspace, size_t workspace_bytes,
+                              const void* bias, void* out, void* stream);
 
 /* The whole forward: dcn_pack_weight then dcn_forward_packed, both on
- * `stream`. */
+ * `stream`, with one workspace (>= dcn_packed_weight_bytes bytes;
+ * dcn_workspace_bytes enables the tap split). */
 dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const void* mask,
                        const void* weight, const void* bias, void* out, void* workspace,
                        size_t workspace_bytes, void* stream);
@@ -138,13 +155,14 @@ dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const v
  *   offset [B, 2K, rows, Wo], mask [B, K, rows, Wo] or NULL  -- the band's
  *          rows only (row r of the band is output row row0 + r)
  *   out    [B, O, rows, Wo] (NCHW) or [B, rows, Wo, O] (NHWC), fp32
- *   x, packed_weight, bias exactly as for dcn_forward_packed.
+ *   x, workspace, bias exactly as for dcn_forward_packed.
  * Sampling points use the absolute output row, so the bands of a partition
  * of [0, Ho) reproduce dcn_forward_packed's output row for row.
  * DCN_E_SHAPE unless 0 <= row0, 0 <= rows and row0 + rows <= Ho; rows == 0
- * is a no-op.  One fused kernel launch on `stream`. */
+ * is a no-op.  One fused kernel launch on `stream` (plus the reduce when
+ * the band's grid splits its taps). */
 dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const void* x,
-                            const void* offset, const void* mask, const void* packed_weight,
+                            const void* offset, const void* mask, void* workspace,
                             size_t workspace_bytes, const void* bias, void* out,
                             void* stream);
 
@@ -159,7 +177,9 @@ dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const voi
  * differ.  Branches that run the same kernel variant share ONE launch (the
  * workgroups of all of them in one grid); 1 <= n <= 8 (n == 0 is a no-op,
  * more is DCN_E_UNSUPPORTED).  Per-branch pointer rules and errors as for
- * dcn_forward_packed; nothing is launched unless every branch validates. */
+ * dcn_forward_packed, but the branches never split their taps (the common
+ * grid is already wide) and the workspaces are only read; nothing is
+ * launched unless every branch validates. */
 dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
                              const void* const* offsets, const void* const* masks,
                              const void* const* packed_weights, const size_t* workspace_bytes,

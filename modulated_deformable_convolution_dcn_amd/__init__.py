@@ -78,6 +78,8 @@ class Plan:
         ws = ctypes.c_size_t()
         _lib.check(lib.dcn_workspace_bytes(h, ctypes.byref(ws)), "dcn_workspace_bytes")
         self.workspace_bytes = ws.value
+        _lib.check(lib.dcn_packed_weight_bytes(h, ctypes.byref(ws)), "dcn_packed_weight_bytes")
+        self.packed_weight_bytes = ws.value
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -126,19 +128,23 @@ class Plan:
         self._check("bias", bias, (d.out_ch,), optional=True)
 
     # -- calls --------------------------------------------------------------
-    def new_workspace(self):
+    def new_workspace(self, split=True):
+        """A workspace of ``dcn_workspace_bytes`` bytes, or with ``split=False``
+        only ``dcn_packed_weight_bytes`` (forward calls then never split taps)."""
         torch = _torch()
-        return torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        n = self.workspace_bytes if split else self.packed_weight_bytes
+        return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
 
     def new_output(self):
         torch = _torch()
         return torch.empty(self.out_shape(), dtype=torch.float32, device="cuda")
 
-    def pack_weight(self, weight, workspace=None, stream=None):
-        """``dcn_pack_weight``: weight [O,C,kh,kw] -> packed workspace (returned)."""
+    def pack_weight(self, weight, workspace=None, stream=None, split=True):
+        """``dcn_pack_weight``: weight [O,C,kh,kw] -> packed workspace (returned;
+        ``split`` as for ``new_workspace``)."""
         d = self.desc
         self._check("weight", weight, (d.out_ch, d.in_ch, d.kernel_h, d.kernel_w))
-        ws = workspace if workspace is not None else self.new_workspace()
+        ws = workspace if workspace is not None else self.new_workspace(split)
         _lib.check(_lib.load().dcn_pack_weight(self._h, _ptr(weight), _ptr(ws), ws.numel(),
                                                ctypes.c_void_p(_stream_handle(stream))),
                    "dcn_pack_weight")

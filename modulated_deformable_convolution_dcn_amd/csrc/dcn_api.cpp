@@ -29,7 +29,9 @@ struct dcn_plan_s {
   dcn_desc d;
   int K, Ho, Wo;
   dcn::KernelConfig kc;
-  size_t ws_bytes;
+  size_t wpack_bytes;    // packed weight at the start of the workspace (256-B multiple)
+  size_t ws_bytes;       // + scratch for the split tap sum (0 bytes when the plan never splits)
+  int nsplit, kper;      // tap split of the whole-map grid (1, K: none); bands use the same
   uint32_t x_bytes;
 };
 
@@ -99,6 +101,29 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
   kc.tiles_per_img = (int)ceil_div(HoWo, kc.M);
   return kc;
 }
+
+// The 32x32-per-wave kernel holds two workgroups per CU (one wave per SIMD
+// each); 256 CUs give 512 resident workgroups.  A grid that fills at most half
+// of them splits its tap sum over up to 4 workgroups per tile (each split a
+// contiguous run of taps, at least one), so the chip holds two per CU; a
+// reduce then adds the splits and the bias.
+constexpr int64_t kResidentQuadWG = 512;
+
+void choose_split(const dcn::KernelConfig& kc, int K, int64_t nwg, int& nsplit, int& kper) {
+  nsplit = 1;
+  kper = K;
+  if (kc.kind != 2 || nwg <= 0 || 2 * nwg > kResidentQuadWG) return;
+  int ns = (int)(kResidentQuadWG / nwg);
+  if (ns > 4) ns = 4;
+  if (ns > K) ns = K;
+  if (ns < 2) return;
+  kper = (int)ceil_div(K, ns);
+  nsplit = (int)ceil_div(K, kper);
+}
+
+// Floats between consecutive splits' partial outputs: the output's element
+// count rounded up to 64 (keeps every partial 256-byte aligned).
+int64_t split_stride(int64_t B, int64_t O, int64_t HoWo) { return (B * O * HoWo + 63) / 64 * 64; }
 
 dcn_status hip_fail(hipError_t e, const char* what) {
   return fail(DCN_E_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -188,7 +213,12 @@ dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan) {
     p->Ho = (int)Ho;
     p->Wo = (int)Wo;
     p->kc = kc;
-    p->ws_bytes = (size_t)((wp * E + 255) / 256 * 256);
+    p->wpack_bytes = (size_t)((wp * E + 255) / 256 * 256);
+    choose_split(kc, (int)K, (int64_t)d.batch * kc.tiles_per_img * kc.n_otiles, p->nsplit,
+                 p->kper);
+    const int64_t scratch =
+        p->nsplit > 1 ? p->nsplit * split_stride(d.batch, d.out_ch, HoWo) * 4 : 0;
+    p->ws_bytes = p->wpack_bytes + (size_t)scratch;
     p->x_bytes = (uint32_t)x_bytes;
     *plan = p;
     return ok();
@@ -215,14 +245,20 @@ dcn_status dcn_workspace_bytes(dcn_plan plan, size_t* bytes) {
   return ok();
 }
 
+dcn_status dcn_packed_weight_bytes(dcn_plan plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(DCN_E_NULL, "dcn_packed_weight_bytes: NULL argument");
+  *bytes = plan->wpack_bytes;
+  return ok();
+}
+
 dcn_status dcn_pack_weight(dcn_plan plan, const void* weight, void* workspace,
                            size_t workspace_bytes, void* stream) {
   try {
     if (!plan) return fail(DCN_E_NULL, "dcn_pack_weight: plan is NULL");
     if (!weight) return fail(DCN_E_NULL, "dcn_pack_weight: weight is NULL");
-    if (!workspace || workspace_bytes < plan->ws_bytes)
-      return fail(DCN_E_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", plan->ws_bytes,
-                  workspace_bytes, workspace);
+    if (!workspace || workspace_bytes < plan->wpack_bytes)
+      return fail(DCN_E_WORKSPACE, "packed weight needs %zu bytes, got %zu at %p",
+                  plan->wpack_bytes, workspace_bytes, workspace);
     const size_t E = plan->kc.bf16 ? 2 : 4;
     if (!aligned(weight, E)) return fail(DCN_E_ALIGN, "weight is not %zu-byte aligned", E);
     if (!aligned(workspace, 16)) return fail(DCN_E_ALIGN, "workspace is not 16-byte aligned");
@@ -259,9 +295,9 @@ dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
     return ok();
   }
   if (!x || !offset || !out) return fail(DCN_E_NULL, "%s: x, offset and out are required", who);
-  if (!packed_weight || workspace_bytes < plan->ws_bytes)
+  if (!packed_weight || workspace_bytes < plan->wpack_bytes)
     return fail(DCN_E_WORKSPACE, "%s: packed weight needs %zu bytes, got %zu at %p", who,
-                plan->ws_bytes, workspace_bytes, packed_weight);
+                plan->wpack_bytes, workspace_bytes, packed_weight);
   const size_t E = plan->kc.bf16 ? 2 : 4;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(packed_weight, 16))
     return fail(DCN_E_ALIGN, "%s: x, out and the packed weight must be 16-byte aligned", who);
@@ -296,21 +332,46 @@ dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
   a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
   a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
   a.vec_store = (a.HoWo % 4) == 0;
+  a.nsplit = 1;
+  a.kper = plan->K;
+  a.split_stride = 0;
   return ok();
 }
 
 dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
-                        const void* x, const void* offset, const void* mask,
-                        const void* packed_weight, size_t workspace_bytes, const void* bias,
-                        void* out, void* stream) {
+                        const void* x, const void* offset, const void* mask, void* workspace,
+                        size_t workspace_bytes, const void* bias, void* out, void* stream) {
   try {
     dcn::FusedArgs a;
     dcn::KernelConfig kc;
     bool empty;
-    dcn_status st = make_args(who, plan, row0, rows, x, offset, mask, packed_weight,
+    dcn_status st = make_args(who, plan, row0, rows, x, offset, mask, workspace,
                               workspace_bytes, bias, out, a, kc, empty);
     if (st != DCN_OK || empty) return st;
-    hipError_t e = dcn::launch_fused(kc, a, static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // split tap sum when the plan's whole-map grid is small and the workspace
+    // carries the scratch; a band splits like the whole map, so the bands of a
+    // partition reproduce the whole-map output bit for bit
+    const int nsplit = plan->nsplit, kper = plan->kper;
+    const int64_t stride = split_stride(a.B, a.O, a.HoWo);
+    const size_t scratch = workspace_bytes - plan->wpack_bytes;
+    if (nsplit > 1 && (size_t)(nsplit * stride * 4) <= scratch && stride < kLimit31) {
+      float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->wpack_bytes);
+      float* out_f = a.out;
+      const float* bias_f = static_cast<const float*>(a.bias);
+      a.out = part;
+      a.bias = nullptr;
+      a.nsplit = nsplit;
+      a.kper = kper;
+      a.split_stride = (uint32_t)stride;
+      hipError_t e = dcn::launch_fused(kc, a, hs);
+      if (e != hipSuccess) return hip_fail(e, "fused forward launch (tap split)");
+      e = dcn::launch_split_reduce(part, nsplit, (uint32_t)stride, bias_f, out_f, a.B, a.O,
+                                   a.HoWo, kc.nhwc, hs);
+      if (e != hipSuccess) return hip_fail(e, "split reduce launch");
+      return ok();
+    }
+    hipError_t e = dcn::launch_fused(kc, a, hs);
     if (e != hipSuccess) return hip_fail(e, "fused forward launch");
     return ok();
   } catch (...) {
@@ -326,17 +387,17 @@ bool same_kernel(const dcn::KernelConfig& p, const dcn::KernelConfig& q) {
 }  // namespace
 
 dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, const void* mask,
-                              const void* packed_weight, size_t workspace_bytes,
-                              const void* bias, void* out, void* stream) {
+                              void* workspace, size_t workspace_bytes, const void* bias,
+                              void* out, void* stream) {
   return forward_band("dcn_forward_packed", plan, 0, plan ? plan->Ho : 0, x, offset, mask,
-                      packed_weight, workspace_bytes, bias, out, stream);
+                      workspace, workspace_bytes, bias, out, stream);
 }
 
 dcn_status dcn_forward_rows(dcn_plan plan, int32_t row0, int32_t rows, const void* x,
-                            const void* offset, const void* mask, const void* packed_weight,
+                            const void* offset, const void* mask, void* workspace,
                             size_t workspace_bytes, const void* bias, void* out,
                             void* stream) {
-  return forward_band("dcn_forward_rows", plan, row0, rows, x, offset, mask, packed_weight,
+  return forward_band("dcn_forward_rows", plan, row0, rows, x, offset, mask, workspace,
                       workspace_bytes, bias, out, stream);
 }
 

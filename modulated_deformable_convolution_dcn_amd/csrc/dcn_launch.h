@@ -36,6 +36,12 @@ struct FusedArgs {
   uint32_t offset_bytes;  // bytes of offset (< 2^31)
   uint32_t mask_bytes;    // bytes of mask (< 2^31; 0 when mask is NULL)
   int vec_store;       // NCHW: Ho*Wo % 4 == 0, so 4 consecutive pixels store as one 16-B write
+  // Split of the tap sum (32x32-per-wave kernel only; the others need nsplit 1):
+  // split s sums taps [s * kper, min(K, (s + 1) * kper)) into out + s * split_stride,
+  // without bias; a reduce adds the splits and the bias afterwards.
+  int nsplit;          // 1: the whole sum plus bias, straight into out
+  int kper;            // taps per split (K when nsplit is 1)
+  uint32_t split_stride;  // floats between consecutive splits' partial outputs
 };
 
 // Arguments of the fp32 backward kernels (dcn_backward.hip).
@@ -112,6 +118,10 @@ hipError_t launch_fused_wsk_multi(const KernelConfig& kc, const MultiArgs& m, hi
 // The 32-pixel x 32-channel-per-wave kernel (fp32, 64-wide output tiles).
 bool quad_supported(const KernelConfig& kc);
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+// out[i] = bias[o(i)] + sum over s < nsplit of part[s * stride + i], i < B*O*Ho*Wo,
+// summed in split order (deterministic); o(i) from the output layout.
+hipError_t launch_split_reduce(const float* part, int nsplit, uint32_t stride, const float* bias,
+                               float* out, int B, int O, int HoWo, int nhwc, hipStream_t s);
 hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
 
 // The wide bf16 kernel (128 pixels x 256 output channels per workgroup).

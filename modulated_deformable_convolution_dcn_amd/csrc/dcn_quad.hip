@@ -71,14 +71,22 @@ fused_quad_kernel(Src src) {
   // rows and the sixteen-row fragment reads both cover all banks.
   auto a_at = [](int r, int k) { return r * AST + 4 * (k ^ ((r >> 1) & 7)); };
 
+  // workgroup -> (image, pixel tile, tap split, output tile); the splits of
+  // one pixel tile are neighbours, so they share the XCD (and L2) that holds
+  // its input rows.
   const int otile = logical % a.n_otiles;
-  const int t2 = logical / a.n_otiles;
+  const int t1 = logical / a.n_otiles;
+  const int split = t1 % a.nsplit;
+  const int t2 = t1 / a.nsplit;
   const int tile = t2 % a.tiles_per_img;
   const int b = t2 / a.tiles_per_img;
   const int hw0 = tile * M + wh * PW;  // first pixel of this wave
-  const int NKB = a.K * a.nchunk;
+  // taps [k0, k0 + kn) of this split; kt below counts from k0
+  const int k0 = split * a.kper;
+  const int kn = min(a.kper, a.K - k0);
+  const int NKB = kn * a.nchunk;
   auto clampb = [&](int kb) { return kb < NKB ? kb : NKB - 1; };
-  auto clampt = [&](int kt) { return kt < a.K ? kt : a.K - 1; };
+  auto clampt = [&](int kt) { return kt < kn ? kt : kn - 1; };
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const bool has_mask = a.mask != nullptr;
@@ -86,7 +94,7 @@ fused_quad_kernel(Src src) {
   const __amdgpu_buffer_rsrc_t mskr =
       make_rsrc(has_mask ? a.mask : a.offset, has_mask ? a.mask_bytes : 0u);
   const float* wblocks = static_cast<const float*>(a.wpack) +
-                         (size_t)otile * a.K * a.nchunk * (CB * NO);
+                         ((size_t)otile * a.K + k0) * a.nchunk * (CB * NO);
   const uint32_t row_bytes = (uint32_t)a.C * 4;
 
   // ---- (a) coefficients: lane l -> pixel l & 31, corners 2(l>>5), 2(l>>5)+1
@@ -98,8 +106,9 @@ fused_quad_kernel(Src src) {
   const int c_wo = c_hw - c_ho * a.Wo;
   float c_dy[2], c_dx[2], c_mk[2];
   auto coef_load = [&](int kt, float& dy, float& dx, float& mk) {
-    const uint32_t ob = ((uint32_t)(b * 2 * a.K + 2 * kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
-    const uint32_t mb = ((uint32_t)(b * a.K + kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
+    const uint32_t ob =
+        ((uint32_t)(b * 2 * a.K + 2 * (k0 + kt)) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
+    const uint32_t mb = ((uint32_t)(b * a.K + k0 + kt) * (uint32_t)a.HoWo + (uint32_t)c_hw) * 4;
     dy = load_scalar<float>(offr, ob);
     dx = load_scalar<float>(offr, ob + (uint32_t)a.HoWo * 4);
     mk = load_scalar<float>(mskr, mb);
@@ -122,7 +131,7 @@ fused_quad_kernel(Src src) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     if (stage == 0) {
-      const int i = kt / a.kw, j = kt - (kt / a.kw) * a.kw;
+      const int i = (k0 + kt) / a.kw, j = (k0 + kt) - ((k0 + kt) / a.kw) * a.kw;
       const float py = __fadd_rn(c_gyb + (float)i, dy);
       const float px = __fadd_rn(c_gxb + (float)j, dx);
       cs.fy = floorf(py);
@@ -255,7 +264,7 @@ fused_quad_kernel(Src src) {
     const bool ok2 = chan(n2, cb2);
     const float* bsrc = b_src(n1);
     const int tc = (s + 3) / a.nchunk;
-    const bool coef_due = tc * a.nchunk == s + 3 && tc < a.K;
+    const bool coef_due = tc * a.nchunk == s + 3 && tc < kn;
     const int tl = clampt((s + 5) / a.nchunk);
     static_for<2>([&](auto MT) {
       constexpr int mt = decltype(MT)::value;
@@ -332,7 +341,8 @@ fused_quad_kernel(Src src) {
       *reinterpret_cast<f32x4*>(&red[(wave * NO + nt * 16 + rl) * RST + mt * 16 + g * 4]) =
           acc[mt][nt];
   __syncthreads();
-  const float* biasp = static_cast<const float*>(a.bias);
+  const float* biasp = static_cast<const float*>(a.bias);  // NULL for a split
+  float* const outp = a.out + (size_t)split * a.split_stride;
   const int base_hw = tile * M;
   if constexpr (!NHWC) {
     // thread -> (pixel half, output channel, run of 4 pixels)
@@ -348,7 +358,7 @@ fused_quad_kernel(Src src) {
       v += *reinterpret_cast<const f32x4*>(&red[((w0 + 1) * NO + col) * RST + r4 * 4]);
       v += biasp ? biasp[o] : 0.0f;
       const int hw = base_hw + h * PW + r4 * 4;
-      float* dst = a.out + ((size_t)b * a.O + o) * a.HoWo + hw;
+      float* dst = outp + ((size_t)b * a.O + o) * a.HoWo + hw;
       if (a.vec_store && hw + 3 < a.HoWo) {
         *reinterpret_cast<f32x4*>(dst) = v;
       } else {
@@ -367,7 +377,7 @@ fused_quad_kernel(Src src) {
       if (o >= a.O || hw >= a.HoWo) continue;
       const float v = red[(2 * h * NO + col) * RST + row] + red[((2 * h + 1) * NO + col) * RST + row] +
                       (biasp ? biasp[o] : 0.0f);
-      a.out[((size_t)b * a.HoWo + hw) * a.O + o] = v;
+      outp[((size_t)b * a.HoWo + hw) * a.O + o] = v;
     }
   }
 }
@@ -396,7 +406,62 @@ hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, int64_
 }  // namespace
 
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  return launch_quad_src(kc, a, a.C, (int64_t)a.B * kc.tiles_per_img * kc.n_otiles, s);
+  if (a.nsplit < 1 || a.kper < 1 || (int64_t)(a.nsplit - 1) * a.kper >= a.K)
+    return hipErrorInvalidValue;  // every split needs at least one tap
+  return launch_quad_src(kc, a, a.C,
+                         (int64_t)a.B * kc.tiles_per_img * a.nsplit * kc.n_otiles, s);
+}
+
+namespace {
+// Sum of the tap splits plus bias.  Thread -> 4 consecutive elements (16-B
+// loads and store when the count is a multiple of 4; the buffers are 16-B
+// aligned and the split stride is a multiple of 4 floats).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int nsplit, uint32_t stride,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ out, int64_t n,
+                                                           int O, int HoWo, int nhwc) {
+  const int64_t n4 = n / 4;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < (n + 3) / 4;
+       v += (int64_t)gridDim.x * 256) {
+    const int64_t i0 = v * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (v < n4) {
+      for (int s = 0; s < nsplit; ++s)
+        acc += *reinterpret_cast<const f32x4*>(part + (size_t)s * stride + i0);
+    } else {
+      for (int s = 0; s < nsplit; ++s)
+        for (int e = 0; e < 4; ++e)
+          if (i0 + e < n) acc[e] += part[(size_t)s * stride + i0 + e];
+    }
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        const int o = nhwc ? (int)(i % O) : (int)((i / HoWo) % O);
+        if (i < n) acc[e] += bias[o];
+      }
+    }
+    if (v < n4) {
+      *reinterpret_cast<f32x4*>(out + i0) = acc;
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n) out[i0 + e] = acc[e];
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_split_reduce(const float* part, int nsplit, uint32_t stride, const float* bias,
+                               float* out, int B, int O, int HoWo, int nhwc, hipStream_t s) {
+  const int64_t n = (int64_t)B * O * HoWo;
+  if (n <= 0) return hipSuccess;
+  if (nsplit < 1 || stride % 4 != 0 || (int64_t)stride < n) return hipErrorInvalidValue;
+  const int64_t want = ((n + 3) / 4 + 255) / 256;
+  const unsigned nblk = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(nblk), dim3(256), 0, s, part, nsplit, stride, bias,
+                     out, n, O, HoWo, nhwc);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {

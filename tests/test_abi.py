@@ -104,6 +104,29 @@ def test_output_size_and_workspace():
     assert (p2.Ho, p2.Wo) == (33, 40)
     p3 = Plan(Desc(1, 4, 8, 8, 4, 3, 3, 1, 1))
     assert p3.workspace_bytes == 9 * 16 * 16 * 4  # padded to a 16-channel block, 16 outputs
+    for p in (p, p2, p3):
+        assert p.packed_weight_bytes == p.workspace_bytes  # grids that fill the GPU: no split
+
+
+@pytest.mark.parametrize("shape,nsplit", [
+    ((1, 64, 256, 256, 64, 7, 7, 3, 3), 1),     # 1024 workgroups: no split
+    ((1, 64, 128, 128, 64, 7, 7, 3, 3), 2),     # 256 workgroups: two runs of taps
+    ((1, 64, 64, 64, 64, 7, 7, 3, 3), 4),       # 64 workgroups: four runs (13, 13, 13, 10)
+    ((1, 64, 20, 20, 64, 1, 3, 0, 1), 3),       # K = 3: at most one run per tap
+    ((1, 64, 20, 20, 64, 1, 1, 0, 0), 1),       # K = 1: nothing to split
+    ((2, 96, 90, 90, 48, 3, 3, 1, 1), 2),       # 2 images x 127 tiles = 254 workgroups
+])
+def test_tap_split_workspace(shape, nsplit):
+    """fp32 plans of 17..64 output channels whose grid would fill at most half
+    of the 512 resident workgroups split their taps; the scratch holds one
+    fp32 partial output per run (element count rounded up to 64)."""
+    B, C, H, W_, O, kh, kw, ph, pw = shape
+    p = Plan(Desc(B, C, H, W_, O, kh, kw, ph, pw))
+    K = kh * kw
+    assert p.packed_weight_bytes == ((K * -(-C // 64) * 64 * 64 * 4 + 255) // 256) * 256
+    n = B * O * p.Ho * p.Wo
+    scratch = 0 if nsplit == 1 else nsplit * (-(-n // 64) * 64) * 4
+    assert p.workspace_bytes == p.packed_weight_bytes + scratch
 
 
 def test_pointer_checks_fire_before_any_launch():
@@ -117,13 +140,15 @@ def test_pointer_checks_fire_before_any_launch():
     assert lib.dcn_forward_packed(h, fake, None, None, fake, ws, None, fake, None) == 1
     assert lib.dcn_forward_packed(h, fake, fake, None, fake, ws, None, None, None) == 1
     assert lib.dcn_forward_packed(h, fake, fake, None, None, ws, None, fake, None) == 8
-    assert lib.dcn_forward_packed(h, fake, fake, None, fake, ws - 1, None, fake, None) == 8
+    pw = p.packed_weight_bytes  # the least a forward accepts (no tap split)
+    assert pw < ws
+    assert lib.dcn_forward_packed(h, fake, fake, None, fake, pw - 1, None, fake, None) == 8
     odd = ctypes.c_void_p(0x10004)
     assert lib.dcn_forward_packed(h, odd, fake, None, fake, ws, None, fake, None) == 5
     assert lib.dcn_forward_packed(h, fake, ctypes.c_void_p(0x10002), None, fake, ws, None, fake,
                                   None) == 5
     assert lib.dcn_pack_weight(h, None, fake, ws, None) == 1
-    assert lib.dcn_pack_weight(h, fake, fake, ws - 256, None) == 8
+    assert lib.dcn_pack_weight(h, fake, fake, pw - 256, None) == 8
     assert lib.dcn_forward(None, fake, fake, None, fake, None, fake, fake, ws, None) == 1
     assert lib.dcn_debug_coords(h, None, fake, fake, None) == 1
     assert "required" in lib.dcn_last_error().decode()
@@ -165,7 +190,7 @@ def test_row_band_checks_fire_before_any_launch():
     assert call(3, 0, x=None) == 0   # empty band: nothing is read
     assert call(3, 4, x=None) == 1
     assert call(3, 4, pk=None) == 8
-    assert call(3, 4, w=ws - 1) == 8
+    assert call(3, 4, w=p.packed_weight_bytes - 1) == 8
     assert lib.dcn_forward_rows(None, 0, 1, fake, fake, None, fake, ws, None, fake, None) == 1
 
 

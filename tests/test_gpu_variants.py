@@ -114,7 +114,8 @@ def test_torchvision_order_nchw_input(name):
 
 # Multi-branch launches: several deformable convolutions on one input map
 # (page 2: four ASPP branches per BiRefNet decoder block).  Each branch is
-# checked against the oracle and bit for bit against its own single launch.
+# checked against the oracle and bit for bit against its own single launch
+# without a tap split (a multi-branch launch never splits: its grid is wide).
 MULTI_CASES = {
     # all four on the 32x32-per-wave kernel: one launch
     "aspp4_quad": [W["birefnet512_fp32"].scaled(H=30, W=26, kh=k, kw=k, ph=k // 2, pw=k // 2,
@@ -156,7 +157,7 @@ def test_multi_branch(name, optional):
         plans.append(plan)
         offs.append(dev["offset"])
         msks.append(dev["mask"])
-        packs.append(plan.pack_weight(dev["weight"]))
+        packs.append(plan.pack_weight(dev["weight"], split=False))
         biases.append(dev["bias"])
         devs.append(dev)
     x = devs[0]["x"]
