@@ -28,6 +28,8 @@
 //              add per weight element;
 //   bwd_bias   a per-channel sum of g.
 
+#include <type_traits>
+
 #include "dcn_device.h"
 #include "dcn_launch.h"
 
@@ -75,6 +77,21 @@ __device__ __forceinline__ TapTerms tap_terms(const BwdArgs& a, int b, int ho, i
   return r;
 }
 
+// Sum over each row of 16 lanes, the result in every lane of the row (DPP:
+// swap neighbours, swap pairs, mirror halves of 8, mirror the row).
+__device__ __forceinline__ float row16_sum(float v) {
+  auto dpp = [](float x, auto CTRL) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                           decltype(CTRL)::value, 0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw) {
   return a.nhwc_g ? a.gout[((size_t)b * a.HoWo + hw) * a.O + o]
                   : a.gout[((size_t)b * a.O + o) * a.HoWo + hw];
@@ -83,11 +100,12 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 }  // namespace
 
 // ---------------------------------------------------------------- data grads
-// LDS budget of the input-gradient window, per padded output count.
+// LDS budget of the input-gradient window, per padded output count (with the
+// g tile, the gs tile and the tables the kernel uses <= 160 KB of LDS).
 constexpr int bwd_window_floats(int OP) {
   return OP <= 16 ? 32768 : OP <= 64 ? 29696 : OP <= 128 ? 25600 : 16896;
 }
-constexpr int WSTR = 68;  // floats per window position: 64 channels + 4 (bank spread)
+constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 
 // One workgroup = an 8 x 8 block of output pixels of one image.  Its
 // sampling points cluster around the block, so the input gradient of the
@@ -95,18 +113,43 @@ constexpr int WSTR = 68;  // floats per window position: 64 channels + 4 (bank s
 // on every side) is accumulated in LDS with LDS atomics and flushed to
 // memory once per 64-channel chunk; corners outside the window (far
 // offsets) go straight to memory.  R < 0: no window.
+//
+// Per 64-channel chunk the taps run as a two-stage pipeline, one barrier
+// pair per tap: while the MFMAs form gs of tap k, wave 0 turns the offsets of
+// tap k + 1 (loaded a tap earlier) into the sampling tables; after the
+// barrier every thread issues the corner loads of tap k + 1 (and, for up to
+// 64 outputs, the weight fragments of tap k + 1) before it works on tap k
+// with the corners loaded one tap earlier.
+//
+// Tap k's work has two layouts.  The mask / offset sums need the corner
+// values: 16 lanes per pixel, 4 channels each (one 16-byte load per corner),
+// reduced over the 16 lanes.  The input-gradient scatter needs none: one
+// pixel per wave-step, lane = channel, so each LDS atomic instruction covers
+// one window position's 64 consecutive channels (no bank conflicts; a far
+// corner is one coalesced 256-byte atomic run).  The sums of tap k are
+// staged in LDS and written by one wave at the next tap.
 template <int OP>  // padded output channels: 16, 64, 128 or 256
 __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int tiles_x,
                                                        int tiles_per_img) {
   constexpr int GST = OP + GPAD;     // g tile row stride
   constexpr int SST = 64 + GPAD;     // gs tile row stride
+  constexpr bool WPRE = OP <= 64;    // next tap's weight fragments held in registers
+  constexpr int NQ = OP / 16;
   __shared__ __attribute__((aligned(16))) float Gs[TILE * GST];
   __shared__ __attribute__((aligned(16))) float gsT[TILE * SST];
-  __shared__ __attribute__((aligned(16))) float win[bwd_window_floats(OP)];
-  // per-tap table of the block's 64 sampling points (written by wave 0):
-  // {y0, x0, validity bits, pixel inside the output} and {ly, lx, mask}
-  __shared__ int4 Ti[TILE];
-  __shared__ f32x4 Tf[TILE];
+  // the window, then 64 floats that take the scatter's discarded adds
+  constexpr int SINK = bwd_window_floats(OP);
+  __shared__ __attribute__((aligned(16))) float win[SINK + 64];
+  // two sets of tables of the block's 64 sampling points (written by wave 0):
+  //   Ti {y0, x0, validity bits, pixel inside the output}, Tf {ly, lx, mask}
+  //   Si {window offset of corner (0,0), corner flags, image pixel of (0,0)},
+  //   Sf {mask x corner weight, 0 for an invalid corner}
+  // corner flags: bit q = in the window, bit 4 + q = valid but outside it
+  __shared__ int4 Ti[2][TILE];
+  __shared__ f32x4 Tf[2][TILE];
+  __shared__ int4 Si[2][TILE];
+  __shared__ f32x4 Sf[2][TILE];
+  __shared__ float red[2][3][TILE];  // mask, dy, dx sums of a tap
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -132,11 +175,13 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const int rl = lane & 15, g = lane >> 4;
-  const int sl = tid & 15;  // 4-channel slice of the 64-channel chunk
+  const int sl = tid & 15;  // 4-channel slice of the 64-channel chunk (sum layout)
   const int nwin = use_win ? WH * WW : 0;
-  // wave 0: the offsets / mask of the next tap, loaded one tap ahead
+
+  // wave 0: the offsets / mask of a tap, loaded a tap before its tables
   int t_hw = 0;
   const bool t_in = tid < TILE && px_hw(tid, t_hw);
+  const int t_ho = t_hw / a.Wo, t_wo = t_hw - (t_hw / a.Wo) * a.Wo;
   float n_dy = 0.f, n_dx = 0.f, n_m = 1.f;
   auto t_load = [&](int k) {
     if (!t_in) return;
@@ -145,37 +190,112 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
     n_dx = a.offset[ob + a.HoWo];
     n_m = a.mask ? a.mask[(size_t)(b * a.K + k) * a.HoWo + t_hw] : 1.0f;
   };
-  if (tid < TILE) t_load(0);
+  auto t_build = [&](int slot, int k) {  // tid < TILE
+    const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+    const TapPoint tp = tap_point(n_dy, n_dx, t_ho - a.ph + i, t_wo - a.pw + j, a.H, a.W);
+    const int y0 = (int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H);
+    const int x0 = (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W);
+    const uint32_t v4 = t_in ? tp.valid : 0u;
+    Ti[slot][tid] = make_int4(y0, x0, (int)v4, t_in ? 1 : 0);
+    Tf[slot][tid] = f32x4{tp.ly, tp.lx, n_m, 0.0f};
+    const float hy = 1.0f - tp.ly, hx = 1.0f - tp.lx;
+    const float wv[4] = {hy * hx, hy * tp.lx, tp.ly * hx, tp.ly * tp.lx};
+    f32x4 cf;
+    int flags = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = (v4 >> q) & 1u;
+      cf[q] = ok ? n_m * wv[q] : 0.0f;
+      const int wy = y0 + (q >> 1) - wy0, wx = x0 + (q & 1) - wx0;
+      const bool inwin = use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW;
+      if (ok) flags |= inwin ? (1 << q) : (16 << q);
+    }
+    Si[slot][tid] = make_int4(((y0 - wy0) * WW + (x0 - wx0)) * WSTR, flags,
+                              (b * a.H + y0) * a.W + x0, (y0 - wy0) + (x0 - wx0));
+    Sf[slot][tid] = cf;
+  };
+  // wave 1: the mask / offset gradients of tap k from the staged sums
+  auto sums_store = [&](int slot, int k) {
+    int hw;
+    if (!px_hw(lane, hw)) return;
+    if (a.gmask) atomic_add(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, red[slot][0][lane]);
+    if (a.goff) {
+      atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, red[slot][1][lane]);
+      atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, red[slot][2][lane]);
+    }
+  };
+
+  // corner values of the 4 sum passes x 4 corners, one buffer per table slot
+  u32x4 cv[2][4][4];
+  f32x4 bw[WPRE ? NQ : 1][4];
+  auto w_load = [&](int kb) {
+    if constexpr (WPRE) {
+      const float* wt = a.wt + (size_t)kb * OP * 64;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          bw[q][nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+    }
+  };
+
   for (int chunk = 0; chunk < a.nchunk; ++chunk) {
     for (int e = tid; e < nwin * WSTR; e += 256) win[e] = 0.0f;
     const int ch = chunk * 64 + 4 * sl;
-    const bool chan_ok = ch < a.C;
-    for (int k = 0; k < a.K; ++k) {
-      const int kb = k * a.nchunk + chunk;
-      __syncthreads();  // g tile / window zeroed; previous gs tile and table consumed
-      if (tid < TILE) {  // (0) the table of tap k, then the loads of the next tap
-        const int ho = t_hw / a.Wo, wo = t_hw - (t_hw / a.Wo) * a.Wo;
-        const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
-        const TapPoint tp = tap_point(n_dy, n_dx, ho - a.ph + i, wo - a.pw + j, a.H, a.W);
-        Ti[tid] = make_int4((int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H),
-                            (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W), (int)tp.valid,
-                            t_in ? 1 : 0);
-        Tf[tid] = f32x4{tp.ly, tp.lx, n_m, 0.0f};
-        t_load(k + 1 < a.K ? k + 1 : 0);
+    const bool chan_ok = ch < a.C;            // sum layout
+
+    auto c_issue = [&](auto SLOT) {  // corner loads of the tap in table SLOT
+      constexpr int S = decltype(SLOT)::value;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int4 ti = Ti[S][16 * p + (tid >> 4)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = chan_ok && ((ti.z >> q) & 1);
+          const int pix = (b * a.H + ti.x + (q >> 1)) * a.W + ti.y + (q & 1);
+          cv[S][p][q] = load16(xr, ok ? ((uint32_t)pix * (uint32_t)a.C + (uint32_t)ch) * 4u
+                                      : kNoCorner);
+        }
       }
+    };
+
+    // prologue: tables and corners of tap 0, offsets of tap 1, weights of tap 0
+    if (tid < TILE) {
+      t_load(0);
+      t_build(0, 0);
+      t_load(a.K > 1 ? 1 : 0);
+    }
+    __syncthreads();  // tables of tap 0 visible; window zeroed
+    c_issue(std::integral_constant<int, 0>{});
+    w_load(chunk);
+
+    auto step = [&](int k, auto PAR) {
+      constexpr int P = decltype(PAR)::value;  // k & 1: tables / corner buffer of tap k
+      const int kb = k * a.nchunk + chunk;
+      const bool more = k + 1 < a.K;
+      __syncthreads();  // step k-1 is done with gsT, tables P ^ 1 and its sums
+      if (wave == 0 && more) {  // (0) tables of tap k + 1, then the offsets of tap k + 2
+        t_build(P ^ 1, k + 1);
+        t_load(k + 2 < a.K ? k + 2 : 0);
+      }
+      if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
       // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows 16w..
       f32x4 acc[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const float* wt = a.wt + (size_t)kb * OP * 64;
 #pragma unroll 4
-      for (int q = 0; q < OP / 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const f32x4 af =
             *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + rl) * GST + 16 * q + 4 * g]);
         f32x4 bf[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          bf[nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+        for (int nt = 0; nt < 4; ++nt) {
+          if constexpr (WPRE)
+            bf[nt] = bw[q][nt];
+          else
+            bf[nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -188,82 +308,128 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           gsT[(16 * wave + 4 * g + r) * SST + 16 * nt + rl] = acc[nt][r];
-      __syncthreads();
+      __syncthreads();  // gsT and tables P ^ 1 visible
 
-      // (2) per (pixel, 4-channel slice): corners, input-gradient adds,
-      // mask / offset sums
-#pragma unroll 1
+      // (2) weights and corner loads of tap k + 1, then tap k's sums and scatter
+      if (more) {
+        w_load(kb + a.nchunk);
+        c_issue(std::integral_constant<int, P ^ 1>{});
+      }
+      // (2a) sums: pass p -> pixel 16p + tid / 16, 4 channels per lane
+#pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int px = 16 * p + (tid >> 4);
-        int hw;
-        const bool in = px_hw(px, hw);
-        float sm = 0.f, sdy = 0.f, sdx = 0.f, m = 0.f;
-        if (in) {
-          const int4 ti = Ti[px];
-          const f32x4 tf = Tf[px];
-          TapTerms t;
-          {
-            const float ly = tf[0], lx = tf[1], hy = 1.0f - ly, hx = 1.0f - lx;
-            const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
-            const float vy[4] = {-hx, -lx, hx, lx};
-            const float vx[4] = {-hy, hy, -ly, ly};
-            t.y0 = ti.x;
-            t.x0 = ti.y;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              t.ok[q] = (ti.z >> q) & 1;
-              t.w[q] = t.ok[q] ? wv[q] : 0.0f;
-              t.dwy[q] = t.ok[q] ? vy[q] : 0.0f;
-              t.dwx[q] = t.ok[q] ? vx[q] : 0.0f;
-              t.pix[q] = (b * a.H + ti.x + (q >> 1)) * a.W + ti.y + (q & 1);
-            }
-          }
-          m = tf[2];
+        const int4 ti = Ti[P][px];
+        const f32x4 tf = Tf[P][px];
+        float sm = 0.f, sdy = 0.f, sdx = 0.f;
+        if (ti.z != 0 && chan_ok) {
+          const float ly = tf[0], lx = tf[1], hy = 1.0f - ly, hx = 1.0f - lx;
+          const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
+          const float vy[4] = {-hx, -lx, hx, lx};
+          const float vx[4] = {-hy, hy, -ly, ly};
           const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
-          if (chan_ok) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              if (!t.ok[q]) continue;
-              const uint32_t off = ((uint32_t)t.pix[q] * (uint32_t)a.C + (uint32_t)ch) * 4u;
-              const f32x4 v = __builtin_bit_cast(f32x4, load16(xr, off));
-              const float cw = m * t.w[q];
-              const int wy = t.y0 + (q >> 1) - wy0, wx = t.x0 + (q & 1) - wx0;
-              if (use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW) {
-                float* dst = &win[(wy * WW + wx) * WSTR + 4 * sl];
+          for (int q = 0; q < 4; ++q) {
+            if (!((ti.z >> q) & 1)) continue;
+            const f32x4 v = __builtin_bit_cast(f32x4, cv[P][p][q]);
+            float t = gs[0] * v[0];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) atomicAdd(dst + e, gs[e] * cw);
-              } else {
-                float* dst = a.gx + (size_t)t.pix[q] * a.C + ch;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) atomic_add(dst + e, gs[e] * cw);
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                sm = __builtin_fmaf(gs[e] * t.w[q], v[e], sm);
-                sdy = __builtin_fmaf(gs[e] * t.dwy[q], v[e], sdy);
-                sdx = __builtin_fmaf(gs[e] * t.dwx[q], v[e], sdx);
-              }
-            }
+            for (int e = 1; e < 4; ++e) t = __builtin_fmaf(gs[e], v[e], t);
+            sm = __builtin_fmaf(wv[q], t, sm);
+            sdy = __builtin_fmaf(vy[q], t, sdy);
+            sdx = __builtin_fmaf(vx[q], t, sdx);
           }
         }
-        // sum over the 16 lanes of the pixel (lanes 16*(l/16) .. +15)
-#pragma unroll
-        for (int sh = 8; sh >= 1; sh >>= 1) {
-          sm += __shfl_xor(sm, sh, 16);
-          sdy += __shfl_xor(sdy, sh, 16);
-          sdx += __shfl_xor(sdx, sh, 16);
-        }
-        if (sl == 0 && in) {
-          if (a.gmask) atomic_add(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, sm);
-          if (a.goff) {
-            atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, m * sdy);
-            atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, m * sdx);
-          }
+        // sum over the 16 lanes of the pixel (one DPP row)
+        sm = row16_sum(sm);
+        sdy = row16_sum(sdy);
+        sdx = row16_sum(sdx);
+        if (sl == 0) {
+          red[P][0][px] = sm;
+          red[P][1][px] = tf[2] * sdy;
+          red[P][2][px] = tf[2] * sdx;
         }
       }
+      // (2b) scatter, lane = channel.  Window position (wy, wx) belongs to wave
+      // (wy + wx) mod 4, so no two waves ever update one position and the
+      // updates are plain LDS read-add-writes (float atomics cost far more).
+      // Each wave takes its corners in batches of 4: the batch's positions
+      // are wave-uniform, a repeated position is folded into its first
+      // occurrence, then 4 reads, the adds and 4 writes; the next batch's
+      // reads follow the writes in this wave's LDS order.  Far corners of the
+      // wave's 16 pixels go to memory with atomics.
+      {
+        const int4 si = Si[P][lane];  // lane = pixel
+        const f32x4 sf = Sf[P][lane];
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          // the corner weight as bits (a scalar first: taking the bits of a
+          // vector element directly reads element 0 with this compiler)
+          const float sfq = sf[q];
+          const int sfq_bits = __float_as_int(sfq);
+          constexpr int dq = (q >> 1) + (q & 1);
+          const int cwin = (q >> 1) * WW * WSTR + (q & 1) * WSTR;
+          const bool own = ((si.y >> q) & 1) && ((si.w + dq) & 3) == wave;
+          const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 4) == wave;
+          uint64_t m_own = __ballot(own);
+          uint64_t m_far = __ballot(far);
+          while (m_far) {
+            const int p = __builtin_ctzll(m_far);
+            m_far &= m_far - 1;
+            const int pix = __builtin_amdgcn_readlane(si.z, p) + (q >> 1) * a.W + (q & 1);
+            const float c = __int_as_float(__builtin_amdgcn_readlane(sfq_bits, p));
+            if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
+              atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
+          }
+          while (m_own) {
+            int pos[4], pp[4];
+            float cc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (m_own) {
+                const int p = __builtin_ctzll(m_own);
+                m_own &= m_own - 1;
+                pp[i] = p;
+                pos[i] = __builtin_amdgcn_readlane(si.x, p) + cwin;
+                cc[i] = __int_as_float(__builtin_amdgcn_readlane(sfq_bits, p));
+              } else {
+                pp[i] = 0;
+                pos[i] = SINK;
+                cc[i] = 0.0f;
+              }
+            }
+            // first occurrence of each position in the batch
+            const int t1 = pos[1] == pos[0] ? 0 : 1;
+            const int t2 = pos[2] == pos[0] ? 0 : pos[2] == pos[1] ? t1 : 2;
+            const int t3 = pos[3] == pos[0] ? 0 : pos[3] == pos[1] ? t1 : pos[3] == pos[2] ? t2 : 3;
+            const int at[4] = {pos[0], t1 == 1 ? pos[1] : SINK, t2 == 2 ? pos[2] : SINK,
+                               t3 == 3 ? pos[3] : SINK};
+            float t[4], w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = gsT[pp[i] * SST + lane] * cc[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = win[at[i] + lane];
+            // fold each repeat into its first occurrence (a repeat's own slot
+            // then lands in the sink)
+            if (t3 == 0) t[0] += t[3]; else if (t3 == 1) t[1] += t[3]; else if (t3 == 2) t[2] += t[3];
+            if (t2 == 0) t[0] += t[2]; else if (t2 == 1) t[1] += t[2];
+            if (t1 == 0) t[0] += t[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) win[at[i] + lane] = w[i] + t[i];
+          }
+        });
+      }
+    };
+    int k = 0;
+    for (; k + 1 < a.K; k += 2) {
+      step(k, std::integral_constant<int, 0>{});
+      step(k + 1, std::integral_constant<int, 1>{});
     }
-    // (3) flush the window's input gradient of this chunk
+    if (k < a.K) step(k, std::integral_constant<int, 0>{});
+
+    // (3) the last tap's sums, then flush the window's input gradient of this chunk
     __syncthreads();
+    if (wave == 1) sums_store((a.K - 1) & 1, a.K - 1);
     for (int e = tid; e < nwin * 64; e += 256) {
       const int pos = e >> 6, c = e & 63;
       const int y = wy0 + pos / WW, xx = wx0 + pos % WW;
@@ -271,7 +437,7 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
       if (v != 0.0f && y >= 0 && y < a.H && xx >= 0 && xx < a.W && chunk * 64 + c < a.C)
         atomic_add(a.gx + ((size_t)(b * a.H + y) * a.W + xx) * a.C + chunk * 64 + c, v);
     }
-    __syncthreads();  // flush done before the next chunk zeroes the window
+    __syncthreads();  // flush and sums done before the next chunk reuses window and tables
   }
 }
 
