@@ -101,9 +101,10 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 
 // ---------------------------------------------------------------- data grads
 // LDS budget of the input-gradient window, per padded output count (with the
-// g tile, the gs tile and the tables the kernel uses <= 160 KB of LDS).
+// g tile, the gs tile, the tables and the scatter lists the kernel uses
+// <= 160 KB of LDS).
 constexpr int bwd_window_floats(int OP) {
-  return OP <= 16 ? 32768 : OP <= 64 ? 29696 : OP <= 128 ? 25600 : 16896;
+  return OP <= 16 ? 32256 : OP <= 64 ? 29184 : OP <= 128 ? 25088 : 16384;
 }
 constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
   __shared__ int4 Si[2][TILE];
   __shared__ f32x4 Sf[2][TILE];
   __shared__ float red[2][3][TILE];  // mask, dy, dx sums of a tap
+  __shared__ int2 ilist[4][TILE];    // per wave: scatter items of one corner index
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -350,72 +352,75 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
           red[P][2][px] = tf[2] * sdx;
         }
       }
-      // (2b) scatter, lane = channel.  Window position (wy, wx) belongs to wave
-      // (wy + wx) mod 4, so no two waves ever update one position and the
-      // updates are plain LDS read-add-writes (float atomics cost far more).
-      // Each wave takes its corners in batches of 4: the batch's positions
-      // are wave-uniform, a repeated position is folded into its first
-      // occurrence, then 4 reads, the adds and 4 writes; the next batch's
-      // reads follow the writes in this wave's LDS order.  Far corners of the
-      // wave's 16 pixels go to memory with atomics.
+      // (2b) scatter.  Window position (wy, wx) belongs to wave (wy + wx) mod
+      // 4, so no two waves ever update one position and the updates are plain
+      // LDS read-add-writes (float atomics cost far more).  Per corner index
+      // the wave lists its positions (position, pixel, weight) in LDS, then
+      // takes them 4 at a time: 16 lanes per item, 4 channels per lane, one
+      // 16-byte read, 4 FMAs and one 16-byte write per lane.  A batch that
+      // names one position twice runs its items one after another with
+      // lane = channel; the next batch's reads follow this batch's writes in
+      // the wave's LDS order.  Far corners of the wave's 16 pixels go to
+      // memory with atomics.
       {
         const int4 si = Si[P][lane];  // lane = pixel
         const f32x4 sf = Sf[P][lane];
+        const int grp = lane >> 4, sub = lane & 15;
         static_for<4>([&](auto Q) {
           constexpr int q = decltype(Q)::value;
-          // the corner weight as bits (a scalar first: taking the bits of a
-          // vector element directly reads element 0 with this compiler)
-          const float sfq = sf[q];
-          const int sfq_bits = __float_as_int(sfq);
           constexpr int dq = (q >> 1) + (q & 1);
           const int cwin = (q >> 1) * WW * WSTR + (q & 1) * WSTR;
+          // the corner weight as a scalar first: taking the bits of a vector
+          // element directly reads element 0 with this compiler
+          const float sfq = sf[q];
           const bool own = ((si.y >> q) & 1) && ((si.w + dq) & 3) == wave;
           const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 4) == wave;
-          uint64_t m_own = __ballot(own);
           uint64_t m_far = __ballot(far);
           while (m_far) {
             const int p = __builtin_ctzll(m_far);
             m_far &= m_far - 1;
             const int pix = __builtin_amdgcn_readlane(si.z, p) + (q >> 1) * a.W + (q & 1);
-            const float c = __int_as_float(__builtin_amdgcn_readlane(sfq_bits, p));
+            const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
             if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
               atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
           }
-          while (m_own) {
-            int pos[4], pp[4];
-            float cc[4];
+          const uint64_t m_own = __ballot(own);
+          const int n = __builtin_popcountll(m_own);
+          if (own) {
+            const int idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_own >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m_own, 0));
+            ilist[wave][idx] = make_int2(((si.x + cwin) << 6) | lane, __float_as_int(sfq));
+          }
+          for (int j = 0; j < n; j += 4) {
+            const bool valid = j + grp < n;
+            const int2 it = ilist[wave][valid ? j + grp : 0];
+            const int pos = valid ? it.x >> 6 : SINK;
+            const int p = it.x & 63;
+            const float c = valid ? __int_as_float(it.y) : 0.0f;
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gsT[p * SST + 4 * sub]);
+            float* dst = &win[pos + 4 * sub];
+            // positions of the 4 items (wave-uniform): any repeat?
+            const int s0 = __builtin_amdgcn_readlane(pos, 0), s1 = __builtin_amdgcn_readlane(pos, 16);
+            const int s2 = __builtin_amdgcn_readlane(pos, 32), s3 = __builtin_amdgcn_readlane(pos, 48);
+            const bool rep = (s1 != SINK && s1 == s0) ||
+                             (s2 != SINK && (s2 == s0 || s2 == s1)) ||
+                             (s3 != SINK && (s3 == s0 || s3 == s1 || s3 == s2));
+            if (!rep) {
+              f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (m_own) {
-                const int p = __builtin_ctzll(m_own);
-                m_own &= m_own - 1;
-                pp[i] = p;
-                pos[i] = __builtin_amdgcn_readlane(si.x, p) + cwin;
-                cc[i] = __int_as_float(__builtin_amdgcn_readlane(sfq_bits, p));
-              } else {
-                pp[i] = 0;
-                pos[i] = SINK;
-                cc[i] = 0.0f;
+              for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4[e], c, w4[e]);
+              *reinterpret_cast<f32x4*>(dst) = w4;
+            } else {
+              // one item after another, lane = channel: each lane's own
+              // read-add-write sequence then orders the repeats
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int pi = __builtin_amdgcn_readlane(pos, 16 * i);
+                const int ppi = __builtin_amdgcn_readlane(p, 16 * i);
+                const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 16 * i));
+                win[pi + lane] = __builtin_fmaf(gsT[ppi * SST + lane], ci, win[pi + lane]);
               }
             }
-            // first occurrence of each position in the batch
-            const int t1 = pos[1] == pos[0] ? 0 : 1;
-            const int t2 = pos[2] == pos[0] ? 0 : pos[2] == pos[1] ? t1 : 2;
-            const int t3 = pos[3] == pos[0] ? 0 : pos[3] == pos[1] ? t1 : pos[3] == pos[2] ? t2 : 3;
-            const int at[4] = {pos[0], t1 == 1 ? pos[1] : SINK, t2 == 2 ? pos[2] : SINK,
-                               t3 == 3 ? pos[3] : SINK};
-            float t[4], w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] = gsT[pp[i] * SST + lane] * cc[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = win[at[i] + lane];
-            // fold each repeat into its first occurrence (a repeat's own slot
-            // then lands in the sink)
-            if (t3 == 0) t[0] += t[3]; else if (t3 == 1) t[1] += t[3]; else if (t3 == 2) t[2] += t[3];
-            if (t2 == 0) t[0] += t[2]; else if (t2 == 1) t[1] += t[2];
-            if (t1 == 0) t[0] += t[1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) win[at[i] + lane] = w[i] + t[i];
           }
         });
       }
