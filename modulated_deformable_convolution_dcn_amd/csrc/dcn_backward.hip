@@ -104,7 +104,7 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 // g tile, the gs tile, the tables and the scatter lists the kernel uses
 // <= 160 KB of LDS).
 constexpr int bwd_window_floats(int OP) {
-  return OP <= 16 ? 32256 : OP <= 64 ? 29184 : OP <= 128 ? 25088 : 16384;
+  return OP <= 16 ? 31744 : OP <= 64 ? 28672 : OP <= 128 ? 24576 : 15872;
 }
 constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 
@@ -130,11 +130,14 @@ constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 // corner is one coalesced 256-byte atomic run).  The sums of tap k are
 // staged in LDS and written by one wave at the next tap.
 template <int OP>  // padded output channels: 16, 64, 128 or 256
-__global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int tiles_x,
+__global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int tiles_x,
                                                        int tiles_per_img) {
   constexpr int GST = OP + GPAD;     // g tile row stride
   constexpr int SST = 64 + GPAD;     // gs tile row stride
   constexpr bool WPRE = OP <= 64;    // next tap's weight fragments held in registers
+  constexpr int NW = 8;              // waves: two per SIMD
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int NPASS = TILE * 16 / NT;  // sum passes (16 lanes per pixel)
   constexpr int NQ = OP / 16;
   __shared__ __attribute__((aligned(16))) float Gs[TILE * GST];
   __shared__ __attribute__((aligned(16))) float gsT[TILE * SST];
@@ -151,9 +154,10 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
   __shared__ int4 Si[2][TILE];
   __shared__ f32x4 Sf[2][TILE];
   __shared__ float red[2][3][TILE];  // mask, dy, dx sums of a tap
-  __shared__ int2 ilist[4][TILE];    // per wave: scatter items of one corner index
+  __shared__ int2 ilist[NW][TILE];   // per wave: scatter items of one corner index
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mr = wave & 3, mh = wave >> 2;  // MFMA: pixel rows 16 mr .., channels 32 mh ..
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int tile = logical % tiles_per_img, b = logical / tiles_per_img;
   const int ty = tile / tiles_x, tx = tile - (tile / tiles_x) * tiles_x;
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
   };
 
   // g tile [64 pixels][OP outputs], zero outside
-  for (int e = tid; e < TILE * OP; e += 256) {
+  for (int e = tid; e < TILE * OP; e += NT) {
     const int o = e / TILE, px = e % TILE;
     int hw;
     const bool in = px_hw(px, hw);
@@ -227,30 +231,31 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
     }
   };
 
-  // corner values of the 4 sum passes x 4 corners, one buffer per table slot
-  u32x4 cv[2][4][4];
-  f32x4 bw[WPRE ? NQ : 1][4];
+  // corner values of the sum passes x 4 corners, one buffer per table slot
+  u32x4 cv[2][NPASS][4];
+  f32x4 bw[WPRE ? NQ : 1][2];
   auto w_load = [&](int kb) {
     if constexpr (WPRE) {
       const float* wt = a.wt + (size_t)kb * OP * 64;
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          bw[q][nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+        for (int nt = 0; nt < 2; ++nt)
+          bw[q][nt] = *reinterpret_cast<const f32x4*>(
+              &wt[((4 * q + g) * 64 + 16 * (2 * mh + nt) + rl) * 4]);
     }
   };
 
   for (int chunk = 0; chunk < a.nchunk; ++chunk) {
-    for (int e = tid; e < nwin * WSTR; e += 256) win[e] = 0.0f;
+    for (int e = tid; e < nwin * WSTR; e += NT) win[e] = 0.0f;
     const int ch = chunk * 64 + 4 * sl;
     const bool chan_ok = ch < a.C;            // sum layout
 
     auto c_issue = [&](auto SLOT) {  // corner loads of the tap in table SLOT
       constexpr int S = decltype(SLOT)::value;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int4 ti = Ti[S][16 * p + (tid >> 4)];
+      for (int p = 0; p < NPASS; ++p) {
+        const int4 ti = Ti[S][(NT / 16) * p + (tid >> 4)];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bool ok = chan_ok && ((ti.z >> q) & 1);
@@ -281,35 +286,37 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
         t_load(k + 2 < a.K ? k + 2 : 0);
       }
       if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
-      // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows 16w..
-      f32x4 acc[4];
+      // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows
+      // 16 (w % 4) .., channels 32 (w / 4) ..
+      f32x4 acc[2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const float* wt = a.wt + (size_t)kb * OP * 64;
 #pragma unroll 4
       for (int q = 0; q < NQ; ++q) {
         const f32x4 af =
-            *reinterpret_cast<const f32x4*>(&Gs[(16 * wave + rl) * GST + 16 * q + 4 * g]);
-        f32x4 bf[4];
+            *reinterpret_cast<const f32x4*>(&Gs[(16 * mr + rl) * GST + 16 * q + 4 * g]);
+        f32x4 bf[2];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
           if constexpr (WPRE)
             bf[nt] = bw[q][nt];
           else
-            bf[nt] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * nt + rl) * 4]);
+            bf[nt] = *reinterpret_cast<const f32x4*>(
+                &wt[((4 * q + g) * 64 + 16 * (2 * mh + nt) + rl) * 4]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
+          for (int nt = 0; nt < 2; ++nt)
             acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[nt][e], acc[nt], 0, 0, 0);
       }
       // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r, column l % 16
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gsT[(16 * wave + 4 * g + r) * SST + 16 * nt + rl] = acc[nt][r];
+          gsT[(16 * mr + 4 * g + r) * SST + 16 * (2 * mh + nt) + rl] = acc[nt][r];
       __syncthreads();  // gsT and tables P ^ 1 visible
 
       // (2) weights and corner loads of tap k + 1, then tap k's sums and scatter
@@ -317,10 +324,10 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
         w_load(kb + a.nchunk);
         c_issue(std::integral_constant<int, P ^ 1>{});
       }
-      // (2a) sums: pass p -> pixel 16p + tid / 16, 4 channels per lane
+      // (2a) sums: pass p -> pixel (NT / 16) p + tid / 16, 4 channels per lane
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int px = 16 * p + (tid >> 4);
+      for (int p = 0; p < NPASS; ++p) {
+        const int px = (NT / 16) * p + (tid >> 4);
         const int4 ti = Ti[P][px];
         const f32x4 tf = Tf[P][px];
         float sm = 0.f, sdy = 0.f, sdx = 0.f;
@@ -353,14 +360,14 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
         }
       }
       // (2b) scatter.  Window position (wy, wx) belongs to wave (wy + wx) mod
-      // 4, so no two waves ever update one position and the updates are plain
+      // 8, so no two waves ever update one position and the updates are plain
       // LDS read-add-writes (float atomics cost far more).  Per corner index
       // the wave lists its positions (position, pixel, weight) in LDS, then
       // takes them 4 at a time: 16 lanes per item, 4 channels per lane, one
       // 16-byte read, 4 FMAs and one 16-byte write per lane.  A batch that
       // names one position twice runs its items one after another with
       // lane = channel; the next batch's reads follow this batch's writes in
-      // the wave's LDS order.  Far corners of the wave's 16 pixels go to
+      // the wave's LDS order.  Far corners of the wave's 8 pixels go to
       // memory with atomics.
       {
         const int4 si = Si[P][lane];  // lane = pixel
@@ -373,8 +380,8 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
           // the corner weight as a scalar first: taking the bits of a vector
           // element directly reads element 0 with this compiler
           const float sfq = sf[q];
-          const bool own = ((si.y >> q) & 1) && ((si.w + dq) & 3) == wave;
-          const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 4) == wave;
+          const bool own = ((si.y >> q) & 1) && ((si.w + dq) & (NW - 1)) == wave;
+          const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 3) == wave;
           uint64_t m_far = __ballot(far);
           while (m_far) {
             const int p = __builtin_ctzll(m_far);
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(256) void bwd_data_kernel(BwdArgs a, int R, int til
     // (3) the last tap's sums, then flush the window's input gradient of this chunk
     __syncthreads();
     if (wave == 1) sums_store((a.K - 1) & 1, a.K - 1);
-    for (int e = tid; e < nwin * 64; e += 256) {
+    for (int e = tid; e < nwin * 64; e += NT) {
       const int pos = e >> 6, c = e & 63;
       const int y = wy0 + pos / WW, xx = wx0 + pos % WW;
       const float v = win[pos * WSTR + c];
@@ -617,7 +624,7 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     int R = -1;
     for (int r = 0; r <= 8; ++r)
       if ((int64_t)(8 + a.kh + 2 * r) * (8 + a.kw + 2 * r) * WSTR <= budget) R = r;
-    const dim3 grid((unsigned)nblk), block(256);
+    const dim3 grid((unsigned)nblk), block(512);
     switch (OP) {
       case 16: hipLaunchKernelGGL(bwd_data_kernel<16>, grid, block, 0, s, a, R, tiles_x, tiles); break;
       case 64: hipLaunchKernelGGL(bwd_data_kernel<64>, grid, block, 0, s, a, R, tiles_x, tiles); break;
