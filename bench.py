@@ -32,14 +32,29 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_DIR = os.path.join(ROOT, "modulated_deformable_convolution_dcn_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over every kernel source and internal header (sorted by name)."""
+# The sources each workload's forward kernel is built from (the kernel, its
+# device helpers and argument structs, and the host code that sizes and
+# launches it); a traffic record counts only while these are unchanged.
+_QUAD = ("dcn_quad.hip", "dcn_device.h", "dcn_launch.h", "dcn_api.cpp")
+KERNEL_SOURCES = {
+    "birefnet512_fp32": _QUAD,
+    "birefnet1024_fp32": _QUAD,
+    "detection_bf16": ("dcn_bf16.hip", "dcn_device.h", "dcn_launch.h", "dcn_api.cpp"),
+    "edge_stress_fp32": ("dcn_wsk.hip", "dcn_device.h", "dcn_launch.h", "dcn_api.cpp"),
+}
+
+
+def kernel_source_hash(workload: str = None) -> str:
+    """sha256 over the workload's kernel sources (every kernel source and
+    internal header when the workload has no entry), sorted by name."""
+    names = KERNEL_SOURCES.get(workload)
+    if names is None:
+        names = [n for n in os.listdir(KERNEL_DIR) if n.endswith((".hip", ".h", ".cpp"))]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_DIR)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(KERNEL_DIR, name), "rb") as fh:
-                h.update(fh.read())
+    for name in sorted(names):
+        h.update(name.encode())
+        with open(os.path.join(KERNEL_DIR, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -51,7 +66,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(workload):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -101,7 +116,7 @@ def summarize_traffic(pmc_dir: str, workload: str, copy_mib: int) -> dict:
         "traffic_read_bytes_per_launch": round(fk * 1024 * fs),
         "traffic_write_bytes_per_launch": round(wk * 1024 * ws),
         "traffic_bytes_per_launch": round(fk * 1024 * fs + wk * 1024 * ws),
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(workload),
     }
 
 
