@@ -538,19 +538,242 @@ __global__ __launch_bounds__(256) void bwd_weight_kernel(BwdArgs a, int tiles_pe
   }
 }
 
-// ---------------------------------------------------------------- bias grad
-__global__ __launch_bounds__(256) void bwd_bias_kernel(BwdArgs a) {
-  __shared__ float red[256];
-  const int o = blockIdx.x % a.O, b = blockIdx.x / a.O;
-  float s = 0.f;
-  for (int hw = threadIdx.x; hw < a.HoWo; hw += 256) s += gout_at(a, b, o, hw);
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
+// Weight gradient, wave-private pipeline (fp32, up to 64 outputs).
+// dW[o, c, k] = sum over pixels of g[px, o] * s[px, k, c], s the modulated
+// sample of the forward.  One workgroup per (tap, chunk, image, run of
+// 64-pixel tiles); wave w owns pixels [16w, 16w + 16) of every tile and
+// accumulates dW[all o][chunk's 64 c] over them in registers, so the main
+// loop has no barrier: per tile it blends its 16 samples x 64 channels
+// (corners loaded one tile ahead, 16 lanes per pixel, one 16-byte load per
+// corner) into a private transposed tile s[c][px] in LDS, then runs
+// 4 x NTO x 4 MFMAs: A = g^T fragments (4 consecutive pixels of one output,
+// one 16-byte load from an NCHW gradient), B = s^T fragments (one 16-byte
+// LDS read).  The four waves' partial sums meet in LDS once per run, then one
+// atomic add per weight element.
+template <int NTO, bool GV>  // 16-output tiles (OP / 16: 1 or 4); GV: NCHW g, Ho*Wo % 4 == 0
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
+  constexpr int OP = 16 * NTO;
+  constexpr int SST = 20;                       // s^T row: 16 pixels + 4 (bank spread)
+  constexpr int ST_FLOATS = 64 * SST;           // one wave's s^T tile
+  constexpr int RST = 64 + 4;                   // epilogue row: 64 channels + 4
+  constexpr int LOOP_BYTES = 4 * (ST_FLOATS * 4 + 2 * 16 * 32);
+  constexpr int RED_BYTES = 4 * OP * RST * 4;
+  constexpr int SMEM = LOOP_BYTES > RED_BYTES ? LOOP_BYTES : RED_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* const sT = reinterpret_cast<float*>(smem) + wave * ST_FLOATS;
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * ST_FLOATS * 4) + wave * 32;  // [2][16]
+  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * ST_FLOATS * 4 + 4 * 32 * 16) + wave * 32;
+  float* const red = reinterpret_cast<float*>(smem);  // [wave][o][RST]
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int run = logical % runs_per_img;
+  const int t2 = logical / runs_per_img;
+  const int b = t2 % a.B;
+  const int kb = t2 / a.B;
+  const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
+  const int ki = k / a.kw, kj = k - ki * a.kw;
+  const int t_begin = run * tiles_per_run;
+  const int t_end = min(t_begin + tiles_per_run, a.tiles_per_img);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const uint32_t row_bytes = (uint32_t)a.C * 4;
+
+  // ---- table of one tile: lanes 0..15 -> pixel 16 wave + lane (all lanes
+  // load, so every wave issues the same memory operations)
+  const int tl = lane & 15;
+  float n_dy = 0.f, n_dx = 0.f, n_m = 0.f;
+  auto t_load = [&](int tile) {
+    const int hw = tile * 64 + 16 * wave + tl;
+    const int hc = hw < a.HoWo ? hw : a.HoWo - 1;
+    const size_t ob = (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hc;
+    n_dy = a.offset[ob];
+    n_dx = a.offset[ob + a.HoWo];
+    n_m = hw < a.HoWo ? (a.mask ? a.mask[(size_t)(b * a.K + k) * a.HoWo + hc] : 1.0f) : 0.0f;
+  };
+  auto t_build = [&](int slot, int tile) {
+    const int hw = tile * 64 + 16 * wave + tl;
+    const int ho = hw / a.Wo, wo = hw - (hw / a.Wo) * a.Wo;
+    const TapPoint tp = tap_point(n_dy, n_dx, ho - a.ph + ki, wo - a.pw + kj, a.H, a.W);
+    const float hy = 1.0f - tp.ly, hx = 1.0f - tp.lx;
+    const float wv[4] = {hy * hx, hy * tp.lx, tp.ly * hx, tp.ly * tp.lx};
+    const int y0 = (int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H);
+    const int x0 = (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W);
+    f32x4 w4;
+    u32x4 o4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = ((tp.valid >> q) & 1u) && n_m != 0.0f;
+      w4[q] = ok ? n_m * wv[q] : 0.0f;
+      const uint32_t pix = (uint32_t)((b * a.H + y0 + (q >> 1)) * a.W + x0 + (q & 1));
+      o4[q] = ok ? pix * row_bytes : kNoCorner;
+    }
+    if (lane < 16) {
+      Cw[slot * 16 + tl] = w4;
+      Co[slot * 16 + tl] = o4;
+    }
+  };
+
+  // ---- corners: pass p -> pixel 4p + lane / 16, channels 4 (lane % 16) ..
+  const int sl = lane & 15, pq = lane >> 4;
+  const uint32_t cbyte = (uint32_t)(chunk * 64 + 4 * sl) * 4;
+  const bool chan_ok = chunk * 64 + 4 * sl < a.C;
+  u32x4 cv[4][4];
+  auto c_issue = [&](int slot, int p) {
+    const u32x4 o4 = Co[slot * 16 + 4 * p + pq];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cv[p][q] = load16(xr, chan_ok ? o4[q] + cbyte : kNoCorner);
+  };
+  // s^T[c][px]: 16-byte chunk (px / 4) of row c stored at chunk (px / 4) ^ ((c / 4) & 3),
+  // so a pass's 64 single-float writes and the fragment reads both spread over the banks
+  auto st_at = [](int c, int px) { return c * SST + 4 * ((px >> 2) ^ ((c >> 2) & 3)) + (px & 3); };
+  auto blend = [&](int slot, int p) {
+    const f32x4 w4 = Cw[slot * 16 + 4 * p + pq];
+    f32x4 sv = __builtin_bit_cast(f32x4, cv[p][0]) * w4[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      const f32x4 v = __builtin_bit_cast(f32x4, cv[p][q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(w4[q], v[e], sv[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[st_at(4 * sl + e, 4 * p + pq)] = sv[e];
+  };
+
+  // ---- g^T fragments: lane -> output 16t + lane % 16, pixels 4 (lane / 16) ..
+  const int rl = lane & 15, g = lane >> 4;
+  f32x4 gf[NTO];  // of the current tile; the next tile's are loaded after its MFMAs
+  auto g_load = [&](int tile) {
+    const int hw = tile * 64 + 16 * wave + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NTO; ++t) {
+      const int o = 16 * t + rl;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (o < a.O) {
+        if constexpr (GV) {
+          if (hw < a.HoWo)
+            v = *reinterpret_cast<const f32x4*>(a.gout + ((size_t)b * a.O + o) * a.HoWo + hw);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (hw + e < a.HoWo) v[e] = gout_at(a, b, o, hw + e);
+        }
+      }
+      gf[t] = v;
+    }
+  };
+
+  f32x4 acc[NTO][4];
+#pragma unroll
+  for (int t = 0; t < NTO; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int tile, auto PAR) {
+    constexpr int P = decltype(PAR)::value;  // slot / buffer of this tile
+    const bool more = tile + 1 < t_end;
+    if (more) {
+      t_build(P ^ 1, tile + 1);
+      t_load(tile + 2 < t_end ? tile + 2 : tile + 1);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      blend(P, p);
+      if (more) c_issue(P ^ 1, p);
+    }
+    // dW[o][c] += sum over the wave's 16 pixels: 4 k-steps of 4 pixels
+    f32x4 bf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 16 * u + rl;
+      bf[u] = *reinterpret_cast<const f32x4*>(&sT[c * SST + 4 * (g ^ ((c >> 2) & 3))]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int t = 0; t < NTO; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(gf[t][e], bf[u][e], acc[t][u], 0, 0, 0);
+    if (more) g_load(tile + 1);
+  };
+
+  if (t_begin < t_end) {
+    t_load(t_begin);
+    t_build(0, t_begin);
+    t_load(t_begin + 1 < t_end ? t_begin + 1 : t_begin);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c_issue(0, p);
+    g_load(t_begin);
+    int tile = t_begin;
+    for (; tile + 1 < t_end; tile += 2) {
+      step(tile, std::integral_constant<int, 0>{});
+      step(tile + 1, std::integral_constant<int, 1>{});
+    }
+    if (tile < t_end) step(tile, std::integral_constant<int, 0>{});
   }
-  if (threadIdx.x == 0) atomic_add(a.gb + o, red[0]);
+
+  // ---- the four waves' partial sums, then one atomic add per element
+  __syncthreads();  // every wave is done with its s^T tile and tables
+  // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r (output), column l % 16 (channel)
+#pragma unroll
+  for (int t = 0; t < NTO; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(wave * OP + 16 * t + 4 * g + r) * RST + 16 * u + rl] = acc[t][u][r];
+  __syncthreads();
+  for (int e = tid; e < OP * 64; e += 256) {
+    const int o = e >> 6, c = e & 63;
+    const int cc = chunk * 64 + c;
+    if (o >= a.O || cc >= a.C) continue;
+    const float v = red[(0 * OP + o) * RST + c] + red[(1 * OP + o) * RST + c] +
+                    red[(2 * OP + o) * RST + c] + red[(3 * OP + o) * RST + c];
+    atomic_add(a.gw + (((size_t)o * a.C + cc) * a.kh + ki) * a.kw + kj, v);
+  }
+}
+
+// ---------------------------------------------------------------- bias grad
+// dL/dbias[o] = sum of g over images and pixels.  NCHW g: one workgroup per
+// (output, image, pixel range), threads along the contiguous pixels, a tree
+// sum in LDS, one atomic add.  NHWC g: one workgroup per (image, pixel
+// range), thread t -> output t % 64 of rows t / 64, 4 rows ..., per-output
+// sums in LDS, one atomic add per output.
+constexpr int kBiasPixels = 4096;  // pixels per workgroup
+__global__ __launch_bounds__(256) void bwd_bias_kernel(BwdArgs a, int nsplit) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  if (!a.nhwc_g) {
+    const int split = blockIdx.x % nsplit, t2 = blockIdx.x / nsplit;
+    const int o = t2 % a.O, b = t2 / a.O;
+    const int h0 = split * kBiasPixels, h1 = min(h0 + kBiasPixels, a.HoWo);
+    const float* src = a.gout + ((size_t)b * a.O + o) * a.HoWo;
+    float s = 0.f;
+    for (int hw = h0 + tid; hw < h1; hw += 256) s += src[hw];
+    red[tid] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) atomic_add(a.gb + o, red[0]);
+  } else {
+    const int split = blockIdx.x % nsplit, b = blockIdx.x / nsplit;
+    const int h0 = split * kBiasPixels, h1 = min(h0 + kBiasPixels, a.HoWo);
+    for (int o0 = 0; o0 < a.O; o0 += 64) {
+      const int o = o0 + (tid & 63);
+      float s = 0.f;
+      if (o < a.O)
+        for (int hw = h0 + (tid >> 6); hw < h1; hw += 4)
+          s += a.gout[((size_t)b * a.HoWo + hw) * a.O + o];
+      red[tid] = s;
+      __syncthreads();
+      if (tid < 64 && o < a.O) atomic_add(a.gb + o, red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]);
+      __syncthreads();
+    }
+  }
 }
 
 // ---------------------------------------------------------------- helpers
@@ -634,9 +857,12 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.gw) {
-    // runs of pixel tiles: about 2048 workgroups in all
+    // runs of pixel tiles.  The wave-private kernel (O <= 64) holds two
+    // workgroups per CU: at most 512 workgroups, so the grid is one round
+    // and each run's closing reduction is spread over many tiles.  The
+    // other: about 2048 workgroups.
     const int64_t per_run_units = (int64_t)a.K * a.nchunk * a.B;
-    int64_t runs = (2048 + per_run_units - 1) / per_run_units;
+    int64_t runs = OP <= 64 ? 512 / per_run_units : (2048 + per_run_units - 1) / per_run_units;
     if (runs > a.tiles_per_img) runs = a.tiles_per_img;
     if (runs < 1) runs = 1;
     const int tiles_per_run = (int)((a.tiles_per_img + runs - 1) / runs);
@@ -644,16 +870,26 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     const int64_t g = per_run_units * runs_per_img;
     if (g > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)g), block(256);
+    const bool gv = !a.nhwc_g && a.HoWo % 4 == 0;
+#define DCN_W2(NTO)                                                                         \
+  if (gv) hipLaunchKernelGGL((bwd_weight2_kernel<NTO, true>), grid, block, 0, s, a,         \
+                             tiles_per_run, runs_per_img);                                  \
+  else hipLaunchKernelGGL((bwd_weight2_kernel<NTO, false>), grid, block, 0, s, a,           \
+                          tiles_per_run, runs_per_img)
     switch (OP) {
-      case 16: hipLaunchKernelGGL(bwd_weight_kernel<1>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
-      case 64: hipLaunchKernelGGL(bwd_weight_kernel<4>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
+      case 16: DCN_W2(1); break;
+      case 64: DCN_W2(4); break;
       case 128: hipLaunchKernelGGL(bwd_weight_kernel<8>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
       default: hipLaunchKernelGGL(bwd_weight_kernel<16>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
     }
+#undef DCN_W2
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.gb) {
-    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(a.O * a.B)), dim3(256), 0, s, a);
+    const int nsplit = (a.HoWo + kBiasPixels - 1) / kBiasPixels;
+    const int64_t nb = (a.nhwc_g ? (int64_t)a.B : (int64_t)a.B * a.O) * nsplit;
+    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)nb), dim3(256), 0, s, a, nsplit);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
