@@ -36,12 +36,16 @@ constexpr int TPP = 256 / NPAIR;  // coefficient threads per pair
 
 __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
   constexpr int MAXLK = kMsdaMaxLevels * kMsdaMaxPoints;
-  __shared__ f32x4 Cw[NPAIR * MAXLK];
-  __shared__ u32x4 Co[NPAIR * MAXLK];
+  // the table, sized by the launch for this problem's L * K points per pair
+  // (a smaller table leaves room for more workgroups per CU):
+  // Cw [NPAIR * LK] corner weights, then Co [NPAIR * LK] corner byte offsets
+  extern __shared__ __attribute__((aligned(16))) char msda_smem[];
   __shared__ int lv[kMsdaMaxLevels][3];  // H, W, start
 
   const int tid = threadIdx.x;
   const int LK = a.L * a.K;
+  f32x4* const Cw = reinterpret_cast<f32x4*>(msda_smem);
+  u32x4* const Co = reinterpret_cast<u32x4*>(msda_smem + (size_t)NPAIR * LK * 16);
   if (tid < a.L) {
     lv[tid][0] = a.H[tid];
     lv[tid][1] = a.W[tid];
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
           }
         }
       }
-      Cw[pl * MAXLK + e] = w4;
-      Co[pl * MAXLK + e] = o4;
+      Cw[pl * LK + e] = w4;
+      Co[pl * LK + e] = o4;
     }
   }
   __syncthreads();
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
       f32x4 w[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 o = Co[pl * MAXLK + e + u];
-        w[u] = Cw[pl * MAXLK + e + u];
+        const u32x4 o = Co[pl * LK + e + u];
+        w[u] = Cw[pl * LK + e + u];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[u][q] = load16(vr, o[q] + lb);  // kNoCorner + lb stays outside
       }
@@ -145,8 +149,8 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
         }
     }
     for (; e < LK; ++e) {
-      const u32x4 o = Co[pl * MAXLK + e];
-      const f32x4 w = Cw[pl * MAXLK + e];
+      const u32x4 o = Co[pl * LK + e];
+      const f32x4 w = Cw[pl * LK + e];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 f = __builtin_bit_cast(f32x4, load16(vr, o[q] + lb));
@@ -162,7 +166,9 @@ hipError_t launch_msda(const MsdaArgs& a, hipStream_t s) {
   const int64_t nblk = (a.npairs + NPAIR - 1) / NPAIR;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(msda_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a);
+  const int LK = a.L * a.K;
+  if (LK < 1 || LK > kMsdaMaxLevels * kMsdaMaxPoints) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(msda_kernel, dim3((unsigned)nblk), dim3(256), (size_t)NPAIR * LK * 32, s, a);
   return hipGetLastError();
 }
 
