@@ -192,9 +192,17 @@ def cpu_baseline(spec, d, seconds: float):
     t = time.perf_counter()
     oracle.forward(s, *args, pixels=pix, nthreads=cores, with_norm=False)
     dt = time.perf_counter() - t
+    # the same oracle on one thread, over a short evenly spaced sample
+    n1 = int(min(P, max(64, rate / cores * min(seconds, 5.0))))
+    pix1 = np.linspace(0, P - 1, num=n1).astype(np.int64)
+    t = time.perf_counter()
+    oracle.forward(s, *args, pixels=pix1, nthreads=1, with_norm=False)
+    dt1 = time.perf_counter() - t
     return {"value": n / dt, "unit": "px/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d output pixels (evenly spaced, all %d output channels), %.1f s"
-                      % (n, P, spec.O, dt)}
+                      % (n, P, spec.O, dt),
+            "one_thread": {"value": n1 / dt1, "unit": "px/s",
+                           "sample": "%d output pixels, %.1f s" % (n1, dt1)}}
 
 
 def copy_calibration(mib: int, reps: int) -> None:
