@@ -161,7 +161,10 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int tile = logical % tiles_per_img, b = logical / tiles_per_img;
   const int ty = tile / tiles_x, tx = tile - (tile / tiles_x) * tiles_x;
-  const bool use_win = R >= 0;
+  // the input gradient is optional: without it there is no window, no
+  // scatter and no flush (only the mask / offset sums run)
+  const bool want_gx = a.gx != nullptr;
+  const bool use_win = R >= 0 && want_gx;
   const int WH = 8 + a.kh + 2 * R, WW = 8 + a.kw + 2 * R;
   const int wy0 = 8 * ty - a.ph - R, wx0 = 8 * tx - a.pw - R;
   // pixel px of the block -> output (8ty + px / 8, 8tx + px % 8)
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       // lane = channel; the next batch's reads follow this batch's writes in
       // the wave's LDS order.  Far corners of the wave's 8 pixels go to
       // memory with atomics.
-      {
+      if (want_gx) {
         const int4 si = Si[P][lane];  // lane = pixel
         const f32x4 sf = Sf[P][lane];
         const int grp = lane >> 4, sub = lane & 15;

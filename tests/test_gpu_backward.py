@@ -121,3 +121,19 @@ def test_backward_birefnet512_full_size():
     got = _run(spec, d, gout, "nchw")
     for k in ("x", "offset", "mask", "weight", "bias"):
         _check("full grad_%s" % k, got[k], ref[k], norm[k])
+
+
+@pytest.mark.parametrize("want", [("offset", "mask"), ("offset",), ("mask", "bias"), ("x",)])
+def test_backward_partial_outputs_without_grad_x(want):
+    """Offset / mask gradients without the input gradient: the data kernel
+    runs its sums but no input-gradient scatter (there is no grad_x buffer)."""
+    spec = CASES["c64_o64_k7"].scaled(H=13, W=15)
+    d = synth.make_inputs(spec)
+    gout = _grad_out(spec, 31)
+    ref, norm = oracle.backward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                                gout)
+    print("case partial", want, flush=True)
+    got = _run(spec, d, gout, "nchw", want=want)
+    assert set(got) == set(want)
+    for k in want:
+        _check("partial %s grad_%s" % ("+".join(want), k), got[k], ref[k], norm[k])
