@@ -258,6 +258,23 @@ dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* l
 dcn_status dcn_nchw_to_nhwc(const void* src, void* dst, int32_t batch, int32_t channels,
                             int32_t height, int32_t width, int32_t dtype, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the whole
+ * forward of dcn_forward without a caller workspace.  The packed weight (and,
+ * when it fits, the tap split's partial sums) live in a static device array of
+ * DCN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; the call itself allocates nothing.  Arguments,
+ * layouts and errors as for dcn_forward; DCN_E_UNSUPPORTED when the plan's
+ * packed weight is larger than the array.  Every call on one GPU uses that
+ * GPU's one array, so calls that may overlap in time on one GPU (different
+ * streams, or different host threads) race and must be serialised by the
+ * caller; calls on one stream are ordered and safe.  The first call on a
+ * device resolves the array's address there (a host-side runtime query). */
+#define DCN_NOALLOC_SCRATCH_BYTES (32u << 20)
+dcn_status dcn_forward_noalloc(dcn_plan plan, const void* x, const void* offset,
+                               const void* mask, const void* weight, const void* bias,
+                               void* out, void* stream);
+
 /* Test hook, not on the timed path: the sampling-corner stage alone, from
  * the same device function the fused kernel uses.  For every (b, k, ho, wo)
  * it writes y0x0[2e], y0x0[2e+1] = floor of the fp32 sampling row / column

@@ -8,13 +8,14 @@
 
 #include "dcn.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <new>
 
 #include "dcn_launch.h"
@@ -663,6 +664,66 @@ dcn_status dcn_forward(dcn_plan plan, const void* x, const void* offset, const v
   if (s != DCN_OK) return s;
   return dcn_forward_packed(plan, x, offset, mask, workspace, workspace_bytes, bias, out,
                             stream);
+}
+
+namespace {
+
+// Workspace of dcn_forward_noalloc: one array per GPU, resident for the life
+// of the process.  Host code never passes `scratch` itself to a kernel (on the
+// host the name is a stand-in, not a device address): it asks the runtime for
+// the array's address on the current device once and keeps that pointer.
+static __device__ __align__(256) char scratch[DCN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first
+// call made with that device current).
+dcn_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "dcn_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DCN_E_UNSUPPORTED, "dcn_forward_noalloc: device %d (at most %d devices)", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "dcn_forward_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCN_OK;
+}
+
+}  // namespace
+
+dcn_status dcn_forward_noalloc(dcn_plan plan, const void* x, const void* offset, const void* mask,
+                               const void* weight, const void* bias, void* out, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_forward_noalloc: plan is NULL");
+    if (plan->d.batch == 0) return ok();
+    if (plan->wpack_bytes > DCN_NOALLOC_SCRATCH_BYTES)
+      return fail(DCN_E_UNSUPPORTED,
+                  "dcn_forward_noalloc: the packed weight needs %zu bytes, more than the %u "
+                  "bytes of the library's static scratch; use dcn_forward with a workspace",
+                  plan->wpack_bytes, (unsigned)DCN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    dcn_status s = scratch_on_current_device(&ws);
+    if (s != DCN_OK) return s;
+    // the tap split's partial sums only when they fit beside the weight
+    const size_t bytes = plan->ws_bytes <= DCN_NOALLOC_SCRATCH_BYTES ? plan->ws_bytes
+                                                                     : plan->wpack_bytes;
+    s = dcn_pack_weight(plan, weight, ws, bytes, stream);
+    if (s != DCN_OK) return s;
+    return dcn_forward_packed(plan, x, offset, mask, ws, bytes, bias, out, stream);
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_forward_noalloc: unexpected exception");
+  }
 }
 
 dcn_status dcn_debug_coords(dcn_plan plan, const void* offset, int32_t* y0x0, uint8_t* valid4,
