@@ -275,14 +275,32 @@ dcn_status dcn_forward_noalloc(dcn_plan plan, const void* x, const void* offset,
                                const void* mask, const void* weight, const void* bias,
                                void* out, void* stream);
 
-/* Test hook, not on the timed path: the sampling-corner stage alone, from
- * the same device function the fused kernel uses.  For every (b, k, ho, wo)
- * it writes y0x0[2e], y0x0[2e+1] = floor of the fp32 sampling row / column
- * (saturated to int32) and valid4[e] = bit (2a + b) set when corner
- * (y0 + a, x0 + b) is inside the image, where e = ((b*K + k)*Ho + ho)*Wo + wo.
- * Both are device buffers of B*K*Ho*Wo (x2 for y0x0) elements. */
+/* Test hook, not on the timed path: the sampling-corner stage alone (the
+ * floor of the sampling point and the validity of its four corners, page 1
+ * "deform_conv.py", deform_conv2d_gather: torch.floor and the `valid`
+ * comparison), from the device functions every kernel builds its corner
+ * table with.  For every (b, k, ho, wo) it writes y0x0[2e], y0x0[2e+1] =
+ * floor of the fp32 sampling row / column (saturated to int32) and
+ * valid4[e] = bit (2a + b) set when corner (y0 + a, x0 + b) is inside the
+ * image, where e = ((b*K + k)*Ho + ho)*Wo + wo.  Both are device buffers of
+ * B*K*Ho*Wo (x2 for y0x0) elements. */
 dcn_status dcn_debug_coords(dcn_plan plan, const void* offset, int32_t* y0x0, uint8_t* valid4,
                             void* stream);
+
+/* Test hook: exactly dcn_forward_packed (same kernel, same launch, `out`
+ * written as usual), and in addition the fused kernel exports the corner
+ * table it builds and gathers from -- for every (b, k, pixel p = ho*Wo + wo)
+ * and corner c = 2a + b of the sampling point's floor (y0, x0):
+ *   corner_index[e] = (b*H + y0 + a)*W + x0 + b, the input pixel the corner
+ *                     loads, or -1 for a corner outside the image (not loaded)
+ *   corner_weight[e] = bilinear weight x mask of that corner as the blend
+ *                     uses it (0 outside; rounded to bf16 in the wide bf16
+ *                     kernel), with e = ((b*K + k)*Ho*Wo + p)*4 + c.
+ * Both are device buffers of B*K*Ho*Wo*4 elements, 4-byte aligned. */
+dcn_status dcn_debug_corner_table(dcn_plan plan, const void* x, const void* offset,
+                                  const void* mask, void* workspace, size_t workspace_bytes,
+                                  const void* bias, void* out, int32_t* corner_index,
+                                  float* corner_weight, void* stream);
 
 /* Static string naming a status. */
 const char* dcn_status_string(dcn_status status);

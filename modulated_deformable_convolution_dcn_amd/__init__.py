@@ -233,6 +233,24 @@ class Plan:
             ctypes.c_void_p(_stream_handle(stream))), "dcn_backward")
         return {k: grads[k] for k in want}
 
+    def debug_corner_table(self, x, offset, mask, packed, bias=None, out=None, stream=None):
+        """``dcn_debug_corner_table``: the forward from a packed weight (as
+        ``forward_packed``) plus the corner table its kernel built:
+        (out, corner_index [B,K,Ho,Wo,4] int32, corner_weight [B,K,Ho,Wo,4] fp32)."""
+        torch = _torch()
+        d = self.desc
+        self._check_inputs(x, offset, mask, bias)
+        out = out if out is not None else self.new_output()
+        self._check("out", out, self.out_shape(), dtype=torch.float32)
+        shape = (d.batch, self.K, self.Ho, self.Wo, 4)
+        idx = torch.full(shape, -2, dtype=torch.int32, device="cuda")
+        wgt = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        _lib.check(_lib.load().dcn_debug_corner_table(
+            self._h, _ptr(x), _ptr(offset), _ptr(mask), _ptr(packed), packed.numel(), _ptr(bias),
+            _ptr(out), _ptr(idx), _ptr(wgt), ctypes.c_void_p(_stream_handle(stream))),
+            "dcn_debug_corner_table")
+        return out, idx, wgt
+
     def debug_coords(self, offset, stream=None):
         """``dcn_debug_coords``: (y0x0 [B,K,Ho,Wo,2] int32, valid4 [B,K,Ho,Wo] uint8)."""
         torch = _torch()

@@ -26,7 +26,8 @@ EXPORTS = ("dcn_create", "dcn_destroy", "dcn_output_size", "dcn_workspace_bytes"
            "dcn_pack_weight", "dcn_forward_packed", "dcn_forward", "dcn_forward_rows",
            "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_backward_workspace_bytes",
            "dcn_backward", "dcn_msda_create", "dcn_msda_destroy", "dcn_msda_value_positions",
-           "dcn_msda_forward", "dcn_forward_noalloc", "dcn_debug_coords", "dcn_status_string", "dcn_last_error",
+           "dcn_msda_forward", "dcn_forward_noalloc", "dcn_debug_coords", "dcn_debug_corner_table",
+           "dcn_status_string", "dcn_last_error",
            "dcn_version")
 
 
@@ -86,6 +87,7 @@ def load():
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
         "dcn_forward_noalloc": (st, [vp, vp, vp, vp, vp, vp, vp, vp]),
         "dcn_debug_coords": (st, [vp, vp, vp, vp, vp]),
+        "dcn_debug_corner_table": (st, [vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp]),
         "dcn_status_string": (ctypes.c_char_p, [st]),
         "dcn_last_error": (ctypes.c_char_p, []),
         "dcn_version": (i32, []),

@@ -341,7 +341,8 @@ dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
 
 dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
                         const void* x, const void* offset, const void* mask, void* workspace,
-                        size_t workspace_bytes, const void* bias, void* out, void* stream) {
+                        size_t workspace_bytes, const void* bias, void* out, void* stream,
+                        int32_t* dbg_corner = nullptr, float* dbg_weight = nullptr) {
   try {
     dcn::FusedArgs a;
     dcn::KernelConfig kc;
@@ -349,6 +350,8 @@ dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t ro
     dcn_status st = make_args(who, plan, row0, rows, x, offset, mask, workspace,
                               workspace_bytes, bias, out, a, kc, empty);
     if (st != DCN_OK || empty) return st;
+    a.dbg_corner = dbg_corner;
+    a.dbg_weight = dbg_weight;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     // split tap sum when the plan's whole-map grid is small and the workspace
     // carries the scratch; a band splits like the whole map, so the bands of a
@@ -724,6 +727,20 @@ dcn_status dcn_forward_noalloc(dcn_plan plan, const void* x, const void* offset,
   } catch (...) {
     return fail(DCN_E_INTERNAL, "dcn_forward_noalloc: unexpected exception");
   }
+}
+
+dcn_status dcn_debug_corner_table(dcn_plan plan, const void* x, const void* offset,
+                                  const void* mask, void* workspace, size_t workspace_bytes,
+                                  const void* bias, void* out, int32_t* corner_index,
+                                  float* corner_weight, void* stream) {
+  if (!plan) return fail(DCN_E_NULL, "dcn_debug_corner_table: plan is NULL");
+  if (plan->d.batch == 0) return ok();
+  if (!corner_index || !corner_weight)
+    return fail(DCN_E_NULL, "dcn_debug_corner_table: corner_index and corner_weight are required");
+  if (!aligned(corner_index, 4) || !aligned(corner_weight, 4))
+    return fail(DCN_E_ALIGN, "dcn_debug_corner_table: misaligned corner arrays");
+  return forward_band("dcn_debug_corner_table", plan, 0, plan->Ho, x, offset, mask, workspace,
+                      workspace_bytes, bias, out, stream, corner_index, corner_weight);
 }
 
 dcn_status dcn_debug_coords(dcn_plan plan, const void* offset, int32_t* y0x0, uint8_t* valid4,

@@ -44,11 +44,11 @@ __device__ __forceinline__ void atomic_add(float* p, float v) { unsafeAtomicAdd(
 
 // Per (pixel, tap): the sampling point and the validity-masked corner
 // weights, their derivatives and the corner pixel indices (row-major in the
-// image) -- the same tap_point as the forward.
+// image) -- from the forward's corner stage (tap_corners).
 struct TapTerms {
   float w[4], dwy[4], dwx[4];
   int pix[4];
-  int y0, x0;  // corner (0, 0), clamped to [-1, H] x [-1, W]
+  int y0, x0;  // corner (0, 0), clamped to [-2, H] x [-2, W]
   bool ok[4];
 };
 
@@ -56,13 +56,15 @@ __device__ __forceinline__ TapTerms tap_terms(const BwdArgs& a, int b, int ho, i
   const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
   const size_t ob = ((size_t)(b * 2 * a.K + 2 * k) * a.HoWo) + (size_t)ho * a.Wo + wo;
   const float dy = a.offset[ob], dx = a.offset[ob + a.HoWo];
-  const TapPoint t = tap_point(dy, dx, ho - a.ph + i, wo - a.pw + j, a.H, a.W);
-  const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
-  const float wv[4] = {hy * hx, hy * t.lx, t.ly * hx, t.ly * t.lx};
-  const float vy[4] = {-hx, -t.lx, hx, t.lx};
-  const float vx[4] = {-hy, hy, -t.ly, t.ly};
-  const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
-  const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
+  const TapCorners t =
+      tap_corners((float)(ho - a.ph + i), (float)(wo - a.pw + j), dy, dx, a.H, a.W);
+  const float ly = t.p.ly, lx = t.p.lx;
+  const float hy = 1.0f - ly, hx = 1.0f - lx;
+  const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
+  const float vy[4] = {-hx, -lx, hx, lx};
+  const float vx[4] = {-hy, hy, -ly, ly};
+  const int y0 = t.y0;
+  const int x0 = t.x0;
   TapTerms r;
   r.y0 = y0;
   r.x0 = x0;
@@ -201,14 +203,15 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   };
   auto t_build = [&](int slot, int k) {  // tid < TILE
     const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
-    const TapPoint tp = tap_point(n_dy, n_dx, t_ho - a.ph + i, t_wo - a.pw + j, a.H, a.W);
-    const int y0 = (int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H);
-    const int x0 = (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W);
+    const TapCorners tp =
+        tap_corners((float)(t_ho - a.ph + i), (float)(t_wo - a.pw + j), n_dy, n_dx, a.H, a.W);
+    const int y0 = tp.y0;
+    const int x0 = tp.x0;
     const uint32_t v4 = t_in ? tp.valid : 0u;
     Ti[slot][tid] = make_int4(y0, x0, (int)v4, t_in ? 1 : 0);
-    Tf[slot][tid] = f32x4{tp.ly, tp.lx, n_m, 0.0f};
-    const float hy = 1.0f - tp.ly, hx = 1.0f - tp.lx;
-    const float wv[4] = {hy * hx, hy * tp.lx, tp.ly * hx, tp.ly * tp.lx};
+    Tf[slot][tid] = f32x4{tp.p.ly, tp.p.lx, n_m, 0.0f};
+    const float hy = 1.0f - tp.p.ly, hx = 1.0f - tp.p.lx;
+    const float wv[4] = {hy * hx, hy * tp.p.lx, tp.p.ly * hx, tp.p.ly * tp.p.lx};
     f32x4 cf;
     int flags = 0;
 #pragma unroll
@@ -598,11 +601,12 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
   auto t_build = [&](int slot, int tile) {
     const int hw = tile * 64 + 16 * wave + tl;
     const int ho = hw / a.Wo, wo = hw - (hw / a.Wo) * a.Wo;
-    const TapPoint tp = tap_point(n_dy, n_dx, ho - a.ph + ki, wo - a.pw + kj, a.H, a.W);
-    const float hy = 1.0f - tp.ly, hx = 1.0f - tp.lx;
-    const float wv[4] = {hy * hx, hy * tp.lx, tp.ly * hx, tp.ly * tp.lx};
-    const int y0 = (int)fminf(fmaxf(tp.y0, -1.0f), (float)a.H);
-    const int x0 = (int)fminf(fmaxf(tp.x0, -1.0f), (float)a.W);
+    const TapCorners tp =
+        tap_corners((float)(ho - a.ph + ki), (float)(wo - a.pw + kj), n_dy, n_dx, a.H, a.W);
+    const float hy = 1.0f - tp.p.ly, hx = 1.0f - tp.p.lx;
+    const float wv[4] = {hy * hx, hy * tp.p.lx, tp.p.ly * hx, tp.p.ly * tp.p.lx};
+    const int y0 = tp.y0;
+    const int x0 = tp.x0;
     f32x4 w4;
     u32x4 o4;
 #pragma unroll

@@ -109,20 +109,28 @@ fused_bf16_kernel(Src src) {
     const int slot = kt % NSLOT;
     const int i = kt / a.kw;
     const int j = kt - i * a.kw;
-    const TapPoint t = tap_point(c_dy, c_dx, c_ho - a.ph + i, c_wo - a.pw + j, a.H, a.W);
+    const SamplePoint p =
+        sample_point((float)(c_ho - a.ph + i), (float)(c_wo - a.pw + j), c_dy, c_dx);
+    const CornerRow cr = corner_row(p, c_pair, a.H, a.W);
     const float mk = has_mask ? c_mk : 1.0f;
-    const float wy = c_pair ? t.ly : 1.0f - t.ly;
-    const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
-    const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
-    const uint32_t base = (uint32_t)((b * a.H + y0 + c_pair) * a.W + x0) * row_bytes;
-    const bool ok0 = c_in && ((t.valid >> (2 * c_pair)) & 1u);
-    const bool ok1 = c_in && ((t.valid >> (2 * c_pair + 1)) & 1u);
-    const float w0 = static_cast<float>(static_cast<__bf16>(wy * (1.0f - t.lx) * mk));
-    const float w1 = static_cast<float>(static_cast<__bf16>(wy * t.lx * mk));
+    const float wy = c_pair ? p.ly : 1.0f - p.ly;
+    const uint32_t base = (uint32_t)((b * a.H + cr.ry) * a.W + cr.ix) * row_bytes;
+    const bool ok0 = c_in && cr.ok0;
+    const bool ok1 = c_in && cr.ok1;
+    const float w0 = static_cast<float>(static_cast<__bf16>(wy * (1.0f - p.lx) * mk));
+    const float w1 = static_cast<float>(static_cast<__bf16>(wy * p.lx * mk));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const f32x2 w2 = {ok0 ? w0 : 0.0f, ok1 ? w1 : 0.0f};
     const u32x2 o2 = {ok0 ? base : kNoCorner, ok1 ? base + row_bytes : kNoCorner};
+    if (a.dbg_corner != nullptr && c_in) {
+      const size_t e = (((size_t)b * a.K + kt) * a.HoWo + c_hw) * 4 + 2 * c_pair;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        a.dbg_corner[e + q] = o2[q] == kNoCorner ? -1 : (int32_t)(o2[q] / row_bytes);
+        a.dbg_weight[e + q] = w2[q];
+      }
+    }
     *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(&Cw[slot][c_px]) + 2 * c_pair) = w2;
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&Co[slot][c_px]) + 2 * c_pair) = o2;
   };

@@ -1,8 +1,4 @@
-// dcn_device.h -- device-side building blocks of the gfx950 DCNv2 forward.
-//
-// The sampling-point stage lives here as one __device__ function used by both
-// the fused kernel and the corner-export test hook, so the bit-exact corner
-// test covers the code that runs on the timed path.
+// dcn_device.h -- device-side building blocks of the gfx950 DCNv2 kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,37 +20,73 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 2^32, so a load at it returns zero without touching memory.
 constexpr uint32_t kNoCorner = 0x80000000u;
 
-// Sampling point of one (pixel, tap) -- page 1 ("deform_conv.py",
-// deform_conv2d_gather): the base grid row (ho - pad_h + i) is an exact
-// integer, the point is that integer plus the learned offset in ONE fp32
-// add, then floor and fraction in fp32.  Corner (a, b) = (y0 + a, x0 + b) is
-// inside when 0 <= y0+a <= H-1 and 0 <= x0+b <= W-1, compared in float (a far
-// point never goes through an integer conversion).
-struct TapPoint {
-  float y0, x0;   // floor of the sampling row / column
-  float ly, lx;   // fractions in [0, 1)
-  uint32_t valid; // bit (2a + b): corner (y0 + a, x0 + b) inside the image
+// The corner stage of every kernel: the sampling point of one (pixel, tap)
+// and its four corners -- page 1 ("deform_conv.py", deform_conv2d_gather):
+// the base grid coordinate (ho - pad_h + i, wo - pad_w + j) is an exact
+// integer, the point is that integer plus the learned offset in ONE fp32 add,
+// then floor and fraction in fp32; corner (a, b) = (y0 + a, x0 + b) counts
+// only when 0 <= y0+a <= H-1 and 0 <= x0+b <= W-1 (page 1's `valid`).
+// Every forward and backward kernel and the corner-export test hooks form
+// their corner tables from these two functions, so the bit-exact corner test
+// runs this code.
+struct SamplePoint {
+  float fy, fx;  // floor of the sampling row / column
+  float ly, lx;  // fractions in [0, 1)
 };
 
-__device__ __forceinline__ TapPoint tap_point(float dy, float dx, int grid_y, int grid_x, int H,
-                                              int W) {
-  TapPoint t;
-  const float py = __fadd_rn(static_cast<float>(grid_y), dy);
-  const float px = __fadd_rn(static_cast<float>(grid_x), dx);
-  t.y0 = floorf(py);
-  t.x0 = floorf(px);
-  t.ly = __fsub_rn(py, t.y0);
-  t.lx = __fsub_rn(px, t.x0);
-  const float y1 = __fadd_rn(t.y0, 1.0f);
-  const float x1 = __fadd_rn(t.x0, 1.0f);
-  const float hmax = static_cast<float>(H - 1);
-  const float wmax = static_cast<float>(W - 1);
-  const bool vy0 = (t.y0 >= 0.0f) && (t.y0 <= hmax);
-  const bool vy1 = (y1 >= 0.0f) && (y1 <= hmax);
-  const bool vx0 = (t.x0 >= 0.0f) && (t.x0 <= wmax);
-  const bool vx1 = (x1 >= 0.0f) && (x1 <= wmax);
-  t.valid = (uint32_t)(vy0 && vx0) | ((uint32_t)(vy0 && vx1) << 1) |
-            ((uint32_t)(vy1 && vx0) << 2) | ((uint32_t)(vy1 && vx1) << 3);
+// gy, gx: the integer grid coordinate as a float (exact: |value| < 2^24).
+__device__ __forceinline__ SamplePoint sample_point(float gy, float gx, float dy, float dx) {
+  SamplePoint p;
+  const float py = __fadd_rn(gy, dy);
+  const float px = __fadd_rn(gx, dx);
+  p.fy = floorf(py);
+  p.fx = floorf(px);
+  p.ly = __fsub_rn(py, p.fy);
+  p.lx = __fsub_rn(px, p.fx);
+  return p;
+}
+
+// Corner row a (0: row y0, 1: row y0 + 1) of a sampling point: the row, the
+// first column x0 and whether corners (row, x0) and (row, x0 + 1) are inside.
+// The floor is clamped to [-2, H] x [-2, W] before the integer conversion:
+// that keeps every outside corner outside (a row or column of -2, -1, H or
+// H + 1 is out of range) and every conversion exact, also for points far
+// outside or infinite (a NaN point clamps to -2: outside).  Inside corners
+// keep their exact floor.
+struct CornerRow {
+  int ry, ix;    // row y0 + a and column x0 (clamped as above)
+  bool ok0, ok1; // (ry, ix) and (ry, ix + 1) inside the image
+};
+
+__device__ __forceinline__ CornerRow corner_row(const SamplePoint& p, int a, int H, int W) {
+  CornerRow r;
+  const int iy = (int)fminf(fmaxf(p.fy, -2.0f), (float)H);
+  r.ix = (int)fminf(fmaxf(p.fx, -2.0f), (float)W);
+  r.ry = iy + a;
+  const bool rok = (uint32_t)r.ry < (uint32_t)H;
+  r.ok0 = rok && (uint32_t)r.ix < (uint32_t)W;
+  r.ok1 = rok && (uint32_t)(r.ix + 1) < (uint32_t)W;
+  return r;
+}
+
+// Both corner rows at once: the point, its clamped top-left corner and the
+// validity bit (2a + b) of corner (y0 + a, x0 + b).
+struct TapCorners {
+  SamplePoint p;
+  int y0, x0;      // clamped floor (exact for any point with an inside corner)
+  uint32_t valid;  // bit (2a + b): corner (y0 + a, x0 + b) inside the image
+};
+
+__device__ __forceinline__ TapCorners tap_corners(float gy, float gx, float dy, float dx, int H,
+                                                  int W) {
+  TapCorners t;
+  t.p = sample_point(gy, gx, dy, dx);
+  const CornerRow r0 = corner_row(t.p, 0, H, W);
+  const CornerRow r1 = corner_row(t.p, 1, H, W);
+  t.y0 = r0.ry;
+  t.x0 = r0.ix;
+  t.valid = (uint32_t)r0.ok0 | ((uint32_t)r0.ok1 << 1) | ((uint32_t)r1.ok0 << 2) |
+            ((uint32_t)r1.ok1 << 3);
   return t;
 }
 

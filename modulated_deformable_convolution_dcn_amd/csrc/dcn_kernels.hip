@@ -113,19 +113,24 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
       const int hw = hw0 + m;
       const int ho = hw / a.Wo;
       const int wo = hw - ho * a.Wo;
-      const TapPoint t = tap_point(c_dy[r], c_dx[r], ho - a.ph + i, wo - a.pw + j, a.H, a.W);
       const int ca = corner >> 1, cb = corner & 1;
-      const float wy = ca ? t.ly : 1.0f - t.ly;
-      const float wx = cb ? t.lx : 1.0f - t.lx;
+      const SamplePoint p =
+          sample_point((float)(ho - a.ph + i), (float)(wo - a.pw + j), c_dy[r], c_dx[r]);
+      const CornerRow cr = corner_row(p, ca, a.H, a.W);
+      const float wy = ca ? p.ly : 1.0f - p.ly;
+      const float wx = cb ? p.lx : 1.0f - p.lx;
       const float mk = has_mask ? c_mk[r] : 1.0f;
-      const bool ok = (hw < a.HoWo) && ((t.valid >> corner) & 1u);
-      // clamp before converting: only inside corners are used, but the
-      // conversion of a far point must stay defined
-      const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
-      const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
-      Cw[slot][m][corner] = ok ? wy * wx * mk : 0.0f;
-      Co[slot][m][corner] =
-          ok ? (uint32_t)((b * a.H + y0 + ca) * a.W + x0 + cb) * row_bytes : kNoCorner;
+      const bool ok = (hw < a.HoWo) && (cb ? cr.ok1 : cr.ok0);
+      const float cw = ok ? wy * wx * mk : 0.0f;
+      const uint32_t co = ok ? (uint32_t)((b * a.H + cr.ry) * a.W + cr.ix + cb) * row_bytes
+                             : kNoCorner;
+      Cw[slot][m][corner] = cw;
+      Co[slot][m][corner] = co;
+      if (a.dbg_corner != nullptr && hw < a.HoWo) {
+        const size_t e = (((size_t)b * a.K + kt) * a.HoWo + hw) * 4 + corner;
+        a.dbg_corner[e] = co == kNoCorner ? -1 : (int32_t)(co / row_bytes);
+        a.dbg_weight[e] = cw;
+      }
     }
   };
 
@@ -470,11 +475,10 @@ __global__ __launch_bounds__(256) void coords_kernel(const T* __restrict__ offse
     const int ho = hw / Wo, wo = hw % Wo;
     const int i = k / kw, j = k % kw;
     const int64_t ob = ((int64_t)b * 2 * K + 2 * k) * HoWo + hw;
-    const TapPoint t =
-        tap_point(to_f32<T>(offset[ob]), to_f32<T>(offset[ob + HoWo]), ho - ph + i, wo - pw + j,
-                  H, W);
-    y0x0[2 * e] = sat_i32(t.y0);
-    y0x0[2 * e + 1] = sat_i32(t.x0);
+    const TapCorners t = tap_corners((float)(ho - ph + i), (float)(wo - pw + j),
+                                     to_f32<T>(offset[ob]), to_f32<T>(offset[ob + HoWo]), H, W);
+    y0x0[2 * e] = sat_i32(t.p.fy);
+    y0x0[2 * e + 1] = sat_i32(t.p.fx);
     valid4[e] = (uint8_t)t.valid;
   }
 }

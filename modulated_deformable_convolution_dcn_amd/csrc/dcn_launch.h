@@ -42,6 +42,12 @@ struct FusedArgs {
   int nsplit;          // 1: the whole sum plus bias, straight into out
   int kper;            // taps per split (K when nsplit is 1)
   uint32_t split_stride;  // floats between consecutive splits' partial outputs
+  // Test hook (dcn_debug_corner_table; nullptr on every other call): the
+  // kernel also writes each (b, tap, pixel)'s corner-table entry as it builds
+  // it -- corner token index (b*H + y)*W + x (-1 for an outside corner) and
+  // corner weight -- into [B, K, Ho*Wo, 4] arrays, corner (a, b) at 2a + b.
+  int32_t* dbg_corner;
+  float* dbg_weight;
 };
 
 // Arguments of the fp32 backward kernels (dcn_backward.hip).

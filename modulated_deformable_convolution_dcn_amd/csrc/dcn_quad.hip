@@ -114,47 +114,47 @@ fused_quad_kernel(Src src) {
     mk = load_scalar<float>(mskr, mb);
   };
   // The table entry of one tap, in four stages so that the step can spread
-  // them over four MFMA slots (the sampling point of page 1: exact integer
-  // grid plus ONE fp32 add of the offset, floor, fp32 fractions; validity of
-  // corner row y0 + a and columns x0, x0 + 1 compared on the floor, whose
-  // clamp to [-2, H] x [-2, W] keeps every outside corner outside).
+  // them over four MFMA slots: (0) the sampling point (sample_point), (1) the
+  // lane's corner row and the validity of its two corners (corner_row),
+  // (2) corner weights = bilinear weight x validity x mask, (3) the table
+  // write (corner byte offsets, kNoCorner for an outside corner).
   const float c_gyb = (float)(c_ho - a.ph);  // exact: |values| < 2^24
   const float c_gxb = (float)(c_wo - a.pw);
   const float c_s = c_pair ? 1.0f : -1.0f, c_t = c_pair ? 0.0f : 1.0f;  // row weight ly*s + t
   const uint32_t c_img = (uint32_t)b * (uint32_t)a.H * (uint32_t)a.W;
   struct CoefState {
-    float ly, lx, fy, fx, w0, w1;
-    int ry, ix;
-    bool ok0, ok1;
+    SamplePoint p;
+    CornerRow r;
+    float w0, w1;
   } cs;
   auto coef_stage = [&](int stage, int kt, float dy, float dx, float mkr) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     if (stage == 0) {
       const int i = (k0 + kt) / a.kw, j = (k0 + kt) - ((k0 + kt) / a.kw) * a.kw;
-      const float py = __fadd_rn(c_gyb + (float)i, dy);
-      const float px = __fadd_rn(c_gxb + (float)j, dx);
-      cs.fy = floorf(py);
-      cs.fx = floorf(px);
-      cs.ly = __fsub_rn(py, cs.fy);
-      cs.lx = __fsub_rn(px, cs.fx);
+      cs.p = sample_point(c_gyb + (float)i, c_gxb + (float)j, dy, dx);
     } else if (stage == 1) {
-      const int iy = (int)fminf(fmaxf(cs.fy, -2.0f), (float)a.H);
-      cs.ix = (int)fminf(fmaxf(cs.fx, -2.0f), (float)a.W);
-      cs.ry = iy + c_pair;
-      const bool rok = c_in && (uint32_t)cs.ry < (uint32_t)a.H;
-      cs.ok0 = rok && (uint32_t)cs.ix < (uint32_t)a.W;
-      cs.ok1 = rok && (uint32_t)(cs.ix + 1) < (uint32_t)a.W;
+      cs.r = corner_row(cs.p, c_pair, a.H, a.W);
+      cs.r.ok0 = c_in && cs.r.ok0;
+      cs.r.ok1 = c_in && cs.r.ok1;
     } else if (stage == 2) {
-      const float wy = __builtin_fmaf(cs.ly, c_s, c_t);  // 1 - ly or ly, exactly rounded
+      const float wy = __builtin_fmaf(cs.p.ly, c_s, c_t);  // 1 - ly or ly, exactly rounded
       const float wm = has_mask ? wy * mkr : wy;
-      cs.w0 = cs.ok0 ? wm * (1.0f - cs.lx) : 0.0f;
-      cs.w1 = cs.ok1 ? wm * cs.lx : 0.0f;
+      cs.w0 = cs.r.ok0 ? wm * (1.0f - cs.p.lx) : 0.0f;
+      cs.w1 = cs.r.ok1 ? wm * cs.p.lx : 0.0f;
     } else {
       const int slot = kt % NSLOT;
-      const uint32_t base = (c_img + (uint32_t)(cs.ry * a.W + cs.ix)) * row_bytes;
+      const uint32_t base = (c_img + (uint32_t)(cs.r.ry * a.W + cs.r.ix)) * row_bytes;
       const f32x2 w2 = {cs.w0, cs.w1};
-      const u32x2 o2 = {cs.ok0 ? base : kNoCorner, cs.ok1 ? base + row_bytes : kNoCorner};
+      const u32x2 o2 = {cs.r.ok0 ? base : kNoCorner, cs.r.ok1 ? base + row_bytes : kNoCorner};
+      if (a.dbg_corner != nullptr && c_in) {
+        const size_t e = (((size_t)b * a.K + k0 + kt) * a.HoWo + c_hw) * 4 + 2 * c_pair;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          a.dbg_corner[e + q] = o2[q] == kNoCorner ? -1 : (int32_t)(o2[q] / row_bytes);
+          a.dbg_weight[e + q] = w2[q];
+        }
+      }
       *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(&Cw[slot * PW + c_px]) + 2 * c_pair) = w2;
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&Co[slot * PW + c_px]) + 2 * c_pair) =
           o2;

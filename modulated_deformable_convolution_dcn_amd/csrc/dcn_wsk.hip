@@ -95,13 +95,12 @@ fused_wsk_kernel(Src src) {
     const int slot = kt % NSLOT;
     const int i = kt / a.kw;
     const int j = kt - i * a.kw;
-    const TapPoint t = tap_point(c_dy[S], c_dx[S], c_ho - a.ph + i, c_wo - a.pw + j, a.H, a.W);
+    const TapCorners t = tap_corners((float)(c_ho - a.ph + i), (float)(c_wo - a.pw + j), c_dy[S],
+                                     c_dx[S], a.H, a.W);
     const float mk = has_mask ? c_mk[S] : 1.0f;
-    const float hy = 1.0f - t.ly, hx = 1.0f - t.lx;
-    const float wv[4] = {hy * hx, hy * t.lx, t.ly * hx, t.ly * t.lx};
-    const int y0 = (int)fminf(fmaxf(t.y0, -1.0f), (float)a.H);
-    const int x0 = (int)fminf(fmaxf(t.x0, -1.0f), (float)a.W);
-    const uint32_t base = (uint32_t)((b * a.H + y0) * a.W + x0) * row_bytes;
+    const float hy = 1.0f - t.p.ly, hx = 1.0f - t.p.lx;
+    const float wv[4] = {hy * hx, hy * t.p.lx, t.p.ly * hx, t.p.ly * t.p.lx};
+    const uint32_t base = (uint32_t)((b * a.H + t.y0) * a.W + t.x0) * row_bytes;
     f32x4 w4;
     u32x4 o4;
 #pragma unroll
@@ -109,6 +108,14 @@ fused_wsk_kernel(Src src) {
       const bool ok = c_in && ((t.valid >> c) & 1u);
       w4[c] = ok ? wv[c] * mk : 0.0f;
       o4[c] = ok ? base + (uint32_t)((c >> 1) * a.W + (c & 1)) * row_bytes : kNoCorner;
+    }
+    if (a.dbg_corner != nullptr && c_in) {
+      const size_t e = (((size_t)b * a.K + kt) * a.HoWo + c_hw) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        a.dbg_corner[e + c] = o4[c] == kNoCorner ? -1 : (int32_t)(o4[c] / row_bytes);
+        a.dbg_weight[e + c] = w4[c];
+      }
     }
     if (lane < M) {
       Cww[slot * M + lane] = w4;
