@@ -141,3 +141,97 @@ def test_null_mask_is_mask_one_and_thread_count_is_deterministic():
     c, _ = oracle.backward(s, x, off, ones, w, g, nthreads=2)
     for k in a:
         assert np.array_equal(b[k], c[k]), k
+
+
+# ---------------------------------------------------------------- normalisers
+# Each gradient element is a sum of products; its normaliser N is the sum of
+# the absolute values of those products.  Because every bilinear weight is
+# >= 0, the absolute-term sums are themselves bilinear samples of |x| (with
+# per-corner zero fill), which scipy's sampler computes independently of the
+# oracle's code.  The pins below are two-sided: a dropped factor (an inflated
+# N) fails them as surely as a missing term.  scipy takes the fraction of the
+# fp32 point in fp64, the oracle in fp32 (it rounds for negative points), so
+# the two agree to 2.5e-7 relative (two fp32 fraction roundings per weight).
+
+def _fp32_points(s, off):
+    """fp32 sampling points [B, K, Ho, Wo]: exact integer grid + one fp32 add."""
+    o = off.reshape(s.B, s.K, 2, s.Ho, s.Wo)
+    i = (np.arange(s.K) // s.kw).reshape(1, s.K, 1, 1)
+    j = (np.arange(s.K) % s.kw).reshape(1, s.K, 1, 1)
+    gy = (np.arange(s.Ho).reshape(1, 1, s.Ho, 1) - s.ph + i).astype(np.float32)
+    gx = (np.arange(s.Wo).reshape(1, 1, 1, s.Wo) - s.pw + j).astype(np.float32)
+    return (gy + o[:, :, 0]).astype(np.float32), (gx + o[:, :, 1]).astype(np.float32)
+
+
+def _sample_abs(x, b, c, yy, xx):
+    """Bilinear sample of |x[b, :, :, c]| at (yy, xx), zero outside (per corner)."""
+    from scipy import ndimage
+    img = np.abs(x[b, :, :, c].astype(np.float64))
+    return ndimage.map_coordinates(img, [yy.astype(np.float64).ravel(),
+                                         xx.astype(np.float64).ravel()],
+                                   order=1, mode="grid-constant", cval=0.0).reshape(yy.shape)
+
+
+def _normalisers(s, x, off, m, w, g):
+    """The five absolute-term sums, from scipy samples of |x| (and, for grad_x,
+    an explicit scatter of the fp32 bilinear weights)."""
+    py, px = _fp32_points(s, off)
+    y0, x0 = np.floor(py), np.floor(px)
+    am = np.ones((s.B, s.K, s.Ho, s.Wo)) if m is None else np.abs(m.astype(np.float64))
+    ag = np.abs(g.astype(np.float64)).reshape(s.B, s.O, s.Ho, s.Wo)
+    aw = np.abs(w.astype(np.float64)).reshape(s.O, s.C, s.K)
+    # gsa[b, k, ho, wo, c] = sum_o |g| |W[o, c, k]|
+    gsa = np.einsum("bohw,ock->bkhwc", ag, aw)
+    samp = np.zeros((s.B, s.K, s.Ho, s.Wo, s.C))      # sample of |x| at the point
+    rows = np.zeros_like(samp)                         # rows y0, y0+1 at column px
+    cols = np.zeros_like(samp)                         # columns x0, x0+1 at row py
+    for b in range(s.B):
+        for c in range(s.C):
+            samp[b, ..., c] = _sample_abs(x, b, c, py[b], px[b])
+            rows[b, ..., c] = (_sample_abs(x, b, c, y0[b], px[b]) +
+                               _sample_abs(x, b, c, y0[b] + 1, px[b]))
+            cols[b, ..., c] = (_sample_abs(x, b, c, py[b], x0[b]) +
+                               _sample_abs(x, b, c, py[b], x0[b] + 1))
+    n = {}
+    n["mask"] = (gsa * samp).sum(axis=-1)
+    noff = np.zeros((s.B, s.K, 2, s.Ho, s.Wo))
+    noff[:, :, 0] = am * (gsa * rows).sum(axis=-1)
+    noff[:, :, 1] = am * (gsa * cols).sum(axis=-1)
+    n["offset"] = noff.reshape(s.B, 2 * s.K, s.Ho, s.Wo)
+    nw = np.einsum("bohw,bkhw,bkhwc->ock", ag, am, samp)
+    n["weight"] = nw.reshape(s.O, s.C, s.kh, s.kw)
+    n["bias"] = ag.sum(axis=(0, 2, 3))
+    # grad_x: scatter gsa * |m| * w_q to each inside corner
+    ly = (py - y0.astype(np.float32)).astype(np.float64)
+    lx = (px - x0.astype(np.float32)).astype(np.float64)
+    nx = np.zeros((s.B, s.H, s.W, s.C))
+    for a in (0, 1):
+        for bb in (0, 1):
+            wq = (ly if a else 1 - ly) * (lx if bb else 1 - lx)
+            yy, xx = y0 + a, x0 + bb
+            ok = (yy >= 0) & (yy <= s.H - 1) & (xx >= 0) & (xx <= s.W - 1)
+            bi, ki, hi, wi = np.nonzero(ok)
+            vals = (gsa * (am * wq)[..., None])[bi, ki, hi, wi]
+            np.add.at(nx, (bi, yy[bi, ki, hi, wi].astype(np.int64),
+                           xx[bi, ki, hi, wi].astype(np.int64)), vals)
+    n["x"] = nx
+    return n
+
+
+@pytest.mark.parametrize("use_mask", [True, False])
+@pytest.mark.parametrize("si", range(len(SHAPES)))
+def test_normalisers_two_sided(si, use_mask):
+    s = SHAPES[si]
+    x, off, m, w, g = _inputs(s, 40 + si)
+    m = m if use_mask else None
+    _, norms = oracle.backward(s, x, off, m, w, g, nthreads=2)
+    want = _normalisers(s, x, off, m, w, g)
+    for k in ("x", "offset", "mask", "weight", "bias"):
+        err = np.abs(norms[k] - want[k])
+        assert (err <= 2.5e-7 * want[k] + 1e-300).all(), (k, float((err / want[k]).max()))
+    # sensitivity: the same sums without |mask| (a plausible slip in the
+    # input, offset and weight normalisers) lie far outside that bound
+    if use_mask:
+        loose = _normalisers(s, x, off, None, w, g)
+        for k in ("x", "offset", "weight"):
+            assert (np.abs(norms[k] - loose[k]) > 2.5e-7 * loose[k]).any(), k

@@ -130,3 +130,25 @@ def test_partition_of_unity_linearity_and_far_points():
     far = np.full_like(loc, 3.0)
     z, n = oracle.msda(v, c["shapes"], far, w, softmax=True)
     assert not z.any() and not n.any()
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_normaliser_two_sided(ci, softmax):
+    """N = sum over points and corners of |a| * w * |v|: with w >= 0 that is
+    scipy's bilinear sample of |v| weighted by |a|; two-sided, so an N
+    missing its |a| factor (or with |a| inflated) fails as a low one does."""
+    c = CASES[ci]
+    v, loc, w = _inputs(c, 300 + ci)
+    _, norm = oracle.msda(v, c["shapes"], loc, w, softmax=softmax, nthreads=2)
+    if softmax:
+        L, K = len(c["shapes"]), c["K"]
+        e = np.exp(w.astype(np.float64) - w.astype(np.float64).max(axis=-1, keepdims=True))
+        a = (e / e.sum(axis=-1, keepdims=True))
+    else:
+        a = w.astype(np.float64)
+    want = _scipy_msda(c, np.abs(v.astype(np.float64)), loc, np.abs(a))
+    assert (np.abs(norm - want) <= 2.5e-7 * want + 1e-300).all()
+    # sensitivity: without |a| the sum is far off
+    plain = _scipy_msda(c, np.abs(v.astype(np.float64)), loc, np.ones_like(a))
+    assert (np.abs(norm - plain) > 2.5e-7 * plain).any()
