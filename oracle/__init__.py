@@ -107,6 +107,23 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def default_threads() -> int:
+    """Threads for a call that asks for 0: this process's CPU share (the
+    affinity mask, or OMP_NUM_THREADS when set), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def _threads(n: int) -> int:
+    return int(n) if n and n > 0 else default_threads()
+
+
 def forward(shape: Shape, x, offset, mask, weight, bias, pixels=None, nthreads: int = 0,
             with_norm: bool = True):
     """Oracle forward.
@@ -134,7 +151,7 @@ def forward(shape: Shape, x, offset, mask, weight, bias, pixels=None, nthreads: 
     cs = s._c()
     rc = _load().dcn_oracle_forward(ctypes.byref(cs), _ptr(x), _ptr(offset), _ptr(mask),
                                     _ptr(weight), _ptr(bias), _ptr(pix), npix, _ptr(out),
-                                    _ptr(norm), int(nthreads))
+                                    _ptr(norm), _threads(nthreads))
     if rc != 0:
         raise ValueError("dcn_oracle_forward failed with code %d" % rc)
     return out, norm
@@ -157,7 +174,7 @@ def coords(shape: Shape, offset, nthreads: int = 0):
     valid4 = np.empty((s.B, s.K, s.Ho, s.Wo), dtype=np.uint8)
     cs = s._c()
     rc = _load().dcn_oracle_coords(ctypes.byref(cs), _ptr(offset), _ptr(y0x0), _ptr(valid4),
-                                   int(nthreads))
+                                   _threads(nthreads))
     if rc != 0:
         raise ValueError("dcn_oracle_coords failed with code %d" % rc)
     return y0x0, valid4
@@ -188,7 +205,7 @@ def backward(shape: Shape, x, offset, mask, weight, grad_out, nthreads: int = 0)
     rc = _load().dcn_oracle_backward(ctypes.byref(cs), _ptr(x), _ptr(offset), _ptr(mask),
                                      _ptr(weight), _ptr(grad_out),
                                      *[_ptr(g[k]) for k in order], *[_ptr(n[k]) for k in order],
-                                     int(nthreads))
+                                     _threads(nthreads))
     if rc != 0:
         raise ValueError("dcn_oracle_backward failed with code %d" % rc)
     return g, n
@@ -211,7 +228,7 @@ def msda(value, shapes, locations, weights, softmax: bool, nthreads: int = 0):
     norm = np.empty((B, Q, G, D), dtype=np.float64)
     rc = _load().dcn_oracle_msda(B, S, G, D, Q, L, K, _ptr(sh), _ptr(value), _ptr(locations),
                                  _ptr(weights), int(bool(softmax)), _ptr(out), _ptr(norm),
-                                 int(nthreads))
+                                 _threads(nthreads))
     if rc != 0:
         raise ValueError("dcn_oracle_msda failed with code %d" % rc)
     return out, norm

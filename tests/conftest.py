@@ -38,3 +38,16 @@ def pytest_sessionstart(session):
         build.build()
     import oracle
     oracle.build(force=False)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the parity margins of this session (tests/dcn_testlib.MARGINS)
+    to the file named by DCN_PARITY_MARGINS, if set."""
+    path = os.environ.get("DCN_PARITY_MARGINS")
+    if not path:
+        return
+    import json
+    mod = sys.modules.get("dcn_testlib")
+    rows = list(getattr(mod, "MARGINS", [])) if mod is not None else []
+    with open(path, "w") as fh:
+        json.dump(rows, fh, indent=1)

@@ -16,6 +16,22 @@ from modulated_deformable_convolution_dcn_amd import synth
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
+# Per comparison of this session: what, elements compared, the worst
+# err / N, the tolerance factor on N, and the largest share of the whole
+# per-element bound (tol * N + ulp32(|ref|)) that any element used.  Written
+# out at session end when DCN_PARITY_MARGINS names a file (tests/conftest.py).
+MARGINS = []
+
+
+def record_margin(what: str, n: int, worst: float, tol: float, used: float) -> None:
+    MARGINS.append({"what": what, "elements": int(n), "worst_err_over_N": float(worst),
+                    "tol": float(tol), "bound_used": float(used)})
+
+
+def bound_used(err: np.ndarray, bound: np.ndarray, mask: np.ndarray) -> float:
+    """max over masked elements of err / bound (0 when none)."""
+    return float((err[mask] / bound[mask]).max()) if mask.any() else 0.0
+
 
 def oracle_shape(spec: synth.Spec) -> oracle.Shape:
     return oracle.Shape(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw)
@@ -80,18 +96,6 @@ def compare(gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray, bias, dtype: str
                 p, o, gpu[p, o], ref[p, o], norm[p, o], err[p, o] / max(norm[p, o], 1e-300)))
         raise AssertionError("\n".join(msg))
     nz = ~zero
-    return float((err[nz] / norm[nz]).max()) if nz.any() else 0.0
-
-
-def sample_pixels(spec: synth.Spec, n: int, seed: int = 0) -> np.ndarray:
-    """Random pixels plus every image's first/last pixel, row ends and tile seams."""
-    rng = np.random.default_rng(seed)
-    hw = spec.Ho * spec.Wo
-    P = spec.B * hw
-    picks = set(rng.choice(P, size=min(n, P), replace=False).tolist())
-    for b in range(spec.B):
-        base = b * hw
-        for q in (0, spec.Wo - 1, hw - spec.Wo, hw - 1, 63, 64, hw // 2):
-            if 0 <= q < hw:
-                picks.add(base + q)
-    return np.array(sorted(picks), dtype=np.int64)
+    worst = float((err[nz] / norm[nz]).max()) if nz.any() else 0.0
+    record_margin(what, gpu.size, worst, TOL[dtype], bound_used(err, tol, nz))
+    return worst

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from dcn_testlib import device_inputs, oracle_shape
+from dcn_testlib import bound_used, device_inputs, oracle_shape, record_margin
 from modulated_deformable_convolution_dcn_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -50,7 +50,10 @@ def _check(name, got, ref, norm):
         raise AssertionError("%s: %d / %d outside tolerance; first %s gpu %.9g ref %.9g N %.3g" % (
             name, int(bad.sum()), bad.size, tuple(i), got[tuple(i)], ref[tuple(i)], norm[tuple(i)]))
     nz = ~zero
-    return float((err[nz] / norm[nz]).max()) if nz.any() else 0.0
+    worst = float((err[nz] / norm[nz]).max()) if nz.any() else 0.0
+    record_margin("backward " + name, got.size, worst, 1e-4,
+                  bound_used(err, 1e-4 * norm + ulp, nz))
+    return worst
 
 
 def _run(spec, d, gout, layout, use_mask=True, want=("x", "offset", "mask", "weight", "bias")):
@@ -110,17 +113,21 @@ def test_backward_all_corners_outside():
                        atol=1e-4)
 
 
-def test_backward_birefnet512_full_size():
-    """The 128 x 128, 64-channel 7x7 workload at full size, NCHW."""
-    spec = W["birefnet512_fp32"]
+@pytest.mark.parametrize("name", ["birefnet512_fp32", "birefnet1024_fp32"])
+def test_backward_full_size(name):
+    """The 128 x 128 and 256 x 256 (benchmarked) 64-channel 7x7 workloads at
+    full size, NCHW, every element of all five gradients."""
+    spec = W[name]
     d = synth.make_inputs(spec)
     gout = _grad_out(spec, 17)
+    print("case %s backward full: oracle" % name, flush=True)
     ref, norm = oracle.backward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
-                                gout, nthreads=16)
-    print("case birefnet512 full", flush=True)
+                                gout)
+    print("case %s backward full: gpu" % name, flush=True)
     got = _run(spec, d, gout, "nchw")
     for k in ("x", "offset", "mask", "weight", "bias"):
-        _check("full grad_%s" % k, got[k], ref[k], norm[k])
+        worst = _check("%s full grad_%s" % (name, k), got[k], ref[k], norm[k])
+        print("  grad_%s worst err/N %.3g" % (k, worst))
 
 
 @pytest.mark.parametrize("want", [("offset", "mask"), ("offset",), ("mask", "bias"), ("x",)])

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from modulated_deformable_convolution_dcn_amd import synth
-from dcn_testlib import compare, oracle_shape, run_gpu, sample_pixels, device_inputs, pixel_major
+from dcn_testlib import compare, oracle_shape, run_gpu, device_inputs, pixel_major
 
 pytestmark = pytest.mark.gpu
 
@@ -83,21 +83,20 @@ def test_optional_mask_and_bias(use_mask, use_bias):
     compare(got, ref, norm, d["bias"] if use_bias else None, spec.dtype, "optional")
 
 
-# Full-size workloads in the launch configuration the benchmark times:
-# sampled pixels from the oracle, plus properties that hold at any size.
+# Full-size workloads in the launch configuration the benchmark times: the
+# whole output of both layouts against the oracle (the 128 x 128 workload is
+# compared whole in FULL_CASES above).
 FULL_SIZE = ["birefnet1024_fp32", "detection_bf16", "edge_stress_fp32"]
 
 
 @pytest.mark.parametrize("name", FULL_SIZE)
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
     import torch
     from modulated_deformable_convolution_dcn_amd import Desc, Plan
     spec = W[name]
     d = synth.make_inputs(spec)
-    pix = sample_pixels(spec, 1500, seed=11)
-    ref, norm = oracle.forward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
-                               d["bias"], pixels=pix)
-    print("case", name, "pixels", pix.size, flush=True)
+    print("case", name, "oracle on all %d pixels" % spec.pixels, flush=True)
+    ref, norm = _oracle_full(spec, d)
     dev = device_inputs(spec, d)
     outs = {}
     for layout in ("nchw", "nhwc"):
@@ -111,10 +110,11 @@ def test_full_size_sampled_parity(name):
         assert np.array_equal(a1.view(np.uint32), a2.view(np.uint32))
         outs[layout] = pixel_major(a1, layout)
         assert np.isfinite(outs[layout]).all()
+        worst = compare(outs[layout], ref, norm, d["bias"], spec.dtype,
+                        "%s/%s full" % (name, layout))
+        print("%s worst err/N %.3g" % (layout, worst))
     # both layouts run the same arithmetic; only the store differs
     assert np.array_equal(outs["nchw"].view(np.uint32), outs["nhwc"].view(np.uint32))
-    worst = compare(outs["nchw"][pix], ref, norm, d["bias"], spec.dtype, name)
-    print("worst err/N %.3g" % worst)
 
 
 def test_packed_weight_reuse_matches_forward():
