@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "deform-conv output pixels/s + effective TFLOP/s and % roofline, 256^2x64ch 7x7"
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
 HBM_PEAK_GBS = 8000.0
+# vector L1 return bandwidth: 64 B per clock per CU x 256 CUs x 2.4 GHz
+L1_PEAK_GBS = 64 * 256 * 2.4
 KERNEL_DIR = os.path.join(ROOT, "modulated_deformable_convolution_dcn_amd", "csrc")
 
 
@@ -148,6 +150,7 @@ def bench_msda(args, torch, synth) -> int:
     compulsory = 4 * (spec.B * spec.S * spec.G * spec.D + points * 2 + points + pairs * spec.D)
     gathered = points * 4 * spec.D * 4  # four corner vectors per point
     hbm = compulsory / (kern_ms * 1e-3) / 1e9
+    gather_gbs = gathered / (kern_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "msda sampling points/s", "value": points / (ms * 1e-3), "unit": "points/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -156,9 +159,13 @@ def bench_msda(args, torch, synth) -> int:
         "config": {"workload": spec.name, "B": spec.B, "Q": spec.Q, "G": spec.G, "D": spec.D,
                    "levels": [list(x) for x in spec.shapes], "K": spec.K,
                    "softmax": spec.softmax},
-        "roofline": {"bound": "hbm", "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": hbm / HBM_PEAK_GBS, "traffic": None},
-        "gather_gbs": gathered / (kern_ms * 1e-3) / 1e9,
+        # the bound is the corner gather through the vector L1: 4 corner
+        # vectors per point at the L1's 64 B/clk per CU (256 CUs, 2.4 GHz);
+        # the compulsory HBM bytes are reported beside it
+        "roofline": {"bound": "l1_gather", "achieved": gather_gbs, "peak": L1_PEAK_GBS,
+                     "unit": "GB/s", "frac": gather_gbs / L1_PEAK_GBS, "traffic": None},
+        "hbm": {"achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm / HBM_PEAK_GBS, "compulsory_bytes": compulsory},
         "kernels_us": {"msda": kern_ms * 1e3},
         "fused_us_percentiles": {k: v * 1e3 for k, v in percentiles(ks).items()},
     }), flush=True)
@@ -426,7 +433,8 @@ def main() -> int:
         "pct_roofline": 100.0 * tflops / peak,
         "roofline": {"bound": "mfma", "achieved": fused_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
-                     "traffic": measured_traffic(spec.name)},
+                     # the counter record covers the forward kernel only
+                     "traffic": None if args.backward else measured_traffic(spec.name)},
         # "fused" spans the whole forward call: with a tap split, the fused
         # kernel and the reduce that adds the runs
         "kernels_us": {"fused": fused_ms * 1e3,
