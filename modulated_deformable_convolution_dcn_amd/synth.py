@@ -227,3 +227,78 @@ def make_msda_inputs(spec: MsdaSpec) -> dict:
                           size=(spec.B, spec.Q, spec.G, spec.L, spec.K, 2)))
     w = f32(rng.standard_normal((spec.B, spec.Q, spec.G, spec.L * spec.K)))
     return {"value": value, "locations": loc, "weights": w}
+
+
+@dataclass(frozen=True)
+class DsSpec:
+    """A single-scale deformable sampling workload (page 5, DCNv3 form):
+    x [B,H,W,G*D] NHWC, offset [B,G*2K,Ho,Wo], aggregation weights [B,G*K,Ho,Wo]."""
+    name: str
+    B: int
+    G: int
+    D: int
+    H: int
+    W: int
+    kh: int
+    kw: int
+    ph: int
+    pw: int
+    dtype: str          # "f32" or "bf16"
+    softmax: bool       # weights are logits normalised over the K taps in the kernel
+    seed: int
+    offset_std: float = 1.5
+
+    @property
+    def C(self) -> int:
+        return self.G * self.D
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    @property
+    def Ho(self) -> int:
+        return self.H + 2 * self.ph - self.kh + 1
+
+    @property
+    def Wo(self) -> int:
+        return self.W + 2 * self.pw - self.kw + 1
+
+    @property
+    def pixels(self) -> int:
+        return self.B * self.Ho * self.Wo
+
+    def scaled(self, **kw) -> "DsSpec":
+        return replace(self, **kw)
+
+
+# page 5's example layer: DeformSample2d(dim=64, kernel_size=3, groups=4) on a
+# 32 x 32 map; the same layer on the 256 x 256 decoder map of the BiRefNet
+# workloads (page 2) for throughput, in fp32 and bf16
+DS_WORKLOADS = {
+    "dcnv3_page5_fp32": DsSpec("dcnv3_page5_fp32", 1, 4, 16, 32, 32, 3, 3, 1, 1, "f32", True, 31),
+    "dcnv3_map256_fp32": DsSpec("dcnv3_map256_fp32", 1, 4, 16, 256, 256, 3, 3, 1, 1, "f32", True,
+                                32),
+    "dcnv3_map256_bf16": DsSpec("dcnv3_map256_bf16", 1, 4, 16, 256, 256, 3, 3, 1, 1, "bf16", True,
+                                33),
+}
+
+
+def make_ds_inputs(spec: DsSpec) -> dict:
+    """x ~ N(0,1) [B,H,W,G*D]; offsets ~ N(0, offset_std^2) [B,G*2K,Ho,Wo];
+    weights (logits when spec.softmax, else U(0,1)) [B,G*K,Ho,Wo]; drawn in that
+    order in fp64, rounded to fp32 (and to bf16 with ``bits`` for bf16)."""
+    rng = np.random.default_rng(spec.seed)
+    K = spec.K
+    x = rng.standard_normal((spec.B, spec.H, spec.W, spec.C))
+    off = rng.standard_normal((spec.B, spec.G * 2 * K, spec.Ho, spec.Wo)) * spec.offset_std
+    shape = (spec.B, spec.G * K, spec.Ho, spec.Wo)
+    w = rng.standard_normal(shape) if spec.softmax else rng.uniform(0.0, 1.0, size=shape)
+    out = {k: np.ascontiguousarray(v, dtype=np.float32)
+           for k, v in (("x", x), ("offset", off), ("weights", w))}
+    if spec.dtype == "bf16":
+        bits = {}
+        for k in list(out):
+            out[k], bits[k] = round_bf16(out[k])
+        out["bits"] = bits
+    return out

@@ -46,6 +46,12 @@ class _Shape(ctypes.Structure):
         "batch", "in_ch", "height", "width", "out_ch", "kernel_h", "kernel_w", "pad_h", "pad_w")]
 
 
+class _DsShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "batch", "groups", "group_ch", "height", "width", "kernel_h", "kernel_w", "pad_h",
+        "pad_w")]
+
+
 def _load():
     global _lib
     if _lib is None:
@@ -63,6 +69,9 @@ def _load():
         i64 = ctypes.c_int64
         lib.dcn_oracle_msda.argtypes = [i64] * 7 + [vp] * 4 + [ctypes.c_int, vp, vp, ctypes.c_int]
         lib.dcn_oracle_msda.restype = ctypes.c_int
+        lib.dcn_oracle_dsample.argtypes = [ctypes.POINTER(_DsShape), vp, vp, vp, ctypes.c_int, vp,
+                                           vp, ctypes.c_int]
+        lib.dcn_oracle_dsample.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -231,4 +240,58 @@ def msda(value, shapes, locations, weights, softmax: bool, nthreads: int = 0):
                                  _threads(nthreads))
     if rc != 0:
         raise ValueError("dcn_oracle_msda failed with code %d" % rc)
+    return out, norm
+
+
+@dataclass(frozen=True)
+class DsShape:
+    """Single-scale deformable sampling size: x [B,H,W,G*D] NHWC, a kh x kw
+    kernel grid, padding (ph, pw)."""
+    B: int
+    G: int
+    D: int
+    H: int
+    W: int
+    kh: int
+    kw: int
+    ph: int
+    pw: int
+
+    @property
+    def C(self) -> int:
+        return self.G * self.D
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    @property
+    def Ho(self) -> int:
+        return self.H + 2 * self.ph - self.kh + 1
+
+    @property
+    def Wo(self) -> int:
+        return self.W + 2 * self.pw - self.kw + 1
+
+
+def dsample(shape: DsShape, x, offset, weights, softmax: bool, nthreads: int = 0):
+    """Oracle single-scale deformable sampling (see dcn_oracle.h).
+
+    x [B,H,W,G*D], offset [B,G*2K,Ho,Wo] (channel (g*K+k)*2 = dy, +1 = dx),
+    weights [B,G*K,Ho,Wo] (logits when ``softmax``).  Returns ``(out, norm)``,
+    float64 [B, Ho, Wo, G*D] (NHWC).
+    """
+    s = shape
+    x, offset, weights = (_f32(a) for a in (x, offset, weights))
+    assert x.shape == (s.B, s.H, s.W, s.C), x.shape
+    assert offset.shape == (s.B, s.G * 2 * s.K, s.Ho, s.Wo), offset.shape
+    assert weights.shape == (s.B, s.G * s.K, s.Ho, s.Wo), weights.shape
+    out = np.empty((s.B, s.Ho, s.Wo, s.C), dtype=np.float64)
+    norm = np.empty((s.B, s.Ho, s.Wo, s.C), dtype=np.float64)
+    cs = _DsShape(s.B, s.G, s.D, s.H, s.W, s.kh, s.kw, s.ph, s.pw)
+    rc = _load().dcn_oracle_dsample(ctypes.byref(cs), _ptr(x), _ptr(offset), _ptr(weights),
+                                    int(bool(softmax)), _ptr(out), _ptr(norm),
+                                    _threads(nthreads))
+    if rc != 0:
+        raise ValueError("dcn_oracle_dsample failed with code %d" % rc)
     return out, norm

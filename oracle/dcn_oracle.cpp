@@ -457,3 +457,85 @@ extern "C" int dcn_oracle_msda(int64_t B, int64_t S, int64_t G, int64_t D, int64
   for (auto& th : pool) th.join();
   return 0;
 }
+
+// ---------------------------------------------------------------- single-scale
+// Page 5, "Single-scale deformable sampling" (DCNv3 of InternImage): the same
+// sampling points as the deformable convolution, but no spatial weight: each
+// channel group g aggregates its own K bilinear samples with one weight per
+// (group, tap, pixel).  Per (b, ho, wo, g) and channel c of the group:
+//   out = sum_k a_{g,k} * bilinear(x[b, :, :, g*D + c], ho - ph + i_k + dy, wo - pw + j_k + dx)
+// with the point, floor and fractions exactly as in the convolution (one fp32
+// add of the offset to the exact grid) and fp64 from the weights on.
+extern "C" int dcn_oracle_dsample(const dcn_oracle_ds_shape* s, const float* x,
+                                  const float* offset, const float* weights, int softmax,
+                                  double* out, double* norm, int nthreads) {
+  if (!s || !x || !offset || !weights || !out) return 1;
+  if (s->batch < 0 || s->groups <= 0 || s->group_ch <= 0 || s->height <= 0 || s->width <= 0 ||
+      s->kernel_h <= 0 || s->kernel_w <= 0 || s->pad_h < 0 || s->pad_w < 0)
+    return 2;
+  // the convolution's geometry (no output channels here; O is unused)
+  dcn_oracle_shape cs = {s->batch, s->groups * s->group_ch, s->height, s->width, 1,
+                         s->kernel_h, s->kernel_w, s->pad_h, s->pad_w};
+  Dims d;
+  if (!make_dims(&cs, &d)) return 2;
+  const int64_t G = s->groups, D = s->group_ch;
+  const int64_t pairs = d.B * d.Ho * d.Wo * G;  // one work item per (pixel, group)
+  const int nt = resolve_threads(nthreads, pairs);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t) {
+    pool.emplace_back([&, t]() {
+      std::vector<double> a(static_cast<size_t>(d.K));
+      for (int64_t n = t; n < pairs; n += nt) {
+        const int64_t g = n % G;
+        const int64_t p = n / G;  // (b*Ho + ho)*Wo + wo
+        const int64_t b = p / (d.Ho * d.Wo);
+        const int64_t ho = (p / d.Wo) % d.Ho;
+        const int64_t wo = p % d.Wo;
+        // aggregation weights of the K taps: weights[b, g*K + k, ho, wo],
+        // used as given or as a softmax over the K taps (fp64)
+        for (int64_t k = 0; k < d.K; ++k)
+          a[k] = weights[((b * G * d.K + g * d.K + k) * d.Ho + ho) * d.Wo + wo];
+        if (softmax) {
+          double mx = -INFINITY, sum = 0.0;
+          for (int64_t k = 0; k < d.K; ++k) mx = std::fmax(mx, a[k]);
+          for (int64_t k = 0; k < d.K; ++k) sum += std::exp(a[k] - mx);
+          for (int64_t k = 0; k < d.K; ++k) a[k] = std::exp(a[k] - mx) / sum;
+        }
+        double* orow = &out[p * G * D + g * D];
+        double* nrow = norm ? &norm[p * G * D + g * D] : nullptr;
+        for (int64_t c = 0; c < D; ++c) {
+          orow[c] = 0.0;
+          if (nrow) nrow[c] = 0.0;
+        }
+        for (int64_t k = 0; k < d.K; ++k) {
+          const int64_t i = k / d.kw, j = k % d.kw;
+          // offset channel (g*K + k)*2 = dy, +1 = dx: the convolution's
+          // [B, 2K, Ho, Wo] layout with one block of 2K channels per group
+          const int64_t oc = (b * G * 2 * d.K + (g * d.K + k) * 2) * d.Ho * d.Wo + ho * d.Wo + wo;
+          const float dy = offset[oc];
+          const float dx = offset[oc + d.Ho * d.Wo];
+          const Coord cd = tap_coord(d, ho, wo, i, j, dy, dx);
+          const double ly = cd.ly, lx = cd.lx;
+          const double wgt[2][2] = {{(1.0 - ly) * (1.0 - lx), (1.0 - ly) * lx},
+                                    {ly * (1.0 - lx), ly * lx}};
+          for (int64_t c = 0; c < D; ++c) {
+            double sv = 0.0, sa = 0.0;
+            for (int ca = 0; ca < 2; ++ca)
+              for (int cb = 0; cb < 2; ++cb) {
+                if (!corner_valid(d, cd.y0, cd.x0, ca, cb)) continue;  // outside: 0
+                const int64_t yy = static_cast<int64_t>(cd.y0) + ca;
+                const int64_t xx = static_cast<int64_t>(cd.x0) + cb;
+                const double v = x[((b * d.H + yy) * d.W + xx) * G * D + g * D + c];
+                sv += wgt[ca][cb] * v;
+                sa += wgt[ca][cb] * std::fabs(v);
+              }
+            orow[c] += a[k] * sv;
+            if (nrow) nrow[c] += std::fabs(a[k]) * sa;
+          }
+        }
+      }
+    });
+  }
+  for (auto& th : pool) th.join();
+  return 0;
+}

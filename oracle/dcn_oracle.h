@@ -116,6 +116,34 @@ int dcn_oracle_msda(int64_t B, int64_t S, int64_t G, int64_t D, int64_t Q, int64
                     const int64_t* shapes, const float* value, const float* locations,
                     const float* weights, int softmax, double* out, double* norm, int nthreads);
 
+/*
+ * Single-scale deformable sampling (page 5, deformops README, "Single-scale
+ * deformable sampling": the DCNv3 operator of InternImage, sampling and
+ * aggregation without the spatial weight of deformable convolution).  The
+ * channels are G groups of D; each group has its own offsets and one
+ * aggregation weight per (tap, pixel).  For output (b, ho, wo) and channel
+ * g*D + c:
+ *   out = sum_k a[b, g, k, ho, wo] *
+ *         bilinear(x[b, :, :, g*D + c], ho - pad_h + i_k + dy, wo - pad_w + j_k + dx)
+ * with the sampling point, floor, fractions and corner validity exactly as
+ * in dcn_oracle_forward (stride 1, dilation 1, tap k = i*kw + j).
+ *   x       [B, H, W, G*D]     NHWC
+ *   offset  [B, G*2K, Ho, Wo]  channel (g*K + k)*2 = dy, (g*K + k)*2 + 1 = dx
+ *   weights [B, G*K, Ho, Wo]   a of (g, k) at channel g*K + k; logits when
+ *                              softmax != 0 (a = softmax over the K taps of
+ *                              one (b, g, ho, wo), in fp64)
+ *   out     [B, Ho, Wo, G*D] fp64 (NHWC); norm (may be NULL) the same shape:
+ *           sum_k |a| * sum_corners w * |x|.
+ */
+typedef struct {
+  int64_t batch, groups, group_ch, height, width;
+  int64_t kernel_h, kernel_w, pad_h, pad_w;
+} dcn_oracle_ds_shape;
+
+int dcn_oracle_dsample(const dcn_oracle_ds_shape* s, const float* x, const float* offset,
+                       const float* weights, int softmax, double* out, double* norm,
+                       int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
