@@ -172,6 +172,60 @@ def bench_msda(args, torch, synth) -> int:
     return 0
 
 
+def bench_dsample(args, torch, synth) -> int:
+    """Single-scale deformable sampling (page 5, DCNv3 form): one launch per step."""
+    import numpy as np
+    from modulated_deformable_convolution_dcn_amd import DsamplePlan
+    spec = synth.DS_WORKLOADS[args.dsample]
+    d = synth.make_ds_inputs(spec)
+    dev = {k: (torch.from_numpy(d[k]).cuda() if spec.dtype == "f32" else
+               torch.from_numpy(d["bits"][k].astype(np.int16)).cuda().view(torch.bfloat16))
+           for k in ("x", "offset", "weights")}
+    plan = DsamplePlan(spec.B, spec.G, spec.D, spec.H, spec.W, spec.kh, spec.kw, spec.ph,
+                       spec.pw, spec.dtype, spec.softmax, args.layout)
+    out = torch.empty(plan.out_shape(), device="cuda")
+    for _ in range(args.warmup):
+        plan.forward(dev["x"], dev["offset"], dev["weights"], out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        plan.forward(dev["x"], dev["offset"], dev["weights"], out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ks = [e[0].elapsed_time(e[1]) for e in ev]
+    kern_ms = sum(ks) / len(ks)
+    ms = elapsed * 1e3 / args.steps
+    e = 2 if spec.dtype == "bf16" else 4
+    P = spec.pixels
+    # compulsory: x once, offsets, weights, fp32 output; gathered: 4 corner
+    # slices of D channels per (pixel, group, tap)
+    compulsory = (spec.B * spec.H * spec.W * spec.C * e + P * spec.G * spec.K * 3 * e +
+                  P * spec.C * 4)
+    gathered = P * spec.G * spec.K * 4 * spec.D * e
+    hbm = compulsory / (kern_ms * 1e-3) / 1e9
+    gather_gbs = gathered / (kern_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "deformable sampling output pixels/s", "value": P / (ms * 1e-3),
+        "unit": "px/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "G": spec.G, "D": spec.D, "H": spec.H,
+                   "W": spec.W, "kernel": "%dx%d" % (spec.kh, spec.kw),
+                   "pad": [spec.ph, spec.pw], "softmax": spec.softmax,
+                   "out_layout": args.layout},
+        "roofline": {"bound": "l1_gather", "achieved": gather_gbs, "peak": L1_PEAK_GBS,
+                     "unit": "GB/s", "frac": gather_gbs / L1_PEAK_GBS, "traffic": None},
+        "hbm": {"achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm / HBM_PEAK_GBS, "compulsory_bytes": compulsory},
+        "kernels_us": {"dsample": kern_ms * 1e3},
+        "fused_us_percentiles": {k: v * 1e3 for k, v in percentiles(ks).items()},
+    }), flush=True)
+    return 0
+
+
 def percentiles(xs):
     ys = sorted(xs)
     pick = lambda f: ys[min(len(ys) - 1, int(round(f * (len(ys) - 1))))]
@@ -246,6 +300,9 @@ def main() -> int:
     ap.add_argument("--msda", metavar="WORKLOAD", default=None,
                     help="time multi-scale deformable attention sampling on this workload "
                          "(msda_encoder_fp32, msda_decoder_fp32) instead")
+    ap.add_argument("--dsample", metavar="WORKLOAD", default=None,
+                    help="time single-scale deformable sampling on this workload "
+                         "(dcnv3_page5_fp32, dcnv3_map256_fp32, dcnv3_map256_bf16) instead")
     ap.add_argument("--bands", type=int, default=1,
                     help="run the forward as this many output-row bands (row0 calls), "
                          "back to back on one stream")
@@ -282,6 +339,8 @@ def main() -> int:
     from modulated_deformable_convolution_dcn_amd import Desc, Plan, synth
     if args.msda:
         return bench_msda(args, torch, synth)
+    if args.dsample:
+        return bench_dsample(args, torch, synth)
 
     spec = synth.WORKLOADS[args.workload]
     d = synth.make_inputs(spec)

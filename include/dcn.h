@@ -248,6 +248,42 @@ dcn_status dcn_msda_value_positions(dcn_msda_plan plan, int32_t* positions);
 dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* locations,
                             const void* weights, void* out, void* stream);
 
+/*
+ * Single-scale deformable sampling (page 5, deformops README, "Single-scale
+ * deformable sampling": the DCNv3 operator of InternImage, which samples and
+ * aggregates without the spatial weight of deformable convolution).  The
+ * C = G*D channels are G groups of D; each group has its own offsets and one
+ * aggregation weight a per (tap, pixel).  For output (b, ho, wo) and channel
+ * g*D + c:
+ *   out = sum_k a[b, g*K + k, ho, wo] *
+ *         bilinear(x[b, :, :, g*D + c], ho - pad_h + i + dy, wo - pad_w + j + dx)
+ * with tap k = i*kw + j, the sampling point, floor and corner validity of
+ * the deformable convolution above (corners outside count as zero), and a
+ * used as given (softmax = 0) or normalised by a softmax over the K taps of
+ * each (b, g, ho, wo) (softmax = 1).  Stride 1, dilation 1.
+ *   x       [B, H, W, G*D]      NHWC, dtype
+ *   offset  [B, G*2K, Ho, Wo]   channel (g*K + k)*2 = dy, +1 = dx, dtype
+ *   weights [B, G*K, Ho, Wo]    a (or logits), dtype
+ *   out     [B, Ho, Wo, G*D] (DCN_OUT_NHWC) or [B, G*D, Ho, Wo] (DCN_OUT_NCHW), fp32
+ * Limits (DCN_E_UNSUPPORTED otherwise): group_ch a multiple of 4 (fp32) or 8
+ * (bf16); x and offset below 2^31 bytes.  Accumulation is fp32.
+ */
+typedef struct dcn_dsample_plan_s* dcn_dsample_plan;
+typedef struct {
+  int32_t batch, groups, group_ch, height, width;
+  int32_t kernel_h, kernel_w, pad_h, pad_w;
+  int32_t dtype;       /* dcn_dtype of x, offset, weights */
+  int32_t softmax;     /* 0: weights as given; 1: softmax over the K taps */
+  int32_t out_layout;  /* dcn_layout */
+} dcn_dsample_desc;
+dcn_status dcn_dsample_create(const dcn_dsample_desc* desc, dcn_dsample_plan* plan);
+dcn_status dcn_dsample_destroy(dcn_dsample_plan plan);
+dcn_status dcn_dsample_output_size(dcn_dsample_plan plan, int32_t* ho, int32_t* wo);
+/* One kernel launch on `stream`; x and out 16-byte aligned, offset and
+ * weights element-aligned; out must not overlap an input. */
+dcn_status dcn_dsample_forward(dcn_dsample_plan plan, const void* x, const void* offset,
+                               const void* weights, void* out, void* stream);
+
 /* Layout conversion for callers holding NCHW input (page 5's torchvision
  * drop-in takes torchvision's argument order and NCHW layout): writes
  * dst[b, y, x, c] = src[b, c, y, x] for a [batch, channels, height, width]

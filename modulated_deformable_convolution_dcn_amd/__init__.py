@@ -19,8 +19,8 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import DcnError  # noqa: F401
 
-__all__ = ["Plan", "MsdaPlan", "deform_conv2d", "deform_conv2d_nhwc", "forward_multi", "msda",
-           "nchw_to_nhwc", "DcnError"]
+__all__ = ["Plan", "MsdaPlan", "DsamplePlan", "deform_conv2d", "deform_conv2d_nhwc",
+           "forward_multi", "msda", "dsample", "nchw_to_nhwc", "DcnError"]
 
 _DTYPES = {"f32": _lib.DCN_F32, "bf16": _lib.DCN_BF16}
 _LAYOUTS = {"nchw": _lib.DCN_OUT_NCHW, "nhwc": _lib.DCN_OUT_NHWC}
@@ -419,3 +419,93 @@ def msda(value, shapes, locations, weights, softmax=False):
         p = MsdaPlan(B, Q, G, D, shapes, K, softmax)
         _MSDA_PLANS[key] = p
     return p.forward(value, locations, weights)
+
+
+class DsamplePlan:
+    """``dcn_dsample_create``: single-scale deformable sampling (page 5's DCNv3
+    form) of one size: x [B,H,W,G*D] NHWC, offset [B,G*2K,Ho,Wo] (channel
+    (g*K + k)*2 = dy, +1 = dx), weights [B,G*K,Ho,Wo] (logits when
+    ``softmax``); out fp32 [B,Ho,Wo,G*D] ("nhwc") or [B,G*D,Ho,Wo] ("nchw")."""
+
+    def __init__(self, batch, groups, group_ch, height, width, kernel_h, kernel_w, pad_h, pad_w,
+                 dtype="f32", softmax=True, out_layout="nhwc"):
+        lib = _lib.load()
+        if dtype not in _DTYPES or out_layout not in _LAYOUTS:
+            raise ValueError("dtype in %s, out_layout in %s" % (list(_DTYPES), list(_LAYOUTS)))
+        self.B, self.G, self.D = batch, groups, group_ch
+        self.H, self.W, self.kh, self.kw = height, width, kernel_h, kernel_w
+        self.dtype, self.softmax, self.out_layout = dtype, bool(softmax), out_layout
+        d = _lib.DsDesc(batch, groups, group_ch, height, width, kernel_h, kernel_w, pad_h, pad_w,
+                        _DTYPES[dtype], int(bool(softmax)), _LAYOUTS[out_layout])
+        h = ctypes.c_void_p()
+        _lib.check(lib.dcn_dsample_create(ctypes.byref(d), ctypes.byref(h)), "dcn_dsample_create")
+        self._h = h
+        ho, wo = ctypes.c_int32(), ctypes.c_int32()
+        _lib.check(lib.dcn_dsample_output_size(h, ctypes.byref(ho), ctypes.byref(wo)),
+                   "dcn_dsample_output_size")
+        self.Ho, self.Wo = ho.value, wo.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.load().dcn_dsample_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    def out_shape(self):
+        C = self.G * self.D
+        return ((self.B, self.Ho, self.Wo, C) if self.out_layout == "nhwc"
+                else (self.B, C, self.Ho, self.Wo))
+
+    def forward(self, x, offset, weights, out=None, stream=None):
+        torch = _torch()
+        want = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        shapes = {"x": (self.B, self.H, self.W, self.G * self.D),
+                  "offset": (self.B, self.G * 2 * self.K, self.Ho, self.Wo),
+                  "weights": (self.B, self.G * self.K, self.Ho, self.Wo)}
+        for name, t in (("x", x), ("offset", offset), ("weights", weights)):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != want:
+                raise ValueError("%s must be a contiguous %s device tensor" % (name, want))
+            if tuple(t.shape) != shapes[name]:
+                raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
+                                                                    shapes[name]))
+        if out is None:
+            out = torch.empty(self.out_shape(), dtype=torch.float32, device="cuda")
+        if (tuple(out.shape) != self.out_shape() or out.dtype != torch.float32 or
+                not out.is_contiguous()):
+            raise ValueError("out must be a contiguous float32 tensor of shape %s"
+                             % (self.out_shape(),))
+        _lib.check(_lib.load().dcn_dsample_forward(self._h, _ptr(x), _ptr(offset),
+                                                   _ptr(weights), _ptr(out),
+                                                   ctypes.c_void_p(_stream_handle(stream))),
+                   "dcn_dsample_forward")
+        return out
+
+
+_DS_PLANS = {}
+
+
+def dsample(x, offset, weights, groups, kernel_size, padding=0, softmax=True, out_layout="nhwc"):
+    """Single-scale deformable sampling (page 5, DCNv3 form) on NHWC ``x``
+    [B,H,W,G*D]; ``kernel_size`` and ``padding`` an int or a pair."""
+    torch = _torch()
+    kh, kw = (kernel_size, kernel_size) if isinstance(kernel_size, int) else tuple(kernel_size)
+    ph, pw = (padding, padding) if isinstance(padding, int) else tuple(padding)
+    B, H, W, C = x.shape
+    if C % groups:
+        raise ValueError("channels %d are not a multiple of groups %d" % (C, groups))
+    dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(x.dtype)
+    if dtype is None:
+        raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
+    key = (B, groups, C // groups, H, W, kh, kw, ph, pw, dtype, bool(softmax), out_layout)
+    p = _DS_PLANS.get(key)
+    if p is None:
+        p = DsamplePlan(*key)
+        _DS_PLANS[key] = p
+    return p.forward(x, offset, weights)

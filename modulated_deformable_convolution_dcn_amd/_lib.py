@@ -26,7 +26,8 @@ EXPORTS = ("dcn_create", "dcn_destroy", "dcn_output_size", "dcn_workspace_bytes"
            "dcn_pack_weight", "dcn_forward_packed", "dcn_forward", "dcn_forward_rows",
            "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_backward_workspace_bytes",
            "dcn_backward", "dcn_msda_create", "dcn_msda_destroy", "dcn_msda_value_positions",
-           "dcn_msda_forward", "dcn_forward_noalloc", "dcn_debug_coords", "dcn_debug_corner_table",
+           "dcn_msda_forward", "dcn_dsample_create", "dcn_dsample_destroy",
+           "dcn_dsample_output_size", "dcn_dsample_forward", "dcn_forward_noalloc", "dcn_debug_coords", "dcn_debug_corner_table",
            "dcn_status_string", "dcn_last_error",
            "dcn_version")
 
@@ -41,6 +42,12 @@ class MsdaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_queries", "num_heads", "head_dim", "num_levels", "num_points", "dtype",
         "softmax")]
+
+
+class DsDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "groups", "group_ch", "height", "width", "kernel_h", "kernel_w", "pad_h",
+        "pad_w", "dtype", "softmax", "out_layout")]
 
 
 class DcnError(RuntimeError):
@@ -86,6 +93,10 @@ def load():
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(sz),
                                    ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
         "dcn_forward_noalloc": (st, [vp, vp, vp, vp, vp, vp, vp, vp]),
+        "dcn_dsample_create": (st, [ctypes.POINTER(DsDesc), ctypes.POINTER(vp)]),
+        "dcn_dsample_destroy": (st, [vp]),
+        "dcn_dsample_output_size": (st, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "dcn_dsample_forward": (st, [vp, vp, vp, vp, vp, vp]),
         "dcn_debug_coords": (st, [vp, vp, vp, vp, vp]),
         "dcn_debug_corner_table": (st, [vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp]),
         "dcn_status_string": (ctypes.c_char_p, [st]),

@@ -26,6 +26,13 @@ struct dcn_msda_plan_s {
   int H[dcn::kMsdaMaxLevels], W[dcn::kMsdaMaxLevels], start[dcn::kMsdaMaxLevels];
 };
 
+struct dcn_dsample_plan_s {
+  dcn_dsample_desc d;
+  int K, Ho, Wo;
+  int tiles_per_img, n_ctiles;
+  uint32_t x_bytes, offset_bytes, weights_bytes;
+};
+
 struct dcn_plan_s {
   dcn_desc d;
   int K, Ho, Wo;
@@ -633,6 +640,111 @@ dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* l
     return ok();
   } catch (...) {
     return fail(DCN_E_INTERNAL, "dcn_msda_forward: unexpected exception");
+  }
+}
+
+dcn_status dcn_dsample_create(const dcn_dsample_desc* desc, dcn_dsample_plan* plan) {
+  try {
+    if (plan) *plan = nullptr;
+    if (!desc || !plan) return fail(DCN_E_NULL, "dcn_dsample_create: NULL argument");
+    const dcn_dsample_desc& d = *desc;
+    if (d.dtype != DCN_F32 && d.dtype != DCN_BF16)
+      return fail(DCN_E_DTYPE, "dcn_dsample_create: dtype %d", d.dtype);
+    if (d.out_layout != DCN_OUT_NCHW && d.out_layout != DCN_OUT_NHWC)
+      return fail(DCN_E_DTYPE, "dcn_dsample_create: out_layout %d", d.out_layout);
+    if (d.batch < 0 || d.groups < 1 || d.group_ch < 1 || d.height < 1 || d.width < 1 ||
+        d.kernel_h < 1 || d.kernel_w < 1 || d.pad_h < 0 || d.pad_w < 0)
+      return fail(DCN_E_SHAPE, "dcn_dsample_create: sizes must satisfy B>=0, G,D,H,W,kh,kw>=1, "
+                               "pad>=0");
+    const int64_t Ho = (int64_t)d.height + 2 * (int64_t)d.pad_h - d.kernel_h + 1;
+    const int64_t Wo = (int64_t)d.width + 2 * (int64_t)d.pad_w - d.kernel_w + 1;
+    if (Ho < 1 || Wo < 1) return fail(DCN_E_SHAPE, "dcn_dsample_create: empty output");
+    const int64_t E = d.dtype == DCN_BF16 ? 2 : 4;
+    if (d.group_ch % (16 / E) != 0)
+      return fail(DCN_E_UNSUPPORTED, "dcn_dsample_create: group_ch %d must be a multiple of %d "
+                                     "(16-byte channel vectors)", d.group_ch, (int)(16 / E));
+    const int64_t C = (int64_t)d.groups * d.group_ch, K = (int64_t)d.kernel_h * d.kernel_w;
+    const int64_t HoWo = Ho * Wo;
+    const int64_t xb = (int64_t)d.batch * d.height * d.width * C * E;
+    const int64_t ob = (int64_t)d.batch * d.groups * 2 * K * HoWo * E;
+    if (xb >= kLimit31 || ob >= kLimit31 || (int64_t)d.batch * C * HoWo >= kLimit31 ||
+        K >= kLimit31 / 2 || HoWo >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "dcn_dsample_create: tensors must stay below 2^31 bytes / "
+                                     "elements");
+    std::unique_ptr<dcn_dsample_plan_s> p(new dcn_dsample_plan_s{});
+    p->d = d;
+    p->K = (int)K;
+    p->Ho = (int)Ho;
+    p->Wo = (int)Wo;
+    p->tiles_per_img = (int)ceil_div(HoWo, 64);
+    const int ct = dcn::dsample_vectors_per_tile((int)C, d.dtype == DCN_BF16) * (int)(16 / E);
+    p->n_ctiles = (int)ceil_div(C, ct);
+    if ((int64_t)d.batch * p->tiles_per_img * p->n_ctiles >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "dcn_dsample_create: too many tiles");
+    p->x_bytes = (uint32_t)xb;
+    p->offset_bytes = (uint32_t)ob;
+    p->weights_bytes = (uint32_t)(ob / 2);
+    *plan = p.release();
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_dsample_create: unexpected exception");
+  }
+}
+
+dcn_status dcn_dsample_destroy(dcn_dsample_plan plan) {
+  delete plan;
+  return ok();
+}
+
+dcn_status dcn_dsample_output_size(dcn_dsample_plan plan, int32_t* ho, int32_t* wo) {
+  if (!plan) return fail(DCN_E_NULL, "dcn_dsample_output_size: plan is NULL");
+  if (ho) *ho = plan->Ho;
+  if (wo) *wo = plan->Wo;
+  return ok();
+}
+
+dcn_status dcn_dsample_forward(dcn_dsample_plan plan, const void* x, const void* offset,
+                               const void* weights, void* out, void* stream) {
+  try {
+    if (!plan) return fail(DCN_E_NULL, "dcn_dsample_forward: plan is NULL");
+    const dcn_dsample_desc& d = plan->d;
+    if (d.batch == 0) return ok();
+    if (!x || !offset || !weights || !out)
+      return fail(DCN_E_NULL, "dcn_dsample_forward: x, offset, weights and out are required");
+    const size_t E = d.dtype == DCN_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(offset, E) || !aligned(weights, E))
+      return fail(DCN_E_ALIGN, "dcn_dsample_forward: x and out must be 16-byte aligned, offset "
+                               "and weights %zu-byte", E);
+    dcn::DsArgs a{};
+    a.x = x;
+    a.offset = offset;
+    a.weights = weights;
+    a.out = static_cast<float*>(out);
+    a.B = d.batch;
+    a.G = d.groups;
+    a.D = d.group_ch;
+    a.H = d.height;
+    a.W = d.width;
+    a.kh = d.kernel_h;
+    a.kw = d.kernel_w;
+    a.K = plan->K;
+    a.ph = d.pad_h;
+    a.pw = d.pad_w;
+    a.Ho = plan->Ho;
+    a.Wo = plan->Wo;
+    a.HoWo = plan->Ho * plan->Wo;
+    a.softmax = d.softmax ? 1 : 0;
+    a.tiles_per_img = plan->tiles_per_img;
+    a.n_ctiles = plan->n_ctiles;
+    a.x_bytes = plan->x_bytes;
+    a.offset_bytes = plan->offset_bytes;
+    a.weights_bytes = plan->weights_bytes;
+    hipError_t e = dcn::launch_dsample(a, d.dtype == DCN_BF16, d.out_layout == DCN_OUT_NHWC,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dsample launch");
+    return ok();
+  } catch (...) {
+    return fail(DCN_E_INTERNAL, "dcn_dsample_forward: unexpected exception");
   }
 }
 

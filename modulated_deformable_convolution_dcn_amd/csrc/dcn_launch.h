@@ -90,6 +90,24 @@ struct MsdaArgs {
 };
 hipError_t launch_msda(const MsdaArgs& a, hipStream_t stream);
 
+// Single-scale deformable sampling (dcn_dsample.hip): x [B,H,W,G*D] NHWC,
+// offset [B,G*2K,Ho,Wo] (channel (g*K + k)*2 = dy), weights [B,G*K,Ho,Wo]
+// (logits when softmax), out [B,Ho,Wo,G*D] or [B,G*D,Ho,Wo] fp32.
+struct DsArgs {
+  const void* x;
+  const void* offset;
+  const void* weights;
+  float* out;
+  int B, G, D, H, W, kh, kw, K, ph, pw, Ho, Wo, HoWo;
+  int softmax;
+  int tiles_per_img;   // ceil(Ho*Wo / 64)
+  int n_ctiles;        // channel tiles of dsample_vectors_per_tile() vectors
+  uint32_t x_bytes, offset_bytes, weights_bytes;
+};
+// 16-byte vectors per workgroup channel tile (4, 8 or 16) for C channels.
+int dsample_vectors_per_tile(int C, int bf16);
+hipError_t launch_dsample(const DsArgs& a, int bf16, int nhwc, hipStream_t stream);
+
 // Several branches (same input map, own offsets/mask/weight/bias/output and
 // kernel size) in one launch: branch i owns the logical workgroups
 // [start[i], start[i+1]).

@@ -1,0 +1,116 @@
+"""GPU parity of single-scale deformable sampling (dcn_dsample_forward, page 5's
+DCNv3 form) against the oracle, element by element.
+
+Per output element: |gpu - ref| <= 1e-4 * N + ulp32(|ref|), N the oracle's
+absolute-term sum (sum_k |a| sum_corners w |x|); N == 0 must give exactly 0.
+The bf16 path takes bf16 operands but blends and accumulates in fp32 without
+rounding anything to bf16, so the fp32 bound applies to it too.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dcn_testlib import bound_used, record_margin
+from modulated_deformable_convolution_dcn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+S = synth.DS_WORKLOADS
+P5 = S["dcnv3_page5_fp32"]
+CASES = {
+    "page5_fp32": P5,
+    "page5_given_weights": P5.scaled(softmax=False, seed=41),
+    "page5_bf16": P5.scaled(dtype="bf16", seed=42),
+    "map256_fp32": S["dcnv3_map256_fp32"],
+    "map256_bf16": S["dcnv3_map256_bf16"],
+    # odd group sizes and channel counts: 3 x 12 (vectors of one group in two
+    # tiles' worth of lanes), 5 x 16 = 80 channels (two channel tiles, the
+    # second ragged), 2 x 80 (a group spanning both tiles), bf16 8 channels
+    "g3_d12_k5": P5.scaled(G=3, D=12, H=13, W=11, kh=5, kw=5, ph=2, pw=2, seed=43),
+    "g5_d16_b2": P5.scaled(B=2, G=5, D=16, H=9, W=14, seed=44),
+    "g2_d80_k1": P5.scaled(G=2, D=80, H=7, W=9, kh=1, kw=1, ph=0, pw=0, seed=45),
+    "g1_d8_bf16_k2x3": P5.scaled(G=1, D=8, H=10, W=12, kh=2, kw=3, ph=0, pw=1, dtype="bf16",
+                                 seed=46),
+    "g4_d32_bf16": P5.scaled(G=4, D=32, H=12, W=12, dtype="bf16", softmax=False, seed=47),
+    "far_outside": P5.scaled(H=8, W=8, offset_std=40.0, seed=48),
+}
+
+
+def _device(spec, d):
+    import torch
+    out = {}
+    for k in ("x", "offset", "weights"):
+        if spec.dtype == "f32":
+            out[k] = torch.from_numpy(d[k]).cuda()
+        else:
+            out[k] = torch.from_numpy(d["bits"][k].astype(np.int16)).cuda().view(torch.bfloat16)
+    return out
+
+
+def _run(spec, d, layout):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import DsamplePlan
+    dev = _device(spec, d)
+    plan = DsamplePlan(spec.B, spec.G, spec.D, spec.H, spec.W, spec.kh, spec.kw, spec.ph, spec.pw,
+                       spec.dtype, spec.softmax, layout)
+    out = plan.forward(dev["x"], dev["offset"], dev["weights"])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    return got if layout == "nhwc" else got.transpose(0, 2, 3, 1)
+
+
+def _check(got, ref, norm, what):
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    zero = norm == 0
+    assert not (zero & (got != 0)).any(), "%s: outputs with no terms are not 0" % what
+    bound = 1e-4 * norm + ulp
+    bad = (~zero) & (err > bound)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d / %d outside tolerance; first %s gpu %.9g ref %.9g N %.3g"
+                             % (what, int(bad.sum()), bad.size, i, got[i], ref[i], norm[i]))
+    nz = ~zero
+    worst = float((err[nz] / norm[nz]).max()) if nz.any() else 0.0
+    record_margin("dsample " + what, got.size, worst, 1e-4, bound_used(err, bound, nz))
+    return worst
+
+
+def _oracle(spec, d):
+    s = oracle.DsShape(spec.B, spec.G, spec.D, spec.H, spec.W, spec.kh, spec.kw, spec.ph, spec.pw)
+    return oracle.dsample(s, d["x"], d["offset"], d["weights"], spec.softmax)
+
+
+@pytest.mark.parametrize("layout", ["nhwc", "nchw"])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_dsample_parity(name, layout):
+    spec = CASES[name]
+    d = synth.make_ds_inputs(spec)
+    print("case", name, layout, spec, flush=True)
+    ref, norm = _oracle(spec, d)
+    got = _run(spec, d, layout)
+    print("worst err/N %.3g" % _check(got, ref, norm, "%s/%s" % (name, layout)))
+
+
+def test_dsample_layouts_agree_bitwise_and_repeat():
+    spec = S["dcnv3_map256_fp32"]
+    d = synth.make_ds_inputs(spec)
+    a = _run(spec, d, "nhwc")
+    b = _run(spec, d, "nchw")
+    c = _run(spec, d, "nhwc")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_dsample_zero_weights_and_all_outside_give_zero():
+    spec = P5.scaled(H=10, W=10, softmax=False, seed=49)
+    d = synth.make_ds_inputs(spec)
+    d0 = dict(d)
+    d0["weights"] = np.zeros_like(d["weights"])
+    assert not _run(spec, d0, "nhwc").any()
+    d1 = dict(d)
+    d1["offset"] = np.full_like(d["offset"], 1000.0)
+    assert not _run(spec, d1, "nchw").any()
