@@ -127,8 +127,12 @@ def bench_msda(args, torch, synth) -> int:
     from modulated_deformable_convolution_dcn_amd import MsdaPlan
     spec = synth.MSDA_WORKLOADS[args.msda]
     d = synth.make_msda_inputs(spec)
-    dev = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
-    plan = MsdaPlan(spec.B, spec.Q, spec.G, spec.D, spec.shapes, spec.K, spec.softmax)
+    if spec.dtype == "f32":
+        dev = {k: torch.from_numpy(d[k]).cuda() for k in ("value", "locations", "weights")}
+    else:
+        dev = {k: torch.from_numpy(d["bits"][k].astype("int16")).cuda().view(torch.bfloat16)
+               for k in ("value", "locations", "weights")}
+    plan = MsdaPlan(spec.B, spec.Q, spec.G, spec.D, spec.shapes, spec.K, spec.softmax, spec.dtype)
     out = torch.empty((spec.B, spec.Q, spec.G * spec.D), device="cuda")
     for _ in range(args.warmup):
         plan.forward(dev["value"], dev["locations"], dev["weights"], out)
@@ -146,15 +150,16 @@ def bench_msda(args, torch, synth) -> int:
     ms = elapsed * 1e3 / args.steps
     pairs = spec.B * spec.Q * spec.G
     points = pairs * spec.L * spec.K
-    # compulsory bytes: value read once, locations, weights, output
-    compulsory = 4 * (spec.B * spec.S * spec.G * spec.D + points * 2 + points + pairs * spec.D)
-    gathered = points * 4 * spec.D * 4  # four corner vectors per point
+    # compulsory bytes: value read once, locations, weights, fp32 output
+    e = 2 if spec.dtype == "bf16" else 4
+    compulsory = e * (spec.B * spec.S * spec.G * spec.D + points * 2 + points) + 4 * pairs * spec.D
+    gathered = points * 4 * spec.D * e  # four corner vectors per point
     hbm = compulsory / (kern_ms * 1e-3) / 1e9
     gather_gbs = gathered / (kern_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "msda sampling points/s", "value": points / (ms * 1e-3), "unit": "points/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
         "data": "synthetic",
         "config": {"workload": spec.name, "B": spec.B, "Q": spec.Q, "G": spec.G, "D": spec.D,
                    "levels": [list(x) for x in spec.shapes], "K": spec.K,
@@ -299,7 +304,7 @@ def main() -> int:
                     help="time the fp32 backward (all five gradients) instead of the forward")
     ap.add_argument("--msda", metavar="WORKLOAD", default=None,
                     help="time multi-scale deformable attention sampling on this workload "
-                         "(msda_encoder_fp32, msda_decoder_fp32) instead")
+                         "(msda_encoder_fp32, msda_decoder_fp32, msda_encoder_bf16) instead")
     ap.add_argument("--dsample", metavar="WORKLOAD", default=None,
                     help="time single-scale deformable sampling on this workload "
                          "(dcnv3_page5_fp32, dcnv3_map256_fp32, dcnv3_map256_bf16) instead")

@@ -228,15 +228,18 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
  *   out[b,q,g,:] = sum_{l,k} a * bilinear(level l, head g, at
  *                  (x * W_l - 0.5, y * H_l - 0.5) pixels)
  * with each product / difference of the pixel coordinate rounded to fp32
- * and corners outside the level counting as zero.  fp32 only; L <= 8,
- * K <= 8, D a multiple of 4 (<= 1024).  level_hw is a HOST array [L][2] of
+ * and corners outside the level counting as zero.  value, locations and
+ * weights share the plan's dtype (DCN_F32 or DCN_BF16; page 5: half
+ * precision throughout); bf16 values are widened exactly, blending and
+ * accumulation are fp32 and out is fp32.  L <= 8, K <= 8, D a multiple of 4
+ * (fp32) or 8 (bf16), at most 1024.  level_hw is a HOST array [L][2] of
  * (H_l, W_l) copied into the plan.  The value buffer must hold exactly S
  * positions (dcn_msda_value_positions).
  */
 typedef struct dcn_msda_plan_s* dcn_msda_plan;
 typedef struct {
   int32_t batch, num_queries, num_heads, head_dim, num_levels, num_points;
-  int32_t dtype;    /* DCN_F32 */
+  int32_t dtype;    /* DCN_F32 or DCN_BF16: value, locations and weights */
   int32_t softmax;  /* 0: weights as given; 1: softmax of logits */
 } dcn_msda_desc;
 dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
@@ -244,7 +247,7 @@ dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
 dcn_status dcn_msda_destroy(dcn_msda_plan plan);
 dcn_status dcn_msda_value_positions(dcn_msda_plan plan, int32_t* positions);
 /* One kernel launch on `stream`; value and out 16-byte aligned, locations
- * 8-byte, weights 4-byte; no input may overlap out. */
+ * and weights element-aligned; no input may overlap out. */
 dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* locations,
                             const void* weights, void* out, void* stream);
 

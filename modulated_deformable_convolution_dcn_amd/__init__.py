@@ -353,15 +353,18 @@ class MsdaPlan:
     """``dcn_msda_create``: multi-scale deformable attention sampling of one size."""
 
     def __init__(self, batch, num_queries, num_heads, head_dim, shapes, num_points,
-                 softmax=False):
+                 softmax=False, dtype="f32"):
         lib = _lib.load()
+        if dtype not in _DTYPES:
+            raise ValueError("dtype must be one of %s" % list(_DTYPES))
+        self.dtype = dtype
         shapes = [(int(h), int(w)) for h, w in shapes]
         self.shapes = shapes
         self.B, self.Q, self.G, self.D = batch, num_queries, num_heads, head_dim
         self.L, self.K = len(shapes), num_points
         self.softmax = bool(softmax)
         d = _lib.MsdaDesc(batch, num_queries, num_heads, head_dim, len(shapes), num_points,
-                          _lib.DCN_F32, int(bool(softmax)))
+                          _DTYPES[dtype], int(bool(softmax)))
         hw = (ctypes.c_int32 * (2 * len(shapes)))(*[v for s in shapes for v in s])
         h = ctypes.c_void_p()
         _lib.check(lib.dcn_msda_create(ctypes.byref(d), hw, ctypes.byref(h)), "dcn_msda_create")
@@ -380,15 +383,16 @@ class MsdaPlan:
             self._h = None
 
     def forward(self, value, locations, weights, out=None, stream=None):
-        """value [B,S,G,D], locations [B,Q,G,L,K,2], weights [B,Q,G,L*K] (fp32 device
-        tensors) -> out [B,Q,G*D] fp32."""
+        """value [B,S,G,D], locations [B,Q,G,L,K,2], weights [B,Q,G,L*K] (device
+        tensors of the plan's dtype) -> out [B,Q,G*D] fp32."""
         torch = _torch()
+        want = torch.float32 if self.dtype == "f32" else torch.bfloat16
         shapes = {"value": (self.B, self.S, self.G, self.D),
                   "locations": (self.B, self.Q, self.G, self.L, self.K, 2),
                   "weights": (self.B, self.Q, self.G, self.L * self.K)}
         for name, t in (("value", value), ("locations", locations), ("weights", weights)):
-            if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
-                raise ValueError("%s must be a contiguous float32 device tensor" % name)
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != want:
+                raise ValueError("%s must be a contiguous %s device tensor" % (name, want))
             if tuple(t.shape) != shapes[name]:
                 raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
                                                                     shapes[name]))
@@ -411,12 +415,16 @@ def msda(value, shapes, locations, weights, softmax=False):
     """Multi-scale deformable attention sampling (page 5's functional form):
     value [B,S,G,D], shapes [(H, W), ...], locations [B,Q,G,L,K,2] normalised
     (x, y), weights [B,Q,G,L*K] (logits when ``softmax``) -> [B,Q,G*D]."""
+    torch = _torch()
     B, S, G, D = value.shape
     _, Q, _, L, K, _ = locations.shape
-    key = (B, Q, G, D, tuple((int(h), int(w)) for h, w in shapes), K, bool(softmax))
+    dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(value.dtype)
+    if dtype is None:
+        raise ValueError("value must be float32 or bfloat16, got %s" % value.dtype)
+    key = (B, Q, G, D, tuple((int(h), int(w)) for h, w in shapes), K, bool(softmax), dtype)
     p = _MSDA_PLANS.get(key)
     if p is None:
-        p = MsdaPlan(B, Q, G, D, shapes, K, softmax)
+        p = MsdaPlan(B, Q, G, D, shapes, K, softmax, dtype)
         _MSDA_PLANS[key] = p
     return p.forward(value, locations, weights)
 

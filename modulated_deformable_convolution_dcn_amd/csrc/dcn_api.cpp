@@ -559,13 +559,15 @@ dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
     if (d.batch < 0 || d.num_queries < 0 || d.num_heads <= 0 || d.head_dim <= 0 ||
         d.num_levels <= 0 || d.num_points <= 0)
       return fail(DCN_E_SHAPE, "dcn_msda_create: sizes must be positive (batch, queries >= 0)");
-    if (d.dtype != DCN_F32) return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: fp32 only");
+    if (d.dtype != DCN_F32 && d.dtype != DCN_BF16)
+      return fail(DCN_E_DTYPE, "dcn_msda_create: dtype %d", d.dtype);
+    const int vec = d.dtype == DCN_BF16 ? 8 : 4;
     if (d.num_levels > dcn::kMsdaMaxLevels || d.num_points > dcn::kMsdaMaxPoints)
       return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: at most %d levels and %d points",
                   dcn::kMsdaMaxLevels, dcn::kMsdaMaxPoints);
-    if (d.head_dim % 4 != 0 || d.head_dim > 1024)
-      return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: head_dim %d must be a multiple of 4, "
-                                     "at most 1024", d.head_dim);
+    if (d.head_dim % vec != 0 || d.head_dim > 1024)
+      return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: head_dim %d must be a multiple of %d, "
+                                     "at most 1024", d.head_dim, vec);
     std::unique_ptr<dcn_msda_plan_s> p(new dcn_msda_plan_s{});
     p->d = d;
     int64_t S = 0;
@@ -579,7 +581,8 @@ dcn_status dcn_msda_create(const dcn_msda_desc* desc, const int32_t* level_hw,
       if (S >= kLimit31) return fail(DCN_E_UNSUPPORTED, "dcn_msda_create: too many positions");
     }
     p->S = (int)S;
-    const int64_t vbytes = (int64_t)d.batch * S * d.num_heads * d.head_dim * 4;
+    const int64_t vbytes =
+        (int64_t)d.batch * S * d.num_heads * d.head_dim * (d.dtype == DCN_BF16 ? 2 : 4);
     const int64_t pairs = (int64_t)d.batch * d.num_queries * d.num_heads;
     if (vbytes >= kLimit31 || pairs * d.head_dim >= kLimit31 ||
         pairs * d.num_levels * d.num_points * 2 >= kLimit31)
@@ -612,13 +615,15 @@ dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* l
     if (pairs == 0) return ok();
     if (!value || !locations || !weights || !out)
       return fail(DCN_E_NULL, "dcn_msda_forward: value, locations, weights and out are required");
-    if (!aligned(value, 16) || !aligned(out, 16) || !aligned(locations, 8) || !aligned(weights, 4))
+    const size_t E = d.dtype == DCN_BF16 ? 2 : 4;
+    if (!aligned(value, 16) || !aligned(out, 16) || !aligned(locations, E) ||
+        !aligned(weights, E))
       return fail(DCN_E_ALIGN, "dcn_msda_forward: value and out must be 16-byte aligned, "
-                               "locations 8-byte");
+                               "locations and weights %zu-byte", E);
     dcn::MsdaArgs a{};
-    a.value = static_cast<const float*>(value);
-    a.locations = static_cast<const float*>(locations);
-    a.weights = static_cast<const float*>(weights);
+    a.value = value;
+    a.locations = locations;
+    a.weights = weights;
     a.out = static_cast<float*>(out);
     a.npairs = pairs;
     a.B = d.batch;
@@ -634,8 +639,8 @@ dcn_status dcn_msda_forward(dcn_msda_plan plan, const void* value, const void* l
       a.W[l] = plan->W[l];
       a.start[l] = plan->start[l];
     }
-    a.value_bytes = (uint32_t)((int64_t)d.batch * plan->S * d.num_heads * d.head_dim * 4);
-    hipError_t e = dcn::launch_msda(a, static_cast<hipStream_t>(stream));
+    a.value_bytes = (uint32_t)((int64_t)d.batch * plan->S * d.num_heads * d.head_dim * E);
+    hipError_t e = dcn::launch_msda(a, d.dtype == DCN_BF16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "msda launch");
     return ok();
   } catch (...) {

@@ -79,16 +79,16 @@ hipError_t launch_backward(const BwdArgs& a, const float* weight, float* workspa
 constexpr int kMsdaMaxLevels = 8;
 constexpr int kMsdaMaxPoints = 8;
 struct MsdaArgs {
-  const float* value;      // [B, S, G, D]
-  const float* locations;  // [B, Q, G, L, K, 2] normalised (x, y)
-  const float* weights;    // [B, Q, G, L*K]
+  const void* value;       // [B, S, G, D]               operand dtype
+  const void* locations;   // [B, Q, G, L, K, 2] normalised (x, y), operand dtype
+  const void* weights;     // [B, Q, G, L*K]             operand dtype
   float* out;              // [B, Q, G, D]
   int64_t npairs;          // B * Q * G
   int B, S, G, D, Q, L, K, softmax;
   int H[kMsdaMaxLevels], W[kMsdaMaxLevels], start[kMsdaMaxLevels];
   uint32_t value_bytes;
 };
-hipError_t launch_msda(const MsdaArgs& a, hipStream_t stream);
+hipError_t launch_msda(const MsdaArgs& a, int bf16, hipStream_t stream);
 
 // Single-scale deformable sampling (dcn_dsample.hip): x [B,H,W,G*D] NHWC,
 // offset [B,G*2K,Ho,Wo] (channel (g*K + k)*2 = dy), weights [B,G*K,Ho,Wo]

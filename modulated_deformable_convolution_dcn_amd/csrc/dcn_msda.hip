@@ -1,4 +1,5 @@
-// dcn_msda.hip -- multi-scale deformable attention sampling (fp32).
+// dcn_msda.hip -- multi-scale deformable attention sampling (fp32 or bf16
+// operands, fp32 accumulation and output).
 //
 // Page 5 (deformops README, "Multi-scale deformable attention"): value
 // (B, sum_l H_l W_l, G, D) holds L flattened feature maps, locations
@@ -14,28 +15,49 @@
 // rounded to fp32 (no fused multiply-add); corners outside the level count as
 // zero.
 //
-// One workgroup handles 32 (b, q, g) pairs:
+// One workgroup handles NP (b, q, g) pairs (32 for fp32, 64 for bf16, so
+// that the gather's D/VEC lanes per pair fill the workgroup either way):
 //   (a) coefficient stage: every (pair, point) gets its four corner weights
 //       (attention x bilinear x validity) and corner byte offsets in an LDS
-//       table (the softmax, when asked for, is reduced over the 8 threads of
-//       a pair first);
-//   (b) gather: D/4 lanes per pair each own 16 bytes of the head's D
-//       channels; per point they read the table entry (a broadcast), issue
-//       the four 16-byte corner loads (buffer loads: an outside corner reads
-//       zero) and accumulate; one 16-byte store per lane.
+//       table (the softmax, when asked for, is reduced over the 256/NP
+//       threads of a pair first);
+//   (b) gather: D/VEC lanes per pair each own 16 bytes (VEC = 4 fp32 or 8
+//       bf16 channels) of the head's D channels; per point they read the
+//       table entry (a broadcast), issue the four 16-byte corner loads
+//       (buffer loads: an outside corner reads zero) and accumulate in fp32;
+//       one or two 16-byte fp32 stores per lane.
+// bf16 operands (page 5: half precision throughout) are widened exactly to
+// fp32; nothing is rounded back to bf16.
 
 #include "dcn_device.h"
 #include "dcn_launch.h"
 
 namespace dcn {
 
-namespace {
-constexpr int NPAIR = 32;   // (b, q, g) pairs per workgroup
-constexpr int TPP = 256 / NPAIR;  // coefficient threads per pair
-}  // namespace
+template <class T>
+__device__ __forceinline__ void msda_acc(float* acc, float w, u32x4 v);
+template <>
+__device__ __forceinline__ void msda_acc<float>(float* acc, float w, u32x4 v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w, __uint_as_float(v[c]), acc[c]);
+}
+template <>
+__device__ __forceinline__ void msda_acc<__bf16>(float* acc, float w, u32x4 v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] = __builtin_fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);
+    acc[2 * q + 1] = __builtin_fmaf(w, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+  }
+}
 
+template <class T, int NPAIR>
 __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
+  constexpr int TPP = 256 / NPAIR;  // coefficient threads per pair
   constexpr int MAXLK = kMsdaMaxLevels * kMsdaMaxPoints;
+  constexpr int E = sizeof(T);
+  constexpr int VEC = 16 / E;  // channels per 16-byte lane load
+  const T* const wts = static_cast<const T*>(a.weights);
+  const T* const locs = static_cast<const T*>(a.locations);
   // the table, sized by the launch for this problem's L * K points per pair
   // (a smaller table leaves room for more workgroups per CU):
   // Cw [NPAIR * LK] corner weights, then Co [NPAIR * LK] corner byte offsets
@@ -66,7 +88,7 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
 #pragma unroll
     for (int r = 0; r < MAXLK / TPP; ++r) {
       const int e = sub + TPP * r;
-      logit[r] = (r < npt && e < LK && pin) ? a.weights[n * LK + e] : -INFINITY;
+      logit[r] = (r < npt && e < LK && pin) ? to_f32<T>(wts[n * LK + e]) : -INFINITY;
       mx = fmaxf(mx, logit[r]);
     }
     float sum = 0.f;
@@ -91,7 +113,8 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
       u32x4 o4 = {kNoCorner, kNoCorner, kNoCorner, kNoCorner};
       if (pin) {
         const float att = a.softmax ? expf(logit[r] - mx) / sum : logit[r];
-        const float x = a.locations[(n * LK + e) * 2], y = a.locations[(n * LK + e) * 2 + 1];
+        const float x = to_f32<T>(locs[(n * LK + e) * 2]);
+        const float y = to_f32<T>(locs[(n * LK + e) * 2 + 1]);
         const float px = __fsub_rn(__fmul_rn(x, (float)W), 0.5f);
         const float py = __fsub_rn(__fmul_rn(y, (float)H), 0.5f);
         const float x0 = floorf(px), y0 = floorf(py);
@@ -106,7 +129,7 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
           if (ok) {
             w4[q] = att * wv[q];
             const int64_t pix = (int64_t)st + (int64_t)(iy + (q >> 1)) * W + ix + (q & 1);
-            o4[q] = (uint32_t)(((b * a.S + pix) * a.G + g) * a.D * 4);
+            o4[q] = (uint32_t)(((b * a.S + pix) * a.G + g) * a.D * E);
           }
         }
       }
@@ -116,9 +139,9 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
   }
   __syncthreads();
 
-  // ---- (b) gather: lanes per pair = D / 4
+  // ---- (b) gather: lanes per pair = D / VEC
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.value, a.value_bytes);
-  const int lpp = a.D >> 2;
+  const int lpp = a.D / VEC;
   const int ppp = 256 / lpp;  // pairs per pass
   const int pr = tid / lpp, sl = tid - (tid / lpp) * lpp;
   for (int p0 = 0; p0 < NPAIR; p0 += ppp) {
@@ -126,7 +149,9 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
     if (pr >= ppp || pl >= NPAIR) continue;
     const int64_t n = n0 + pl;
     if (n >= a.npairs) continue;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
     const uint32_t lb = (uint32_t)sl * 16u;
     int e = 0;
     for (; e + 4 <= LK; e += 4) {  // four points (16 loads) in flight
@@ -142,33 +167,39 @@ __global__ __launch_bounds__(256) void msda_kernel(MsdaArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 f = __builtin_bit_cast(f32x4, v[u][q]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w[u][q], f[c], acc[c]);
-        }
+        for (int q = 0; q < 4; ++q) msda_acc<T>(acc, w[u][q], v[u][q]);
     }
     for (; e < LK; ++e) {
       const u32x4 o = Co[pl * LK + e];
       const f32x4 w = Cw[pl * LK + e];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 f = __builtin_bit_cast(f32x4, load16(vr, o[q] + lb));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w[q], f[c], acc[c]);
-      }
+      for (int q = 0; q < 4; ++q) msda_acc<T>(acc, w[q], load16(vr, o[q] + lb));
     }
-    *reinterpret_cast<f32x4*>(a.out + n * a.D + 4 * sl) = acc;
+    float* dst = a.out + n * a.D + VEC * sl;
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h)
+      *reinterpret_cast<f32x4*>(dst + 4 * h) =
+          f32x4{acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]};
   }
 }
 
-hipError_t launch_msda(const MsdaArgs& a, hipStream_t s) {
+hipError_t launch_msda(const MsdaArgs& a, int bf16, hipStream_t s) {
+  const int LK = a.L * a.K;
+  // 64 pairs for bf16 when the table (64 * LK * 32 bytes) stays within 64 KB
+  const int NPAIR = bf16 && LK <= 32 ? 64 : 32;
   const int64_t nblk = (a.npairs + NPAIR - 1) / NPAIR;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const int LK = a.L * a.K;
   if (LK < 1 || LK > kMsdaMaxLevels * kMsdaMaxPoints) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(msda_kernel, dim3((unsigned)nblk), dim3(256), (size_t)NPAIR * LK * 32, s, a);
+  if (bf16 && NPAIR == 64)
+    hipLaunchKernelGGL((msda_kernel<__bf16, 64>), dim3((unsigned)nblk), dim3(256),
+                       (size_t)NPAIR * LK * 32, s, a);
+  else if (bf16)
+    hipLaunchKernelGGL((msda_kernel<__bf16, 32>), dim3((unsigned)nblk), dim3(256),
+                       (size_t)NPAIR * LK * 32, s, a);
+  else
+    hipLaunchKernelGGL((msda_kernel<float, 32>), dim3((unsigned)nblk), dim3(256),
+                       (size_t)NPAIR * LK * 32, s, a);
   return hipGetLastError();
 }
 

@@ -193,6 +193,7 @@ class MsdaSpec:
     seed: int
     loc_lo: float = -0.05   # locations ~ U(loc_lo, loc_hi): a few points fall outside
     loc_hi: float = 1.05
+    dtype: str = "f32"      # "f32" or "bf16": value, locations and weights
 
     @property
     def L(self) -> int:
@@ -214,19 +215,30 @@ MSDA_WORKLOADS = {
                                   ((64, 64), (32, 32), (16, 16), (8, 8)), 4, True, 21),
     "msda_decoder_fp32": MsdaSpec("msda_decoder_fp32", 8, 300, 8, 32,
                                   ((64, 64), (32, 32), (16, 16), (8, 8)), 4, True, 22),
+    # page 5 recommends bfloat16 for training: the encoder workload in bf16
+    "msda_encoder_bf16": MsdaSpec("msda_encoder_bf16", 4, 5440, 8, 32,
+                                  ((64, 64), (32, 32), (16, 16), (8, 8)), 4, True, 23,
+                                  dtype="bf16"),
 }
 
 
 def make_msda_inputs(spec: MsdaSpec) -> dict:
     """value ~ N(0,1) [B,S,G,D]; locations ~ U(loc_lo, loc_hi) [B,Q,G,L,K,2];
-    weights (logits) ~ N(0,1) [B,Q,G,L*K]; all float32, drawn in that order."""
+    weights (logits) ~ N(0,1) [B,Q,G,L*K]; drawn in that order, float32 (bf16-
+    rounded with ``bits`` when spec.dtype is "bf16")."""
     rng = np.random.default_rng(spec.seed)
     f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)  # noqa: E731
     value = f32(rng.standard_normal((spec.B, spec.S, spec.G, spec.D)))
     loc = f32(rng.uniform(spec.loc_lo, spec.loc_hi,
                           size=(spec.B, spec.Q, spec.G, spec.L, spec.K, 2)))
     w = f32(rng.standard_normal((spec.B, spec.Q, spec.G, spec.L * spec.K)))
-    return {"value": value, "locations": loc, "weights": w}
+    out = {"value": value, "locations": loc, "weights": w}
+    if spec.dtype == "bf16":
+        bits = {}
+        for k in list(out):
+            out[k], bits[k] = round_bf16(out[k])
+        out["bits"] = bits
+    return out
 
 
 @dataclass(frozen=True)

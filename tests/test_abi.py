@@ -282,6 +282,7 @@ def test_msda_create_validates_and_checks_pointers():
     h = p._h
     assert lib.dcn_msda_forward(h, None, fake, fake, fake, None) == 1
     assert lib.dcn_msda_forward(h, ctypes.c_void_p(0x10008), fake, fake, fake, None) == 5
-    assert lib.dcn_msda_forward(h, fake, ctypes.c_void_p(0x10004), fake, fake, None) == 5
+    assert lib.dcn_msda_forward(h, fake, ctypes.c_void_p(0x10002), fake, fake, None) == 5
+    assert lib.dcn_msda_forward(h, fake, fake, ctypes.c_void_p(0x10001), fake, None) == 5
     empty = MsdaPlan(0, 10, 8, 32, [(8, 8)], 4)
     assert lib.dcn_msda_forward(empty._h, None, None, None, None, None) == 0

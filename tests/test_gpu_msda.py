@@ -1,6 +1,8 @@
 """GPU parity of multi-scale deformable attention sampling (dcn_msda_forward)
 against the oracle: |gpu - ref| <= 1e-4 * N + ulp32(|ref|) per element, N the
-absolute-term sum; elements with N == 0 must be exactly 0."""
+absolute-term sum; elements with N == 0 must be exactly 0.  bf16 operands are
+widened exactly and blended in fp32 with nothing rounded back to bf16, so
+the same bound applies (the oracle reads the same bf16-rounded values)."""
 from __future__ import annotations
 
 import numpy as np
@@ -24,7 +26,24 @@ CASES = {
     "eight_levels_k1_d4": M["msda_decoder_fp32"].scaled(
         B=1, Q=17, G=5, D=4, K=1, shapes=tuple((2 + l, 3 + l) for l in range(8))),
     "far_outside": M["msda_decoder_fp32"].scaled(B=1, Q=20, loc_lo=1.6, loc_hi=3.0),
+    "decoder_small_bf16": M["msda_decoder_fp32"].scaled(B=2, Q=37, dtype="bf16", seed=51),
+    "odd_levels_k3_d16_bf16": M["msda_decoder_fp32"].scaled(
+        B=1, Q=41, G=3, D=16, K=3, shapes=((7, 11), (5, 3), (1, 9)), dtype="bf16", seed=52),
+    # 64 points per pair: the bf16 kernel with 32 pairs per workgroup
+    "eight_levels_k8_d8_bf16": M["msda_decoder_fp32"].scaled(
+        B=1, Q=19, G=2, D=8, K=8, shapes=tuple((3 + l, 2 + l) for l in range(8)), dtype="bf16",
+        seed=54),
+    "one_level_k8_d64_bf16": M["msda_decoder_fp32"].scaled(
+        B=1, Q=33, G=2, D=64, K=8, shapes=((13, 6),), dtype="bf16", softmax=False, seed=53),
 }
+
+
+def _device(spec, d):
+    import torch
+    if spec.dtype == "f32":
+        return {k: torch.from_numpy(d[k]).cuda() for k in ("value", "locations", "weights")}
+    return {k: torch.from_numpy(d["bits"][k].astype(np.int16)).cuda().view(torch.bfloat16)
+            for k in ("value", "locations", "weights")}
 
 
 def _check(got, ref, norm, what):
@@ -49,7 +68,7 @@ def test_msda_parity(name):
     d = synth.make_msda_inputs(spec)
     ref, norm = oracle.msda(d["value"], spec.shapes, d["locations"], d["weights"], spec.softmax)
     print("case", name, spec, flush=True)
-    dev = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
+    dev = _device(spec, d)
     out = msda(dev["value"], spec.shapes, dev["locations"], dev["weights"], softmax=spec.softmax)
     torch.cuda.synchronize()
     got = out.cpu().numpy().reshape(ref.shape)
@@ -65,7 +84,7 @@ def test_msda_full_size(name):
     d = synth.make_msda_inputs(spec)
     print("case", name, flush=True)
     ref, norm = oracle.msda(d["value"], spec.shapes, d["locations"], d["weights"], spec.softmax)
-    dev = {k: torch.from_numpy(v).cuda() for k, v in d.items()}
+    dev = _device(spec, d)
     out = msda(dev["value"], spec.shapes, dev["locations"], dev["weights"], softmax=spec.softmax)
     out2 = msda(dev["value"], spec.shapes, dev["locations"], dev["weights"], softmax=spec.softmax)
     torch.cuda.synchronize()
