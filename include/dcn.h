@@ -185,9 +185,9 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
                              const void* const* packed_weights, const size_t* workspace_bytes,
                              const void* const* biases, void* const* outs, void* stream);
 
-/* Backward of the forward (fp32 plans with out_ch <= 256; DCN_E_UNSUPPORTED
- * otherwise): given grad_out = dL/dout in the plan's output layout (fp32),
- * writes
+/* Backward of the forward (plans with out_ch <= 256; DCN_E_UNSUPPORTED
+ * otherwise): given grad_out = dL/dout in the plan's output layout (fp32,
+ * like out), writes fp32
  *   grad_x      [B, H, W, C]       dL/dx (NHWC, like x)
  *   grad_offset [B, 2K, Ho, Wo]    dL/doffset (channel 2k: dy, 2k+1: dx)
  *   grad_mask   [B, K, Ho, Wo]     dL/dmask (with a NULL mask: at mask = 1)
@@ -202,9 +202,14 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
  * gradients are sums over many output pixels and taps accumulated with fp32
  * atomic adds (page 5 names atomic adds into fp32 accumulators as the way
  * these gradients are gathered), so they are not bitwise repeatable.
+ * Operands x, offset, mask and weight have the plan's in_dtype.  For bf16
+ * plans they are first widened exactly into fp32 copies in the workspace, and
+ * the backward then accumulates and writes fp32 (page 5, "Backend
+ * selection": half-precision training with a float32 accumulator).
  * workspace: >= dcn_backward_workspace_bytes (the weight re-packed for the
- * input-gradient contraction), device, 16-byte aligned.  x, grad_x: 16-byte
- * aligned; the rest 4-byte aligned.  Asynchronous on `stream`. */
+ * input-gradient contraction, plus the fp32 copies for bf16 plans), device,
+ * 16-byte aligned.  x, grad_x: 16-byte aligned; offset, mask, weight
+ * element-aligned; the rest 4-byte aligned.  Asynchronous on `stream`. */
 dcn_status dcn_backward_workspace_bytes(dcn_plan plan, size_t* bytes);
 dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const void* mask,
                         const void* weight, const void* grad_out, void* grad_x,

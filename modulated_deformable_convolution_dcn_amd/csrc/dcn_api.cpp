@@ -480,10 +480,37 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
   }
 }
 
+namespace {
+// Backward workspace: the re-packed weight, then for bf16 plans fp32 copies
+// of x, offset, mask and weight (each region 256-byte aligned).
+struct BwdLayout {
+  size_t wt, x, off, mask, w, total;
+};
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+BwdLayout bwd_layout(dcn_plan plan) {
+  const dcn_desc& d = plan->d;
+  BwdLayout L{};
+  L.wt = 0;
+  size_t at = round256((size_t)dcn::bwd_workspace_floats(d.out_ch, d.in_ch, plan->K) * 4);
+  if (d.in_dtype == DCN_BF16) {
+    const size_t HoWo = (size_t)plan->Ho * plan->Wo;
+    L.x = at;
+    at += round256((size_t)d.batch * d.height * d.width * d.in_ch * 4);
+    L.off = at;
+    at += round256((size_t)d.batch * 2 * plan->K * HoWo * 4);
+    L.mask = at;
+    at += round256((size_t)d.batch * plan->K * HoWo * 4);
+    L.w = at;
+    at += round256((size_t)d.out_ch * d.in_ch * plan->K * 4);
+  }
+  L.total = at;
+  return L;
+}
+}  // namespace
+
 dcn_status dcn_backward_workspace_bytes(dcn_plan plan, size_t* bytes) {
   if (!plan || !bytes) return fail(DCN_E_NULL, "dcn_backward_workspace_bytes: NULL argument");
-  const dcn_desc& d = plan->d;
-  *bytes = (size_t)dcn::bwd_workspace_floats(d.out_ch, d.in_ch, plan->K) * 4;
+  *bytes = bwd_layout(plan).total;
   return ok();
 }
 
@@ -494,8 +521,10 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
   try {
     if (!plan) return fail(DCN_E_NULL, "dcn_backward: plan is NULL");
     const dcn_desc& d = plan->d;
-    if (d.in_dtype != DCN_F32)
-      return fail(DCN_E_UNSUPPORTED, "dcn_backward: fp32 operands only in this build");
+    const bool bf16 = d.in_dtype == DCN_BF16;
+    if (bf16 && 2 * (int64_t)plan->x_bytes >= kLimit31)
+      return fail(DCN_E_UNSUPPORTED, "dcn_backward: the fp32 copy of a bf16 x must stay below "
+                                     "2^31 bytes");
     if (d.out_ch > 256)
       return fail(DCN_E_UNSUPPORTED, "dcn_backward: out_ch %d > 256", d.out_ch);
     size_t need = 0;
@@ -509,10 +538,38 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
     if (!aligned(x, 16) || !aligned(workspace, 16) || (grad_x && !aligned(grad_x, 16)))
       return fail(DCN_E_ALIGN, "dcn_backward: x, grad_x and the workspace must be 16-byte "
                                "aligned");
-    const void* rest[] = {offset, mask, weight, grad_out, grad_offset, grad_mask, grad_weight,
-                          grad_bias};
+    const size_t E = bf16 ? 2 : 4;
+    const void* ops[] = {offset, mask, weight};
+    for (const void* q : ops)
+      if (q && !aligned(q, E)) return fail(DCN_E_ALIGN, "dcn_backward: misaligned operand");
+    const void* rest[] = {grad_out, grad_offset, grad_mask, grad_weight, grad_bias};
     for (const void* q : rest)
       if (q && !aligned(q, 4)) return fail(DCN_E_ALIGN, "dcn_backward: misaligned pointer");
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (bf16) {
+      // bf16 operands: widen x, offset, mask and weight exactly into fp32
+      // copies in the workspace; the backward then runs in fp32 throughout
+      // (fp32 accumulators, fp32 gradients)
+      const BwdLayout L = bwd_layout(plan);
+      char* ws = static_cast<char*>(workspace);
+      const int64_t HoWo = (int64_t)plan->Ho * plan->Wo;
+      struct {
+        const void* src;
+        size_t at;
+        int64_t n;
+      } cv[] = {{x, L.x, (int64_t)d.batch * d.height * d.width * d.in_ch},
+                {offset, L.off, (int64_t)d.batch * 2 * plan->K * HoWo},
+                {mask, L.mask, mask ? (int64_t)d.batch * plan->K * HoWo : 0},
+                {weight, L.w, (int64_t)d.out_ch * d.in_ch * plan->K}};
+      for (auto& c : cv) {
+        hipError_t e = dcn::launch_widen_bf16(c.src, reinterpret_cast<float*>(ws + c.at), c.n, hs);
+        if (e != hipSuccess) return hip_fail(e, "bf16 widen launch");
+      }
+      x = ws + L.x;
+      offset = ws + L.off;
+      mask = mask ? ws + L.mask : nullptr;
+      weight = ws + L.w;
+    }
     dcn::BwdArgs a{};
     a.x = static_cast<const float*>(x);
     a.offset = static_cast<const float*>(offset);
@@ -539,10 +596,9 @@ dcn_status dcn_backward(dcn_plan plan, const void* x, const void* offset, const 
     a.nchunk = (int)ceil_div(d.in_ch, 64);
     a.tiles_per_img = (int)ceil_div(a.HoWo, 64);
     a.nhwc_g = d.out_layout == DCN_OUT_NHWC;
-    a.x_bytes = plan->x_bytes;
+    a.x_bytes = bf16 ? 2 * plan->x_bytes : plan->x_bytes;
     hipError_t e = dcn::launch_backward(a, static_cast<const float*>(weight),
-                                        static_cast<float*>(workspace),
-                                        static_cast<hipStream_t>(stream));
+                                        static_cast<float*>(workspace), hs);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return ok();
   } catch (...) {

@@ -806,6 +806,30 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const float* __restrict__
   }
 }
 
+// bf16 -> fp32, exact: dst[i] = src[i] for i < n (8 elements per thread and
+// step; src and dst 16-byte aligned, a tail of n % 8 element-wise).
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src,
+                                                         float* __restrict__ dst, int64_t n) {
+  const int64_t n8 = n / 8;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n8;
+       v += (int64_t)gridDim.x * 256) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(src + 8 * v);
+    f32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      lo[2 * e] = __uint_as_float(q[e] << 16);
+      lo[2 * e + 1] = __uint_as_float(q[e] & 0xffff0000u);
+      hi[2 * e] = __uint_as_float(q[2 + e] << 16);
+      hi[2 * e + 1] = __uint_as_float(q[2 + e] & 0xffff0000u);
+    }
+    *reinterpret_cast<f32x4*>(dst + 8 * v) = lo;
+    *reinterpret_cast<f32x4*>(dst + 8 * v + 4) = hi;
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += 256)
+      dst[i] = __uint_as_float((uint32_t)src[i] << 16);
+}
+
 namespace {
 unsigned grid_of(int64_t n) {
   int64_t g = (n + 255) / 256;
@@ -818,6 +842,13 @@ hipError_t zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3(grid_of((n + 7) / 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), dst, n);
+  return hipGetLastError();
+}
 
 int bwd_out_pad(int O) { return O <= 16 ? 16 : O <= 64 ? 64 : O <= 128 ? 128 : 256; }
 

@@ -72,6 +72,8 @@ struct BwdArgs {
 // Floats of workspace the backward needs; the launch zero-fills the
 // gradients it writes, re-packs the weight and runs the three kernels.
 int64_t bwd_workspace_floats(int O, int C, int K);
+// bf16 -> fp32 copy of n elements (exact), one kernel on `stream`.
+hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, const float* weight, float* workspace,
                            hipStream_t stream);
 

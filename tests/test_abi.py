@@ -257,7 +257,14 @@ def test_backward_checks_fire_before_any_launch():
     assert call(x=V(0x10004)) == 5
     assert call(gw=V(0x10002)) == 5
     bf = Plan(Desc(1, 64, 16, 16, 64, 3, 3, 1, 1, "bf16"))
-    assert call(plan=bf) == 4
+    nb = ctypes.c_size_t()
+    assert lib.dcn_backward_workspace_bytes(bf._h, ctypes.byref(nb)) == 0
+    # the re-packed weight, then fp32 copies of x, offset, mask and weight
+    r = lambda v: -(-v // 256) * 256  # noqa: E731
+    assert nb.value == ws + r(16 * 16 * 64 * 4) + r(18 * 256 * 4) + r(9 * 256 * 4) + r(
+        64 * 64 * 9 * 4)
+    assert call(plan=bf) == 8                        # the fp32 plan's workspace is too small
+    assert call(plan=bf, off=V(0x10001), wsn=nb.value) == 5
     wide = Plan(Desc(1, 64, 16, 16, 300, 3, 3, 1, 1))
     assert call(plan=wide) == 4
     assert "256" in lib.dcn_last_error().decode()

@@ -61,7 +61,7 @@ def _run(spec, d, gout, layout, use_mask=True, want=("x", "offset", "mask", "wei
     from modulated_deformable_convolution_dcn_amd import Desc, Plan
     dev = device_inputs(spec, d)
     plan = Plan(Desc(spec.B, spec.C, spec.H, spec.W, spec.O, spec.kh, spec.kw, spec.ph, spec.pw,
-                     "f32", layout))
+                     spec.dtype, layout))
     g = torch.from_numpy(gout).cuda()
     if layout == "nhwc":
         g = g.permute(0, 2, 3, 1).contiguous()
@@ -144,3 +144,45 @@ def test_backward_partial_outputs_without_grad_x(want):
     assert set(got) == set(want)
     for k in want:
         _check("partial %s grad_%s" % ("+".join(want), k), got[k], ref[k], norm[k])
+
+
+# bf16 operands: widened exactly to fp32 before the fp32 backward, so the
+# oracle (which reads the same bf16-rounded values) bounds them with the fp32
+# tolerance
+D = W["detection_bf16"]
+BF16_CASES = {
+    "bf16_c64_o64_k3": D.scaled(B=1, C=64, O=64, H=14, W=13),
+    "bf16_c32_o200_k2x3": D.scaled(B=2, C=32, O=200, H=9, W=11, kh=2, kw=3, ph=0, pw=1),
+    "bf16_c256_o256_k3": D.scaled(B=1, H=12, W=10),
+}
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+@pytest.mark.parametrize("name", sorted(BF16_CASES))
+def test_backward_bf16_parity(name, layout):
+    spec = BF16_CASES[name]
+    d = synth.make_inputs(spec)
+    gout = _grad_out(spec, 61)
+    ref, norm = oracle.backward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                                gout)
+    print("case", name, layout, spec, flush=True)
+    got = _run(spec, d, gout, layout)
+    for k in ("x", "offset", "mask", "weight", "bias"):
+        worst = _check("%s/%s grad_%s" % (name, layout, k), got[k], ref[k], norm[k])
+        print("  grad_%s worst err/N %.3g" % (k, worst))
+
+
+def test_backward_bf16_detection_full_size():
+    """The detection workload (B=8, 256 -> 256 channels, 64 x 64, 3x3, bf16) at
+    full size, NCHW, all five gradients."""
+    spec = W["detection_bf16"]
+    d = synth.make_inputs(spec)
+    gout = _grad_out(spec, 63)
+    print("case detection_bf16 backward full: oracle", flush=True)
+    ref, norm = oracle.backward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                                gout)
+    print("case detection_bf16 backward full: gpu", flush=True)
+    got = _run(spec, d, gout, "nchw")
+    for k in ("x", "offset", "mask", "weight", "bias"):
+        worst = _check("detection_bf16 full grad_%s" % k, got[k], ref[k], norm[k])
+        print("  grad_%s worst err/N %.3g" % (k, worst))
