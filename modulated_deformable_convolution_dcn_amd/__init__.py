@@ -14,6 +14,7 @@ memory and the current stream) into those calls.
 from __future__ import annotations
 
 import ctypes
+import os
 from dataclasses import dataclass
 
 from . import _lib
@@ -39,6 +40,24 @@ def _stream_handle(stream=None) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def validation_enabled() -> bool:
+    """DCN_VALIDATE=1 turns on the opt-in input check (page 5's
+    DEFORMOPS_VALIDATE works the same way): before each call, offsets,
+    masks, sampling locations and aggregation weights must be finite.  The
+    check synchronises with the device, so it is off by default and never on
+    a timed path; non-finite offsets are otherwise outside the contract."""
+    return os.environ.get("DCN_VALIDATE", "") not in ("", "0")
+
+
+def _validate(**tensors):
+    if not validation_enabled():
+        return
+    torch = _torch()
+    for name, t in tensors.items():
+        if t is not None and not bool(torch.isfinite(t).all()):
+            raise ValueError("DCN_VALIDATE: %s holds non-finite values" % name)
 
 
 @dataclass(frozen=True)
@@ -126,6 +145,7 @@ class Plan:
         self._check("offset", offset, (d.batch, 2 * self.K, self.Ho, self.Wo))
         self._check("mask", mask, (d.batch, self.K, self.Ho, self.Wo), optional=True)
         self._check("bias", bias, (d.out_ch,), optional=True)
+        _validate(offset=offset, mask=mask)
 
     # -- calls --------------------------------------------------------------
     def new_workspace(self, split=True):
@@ -184,6 +204,7 @@ class Plan:
         self._check("offset", offset, (d.batch, 2 * self.K, rows, self.Wo))
         self._check("mask", mask, (d.batch, self.K, rows, self.Wo), optional=True)
         self._check("bias", bias, (d.out_ch,), optional=True)
+        _validate(offset=offset, mask=mask)
         shape = ((d.batch, d.out_ch, rows, self.Wo) if d.out_layout == "nchw"
                  else (d.batch, rows, self.Wo, d.out_ch))
         if out is None:
@@ -396,6 +417,7 @@ class MsdaPlan:
             if tuple(t.shape) != shapes[name]:
                 raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
                                                                     shapes[name]))
+        _validate(locations=locations, weights=weights)
         if out is None:
             out = torch.empty((self.B, self.Q, self.G * self.D), dtype=torch.float32,
                               device="cuda")
@@ -483,6 +505,7 @@ class DsamplePlan:
             if tuple(t.shape) != shapes[name]:
                 raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
                                                                     shapes[name]))
+        _validate(offset=offset, weights=weights)
         if out is None:
             out = torch.empty(self.out_shape(), dtype=torch.float32, device="cuda")
         if (tuple(out.shape) != self.out_shape() or out.dtype != torch.float32 or
