@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcn_mi355x.so")
 
-SOURCES = ["dcn_kernels.hip", "dcn_wsk.hip", "dcn_quad.hip", "dcn_bf16.hip", "dcn_backward.hip",
+SOURCES = ["dcn_kernels.hip", "dcn_wsk.hip", "dcn_quad.hip", "dcn_bf16.hip", "dcn_bf16win.hip",
+           "dcn_backward.hip",
            "dcn_msda.hip", "dcn_dsample.hip", "dcn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -68,7 +68,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile configuration for a validated descriptor.
-dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
+dcn::KernelConfig choose_config(const dcn_desc& d, int Ho, int Wo) {
   dcn::KernelConfig kc{};
   kc.bf16 = d.in_dtype == DCN_BF16;
   const int O = d.out_ch, C = d.in_ch;
@@ -79,6 +79,13 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
     kc.CB = 64;
     kc.NO = 64;
     kc.M = 64;
+  } else if (kc.bf16 && O > 128 && dcn::bf16win_fits(d.kernel_h, d.kernel_w, C)) {
+    // bf16, wide outputs, small kernels: 8 x 16 pixels x 256 output channels
+    // per workgroup, corners blended from an LDS input window (dcn_bf16win.hip)
+    kc.kind = 4;
+    kc.CB = 64;
+    kc.NO = 256;
+    kc.M = 128;
   } else if (kc.bf16 && O > 128 && C >= 32) {
     // bf16, wide outputs: 128 pixels x 256 output channels per workgroup,
     // one workgroup per CU (dcn_bf16.hip)
@@ -106,7 +113,9 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int HoWo) {
   kc.nhwc = d.out_layout == DCN_OUT_NHWC;
   kc.nchunk = (int)ceil_div(C, kc.CB);
   kc.n_otiles = (int)ceil_div(O, kc.NO);
-  kc.tiles_per_img = (int)ceil_div(HoWo, kc.M);
+  int tiles_x = 0;
+  kc.tiles_per_img = kc.kind == 4 ? dcn::bf16win_tiles(Ho, Wo, tiles_x)
+                                  : (int)ceil_div((int64_t)Ho * Wo, kc.M);
   return kc;
 }
 
@@ -204,7 +213,7 @@ dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan) {
         (int64_t)d.batch * d.out_ch * HoWo >= kLimit31)
       return fail(DCN_E_UNSUPPORTED, "offset/output element counts must stay below 2^31");
 
-    dcn::KernelConfig kc = choose_config(d, (int)HoWo);
+    dcn::KernelConfig kc = choose_config(d, (int)Ho, (int)Wo);
     if (!dcn::config_supported(kc))
       return fail(DCN_E_INTERNAL, "no kernel variant for CB=%d NO=%d", kc.CB, kc.NO);
     const int64_t wp = dcn::packed_weight_elems(kc, (int)K);
@@ -332,14 +341,19 @@ dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
   a.Wo = plan->Wo;
   a.HoWo = rows * plan->Wo;
   kc = plan->kc;
-  kc.tiles_per_img = (int)ceil_div(a.HoWo, kc.M);
+  int tiles_x = 0;
+  kc.tiles_per_img = kc.kind == 4 ? dcn::bf16win_tiles(rows, plan->Wo, tiles_x)
+                                  : (int)ceil_div(a.HoWo, kc.M);
+  a.tiles_x = tiles_x;
   a.nchunk = kc.nchunk;
   a.n_otiles = kc.n_otiles;
   a.tiles_per_img = kc.tiles_per_img;
   a.x_bytes = plan->x_bytes;
   a.offset_bytes = (uint32_t)((size_t)d.batch * 2 * plan->K * a.HoWo * E);
   a.mask_bytes = mask ? (uint32_t)((size_t)d.batch * plan->K * a.HoWo * E) : 0u;
-  a.vec_store = (a.HoWo % 4) == 0;
+  // NCHW: 4 consecutive pixels store as one 16-byte write when they start
+  // 16-byte aligned (kind 4's 2-D tiles start rows at multiples of Wo)
+  a.vec_store = kc.kind == 4 ? (plan->Wo % 4) == 0 : (a.HoWo % 4) == 0;
   a.nsplit = 1;
   a.kper = plan->K;
   a.split_stride = 0;

@@ -570,6 +570,7 @@ bool config_supported(const KernelConfig& kc) {
   if (kc.kind == 1) return wsk_supported(kc);
   if (kc.kind == 2) return quad_supported(kc);
   if (kc.kind == 3) return bf16w_supported(kc);
+  if (kc.kind == 4) return bf16win_supported(kc);
   if (kc.M != 64) return false;
   if (kc.NO != 16 && kc.NO != 64 && kc.NO != 128 && kc.NO != 256) return false;
   if (kc.bf16) return kc.CB == 32 || kc.CB == 64;
@@ -586,7 +587,7 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
   const int64_t total = packed_weight_elems(kc, kh * kw);
   const int K = kh * kw;
   const bool padded = C % kc.CB != 0 || O % kc.NO != 0;
-  const int layout = kc.bf16 ? (kc.kind == 3 ? 3 : 0) : kc.kind;
+  const int layout = kc.bf16 ? (kc.kind >= 3 ? 3 : 0) : kc.kind;
   const unsigned g_src = grid_for((int64_t)O * C * K);
   if (kc.bf16) {
     __bf16* wp = static_cast<__bf16*>(wpack);
@@ -613,6 +614,7 @@ hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t 
   if (kc.kind == 1) return launch_fused_wsk(kc, a, s);
   if (kc.kind == 2) return launch_fused_quad(kc, a, s);
   if (kc.kind == 3) return launch_fused_bf16w(kc, a, s);
+  if (kc.kind == 4) return launch_fused_bf16win(kc, a, s);
   if (kc.bf16) {
     return kc.nhwc ? launch_cb<__bf16, true>(kc, a, s) : launch_cb<__bf16, false>(kc, a, s);
   }
@@ -626,6 +628,7 @@ hipError_t launch_fused_multi(const KernelConfig& kc, const MultiArgs& m, hipStr
   if (kc.kind == 1) return launch_fused_wsk_multi(kc, m, s);
   if (kc.kind == 2) return launch_fused_quad_multi(kc, m, s);
   if (kc.kind == 3) return launch_fused_bf16w_multi(kc, m, s);
+  if (kc.kind == 4) return launch_fused_bf16win_multi(kc, m, s);
   return hipErrorInvalidConfiguration;
 }
 

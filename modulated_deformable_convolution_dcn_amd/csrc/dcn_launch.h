@@ -11,7 +11,9 @@ namespace dcn {
 struct KernelConfig {
   int kind;       // 0: shared column tile (dcn_kernels.hip), 1: k split over waves
                   // (dcn_wsk.hip), 2: 32 pixels x 32 channels per wave (dcn_quad.hip),
-                  // 3: bf16, 128 pixels x 256 outputs per workgroup (dcn_bf16.hip)
+                  // 3: bf16, 128 pixels x 256 outputs per workgroup (dcn_bf16.hip),
+                  // 4: bf16, 8 x 16 pixels x 256 outputs, corners from an LDS
+                  //    window (dcn_bf16win.hip)
   int bf16;       // 0: fp32 operands, 1: bf16 operands
   int M;          // output pixels per workgroup
   int CB;         // channels per k-block (one tap, one channel chunk)
@@ -19,7 +21,7 @@ struct KernelConfig {
   int nhwc;       // output layout: 0 NCHW, 1 NHWC
   int nchunk;     // ceil(C / CB)
   int n_otiles;   // ceil(O / NO)
-  int tiles_per_img;  // ceil(Ho*Wo / M)
+  int tiles_per_img;  // ceil(Ho*Wo / M); kind 4: 2-D tiles, ceil(Ho / 8) * ceil(Wo / 16)
 };
 
 // Arguments of the fused forward kernel (passed by value).
@@ -32,6 +34,7 @@ struct FusedArgs {
   float* out;          // [B,O,Ho,Wo] or [B,Ho,Wo,O] fp32
   int B, C, H, W, O, kh, kw, K, ph, pw, Ho, Wo, HoWo;
   int nchunk, n_otiles, tiles_per_img;
+  int tiles_x;         // kind 4: 16-column tiles per tile row
   uint32_t x_bytes;    // bytes of x (< 2^31)
   uint32_t offset_bytes;  // bytes of offset (< 2^31)
   uint32_t mask_bytes;    // bytes of mask (< 2^31; 0 when mask is NULL)
@@ -154,6 +157,15 @@ hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, h
 bool bf16w_supported(const KernelConfig& kc);
 hipError_t launch_fused_bf16w(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
 hipError_t launch_fused_bf16w_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t stream);
+
+// The wide bf16 kernel with an LDS input window (kh, kw <= 3, C % 64 == 0).
+bool bf16win_supported(const KernelConfig& kc);
+bool bf16win_fits(int kh, int kw, int C);
+// 2-D tiles of the window kernel for `rows` x Wo output pixels; sets tiles_x.
+int bf16win_tiles(int rows, int Wo, int& tiles_x);
+hipError_t launch_fused_bf16win(const KernelConfig& kc, const FusedArgs& a, hipStream_t stream);
+hipError_t launch_fused_bf16win_multi(const KernelConfig& kc, const MultiArgs& m,
+                                      hipStream_t stream);
 
 // dst[b, p, c] = src[b, c, p] for p over height*width pixels.
 hipError_t launch_nchw_to_nhwc(int bf16, const void* src, void* dst, int B, int C, int HW,

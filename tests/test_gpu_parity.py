@@ -50,6 +50,15 @@ FULL_CASES = {
     "b_c128_o300": D.scaled(B=1, C=128, O=300, H=11, W=12, kh=3, kw=2, ph=1, pw=0),
     "b_c256_o256_k1": D.scaled(B=2, C=256, O=256, H=7, W=9, kh=1, kw=1, ph=0, pw=0),
     "b_c32_o129": D.scaled(B=1, C=32, O=129, H=17, W=16, kh=5, kw=5, ph=2, pw=2),
+    # bf16, more than 128 outputs, 3 x 3 kernels, C % 64 == 0: corners from
+    # the LDS input window; ragged 8 x 16 tiles, wide offsets that send many
+    # tiles to the memory path, no padding with three 64-channel chunks, two
+    # output tiles; a 1 x 3 kernel takes the kernel without a window
+    "bw_c128_o256_ragged": D.scaled(B=2, C=128, O=256, H=20, W=37, seed=71),
+    "bw_c64_o300_far": D.scaled(B=1, C=64, O=300, H=19, W=23, offset_dist="normal8", seed=72),
+    "bw_c192_o160_p0": D.scaled(B=1, C=192, O=160, H=13, W=40, ph=0, pw=0, seed=74),
+    "bw_c192_o160_k1x3": D.scaled(B=1, C=192, O=160, H=9, W=40, kh=1, kw=3, ph=0, pw=1,
+                                  seed=73),
     # fp32 tiles of 65..128 output channels (k split over waves)
     "w_c32_o100": E.scaled(B=2, C=32, O=100, H=10, W=11, kh=3, kw=3, ph=1, pw=1),
     "w_c96_o128": E.scaled(B=1, C=96, O=128, H=9, W=15, kh=3, kw=5, ph=1, pw=2),
