@@ -12,7 +12,7 @@ torch.floor, and the per-corner `valid` comparison):
   integers, half-integers, -1, H-1, H and +-1e30 on each kernel variant.
   The corner weights (bilinear weight x mask) are compared against an
   independent float32 numpy derivation within the rounding of their few fp32
-  products (bf16 rounding for the wide bf16 kernel).
+  products (bf16 rounding for the two wide bf16 kernels).
 * test_coords_*: dcn_debug_coords, the stage alone from the same device
   functions, for the floor of every point (also those with no corner inside).
 """
@@ -103,14 +103,16 @@ def test_corner_table_bit_exact(name):
     _check_table(oracle_shape(spec), d["offset"], d["mask"], idx, wgt, spec.dtype, name)
 
 
-# one plan shape per kernel variant: (dtype, C, O) -> general, k split,
-# 32 x 32 per wave, wide bf16
+# one plan shape per kernel variant: (dtype, C, O, kernel size) -> general,
+# k split, 32 x 32 per wave, wide bf16 (5 x 5: no window), wide bf16 with the
+# LDS input window (3 x 3)
 VARIANTS = {
-    "general_f32": ("f32", 4, 4),
-    "general_bf16": ("bf16", 32, 64),
-    "ksplit_f32": ("f32", 64, 128),
-    "quad_f32": ("f32", 64, 64),
-    "wide_bf16": ("bf16", 64, 256),
+    "general_f32": ("f32", 4, 4, 3),
+    "general_bf16": ("bf16", 32, 64, 3),
+    "ksplit_f32": ("f32", 64, 128, 3),
+    "quad_f32": ("f32", 64, 64, 3),
+    "wide_bf16": ("bf16", 64, 256, 5),
+    "window_bf16": ("bf16", 64, 256, 3),
 }
 SPECIAL = np.array([-2.0, -1.5, -1.0, -0.5, -1e-7, 0.0, 0.5, 1.0, 2.5, 5.0, 5.5, 6.0, 1e30, -1e30],
                    np.float32)  # H = 6: -1, H - 1 = 5, H = 6 and half-integers around them
@@ -118,8 +120,8 @@ SPECIAL = np.array([-2.0, -1.5, -1.0, -0.5, -1e-7, 0.0, 0.5, 1.0, 2.5, 5.0, 5.5,
 
 @pytest.mark.parametrize("variant", sorted(VARIANTS))
 def test_corner_table_at_exact_integers_and_halves(variant):
-    dtype, C, O = VARIANTS[variant]
-    spec = synth.Spec(name="special", B=2, C=C, O=O, H=6, W=5, kh=3, kw=3, ph=1, pw=1,
+    dtype, C, O, k = VARIANTS[variant]
+    spec = synth.Spec(name="special", B=2, C=C, O=O, H=6, W=5, kh=k, kw=k, ph=k // 2, pw=k // 2,
                       dtype=dtype, seed=5, offset_dist="normal1.5", mask_dist="uniform",
                       weight_std=0.3, bias_dist="normal1")
     d = synth.make_inputs(spec)
