@@ -35,6 +35,11 @@ CASES = {
                                  seed=46),
     "g4_d32_bf16": P5.scaled(G=4, D=32, H=12, W=12, dtype="bf16", softmax=False, seed=47),
     "far_outside": P5.scaled(H=8, W=8, offset_std=40.0, seed=48),
+    # 8 groups of 4 fp32 channels with a 2 x 2 kernel; two bf16 groups of 64
+    # channels; wider offsets (std 4)
+    "win_g8_d4_k2": P5.scaled(G=8, D=4, H=13, W=11, kh=2, kw=2, ph=0, pw=1, seed=50),
+    "win_g2_d64_bf16": P5.scaled(G=2, D=64, H=19, W=21, dtype="bf16", seed=51),
+    "win_reach": P5.scaled(H=24, W=20, offset_std=4.0, seed=52),
 }
 
 
