@@ -51,14 +51,18 @@ __device__ __forceinline__ void blend_acc<__bf16>(float* acc, float w, u32x4 v) 
 
 }  // namespace
 
-template <class T, int NV, bool NHWC>
+// GT: the most groups one channel tile can touch -- NV + 1 in general (groups
+// of one 16-byte vector, misaligned), 8 for a launch whose groups are wide
+// enough (fewer table entries per thread, fewer registers, more workgroups
+// per CU).
+template <class T, int NV, bool NHWC, int GT>
 __global__ __launch_bounds__(256) void dsample_kernel(DsArgs a) {
   constexpr int E = sizeof(T);
   constexpr int VEC = 16 / E;           // channels per 16-byte vector
   constexpr int CT = NV * VEC;          // channels per workgroup
   constexpr int M = 64;                 // pixels per workgroup
   constexpr int U = M * NV / 256;       // (pixel, vector) units per thread
-  constexpr int GTM = NV + 1;           // most groups one channel tile touches
+  constexpr int GTM = GT;               // most groups one channel tile touches
   constexpr int EPT = (GTM * M + 255) / 256;  // table entries per thread
   constexpr int TAB_BYTES = GTM * M * 32;
   constexpr int TR_BYTES = NHWC ? 0 : CT * (M + 1) * 4;
@@ -118,13 +122,27 @@ __global__ __launch_bounds__(256) void dsample_kernel(DsArgs a) {
     s_inv[r] = 1.0f;
   }
   if (a.softmax) {
+    // the logits of up to KB taps are loaded at once (one memory latency per
+    // KB taps instead of one per tap), then reduced from registers
+    constexpr int KB = 9;
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
       if (!e_in[r]) continue;
-      float mx = -INFINITY;
-      for (int k = 0; k < a.K; ++k) mx = fmaxf(mx, load_scalar<T>(wr, w_at(r, k)));
-      float sum = 0.0f;
-      for (int k = 0; k < a.K; ++k) sum += expf(load_scalar<T>(wr, w_at(r, k)) - mx);
+      float mx = -INFINITY, sum = 0.0f;
+      for (int k0 = 0; k0 < a.K; k0 += KB) {
+        float lg[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
+          lg[q] = k0 + q < a.K ? load_scalar<T>(wr, w_at(r, k0 + q)) : -INFINITY;
+        float cm = mx;
+#pragma unroll
+        for (int q = 0; q < KB; ++q) cm = fmaxf(cm, lg[q]);
+        sum *= expf(mx - cm);  // rescale the running sum to the new maximum
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
+          if (k0 + q < a.K) sum += expf(lg[q] - cm);
+        mx = cm;
+      }
       s_max[r] = mx;
       s_inv[r] = 1.0f / sum;
     }
@@ -245,8 +263,13 @@ namespace {
 template <class T, int NV>
 hipError_t launch_ds_nv(const DsArgs& a, bool nhwc, int64_t nblk, hipStream_t s) {
   const dim3 grid((unsigned)nblk), block(256);
-  if (nhwc) hipLaunchKernelGGL((dsample_kernel<T, NV, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((dsample_kernel<T, NV, false>), grid, block, 0, s, a);
+  constexpr int VEC = 16 / (int)sizeof(T);
+  // groups a tile of NV * VEC channels can touch: one more than it holds
+  const bool wide = (NV * VEC + a.D - 1) / a.D + 1 <= 8 && NV + 1 > 8;
+  if (wide && nhwc) hipLaunchKernelGGL((dsample_kernel<T, NV, true, 8>), grid, block, 0, s, a);
+  else if (wide) hipLaunchKernelGGL((dsample_kernel<T, NV, false, 8>), grid, block, 0, s, a);
+  else if (nhwc) hipLaunchKernelGGL((dsample_kernel<T, NV, true, NV + 1>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((dsample_kernel<T, NV, false, NV + 1>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 template <class T>
