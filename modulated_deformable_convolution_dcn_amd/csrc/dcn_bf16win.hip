@@ -18,16 +18,16 @@
 // The window of the next 32 channels is loaded while the current ones are
 // consumed (two window buffers), so the copy costs no time of its own after
 // the first.  A tile with any inside-image corner beyond its window (an
-// offset larger than R near the tile's edge: 2 % of the detection workload's
-// tiles) runs the same pipeline with every corner fetched from memory
+// offset larger than R near the tile's edge: 1 of the detection workload's
+// 256 tiles) runs the same pipeline with
+// every corner fetched from memory
 // instead, so the result never depends on R.  The choice is made once per
 // tile: a load under a branch inside the pipelined slots would make the
 // compiler wait for every load in flight.
 //
 // Work layout: one workgroup of 8 waves (two per SIMD: while one waits on
-// LDS or memory the other issues, and the blend arithmetic of one overlaps
-// the matrix instructions of the other) owns an 8 x 16 pixel tile x 256
-// output channels, accumulators in AGPRs; wave w owns outputs [32w, 32w+32)
+// LDS or memory the other issues) owns an 8 x 16 pixel tile x 256 output
+// channels, accumulators in registers; wave w owns outputs [32w, 32w+32)
 // and loads exactly its own weight fragments from L2.  The k-axis runs
 // chunk-major: for each 32-channel chunk, the 9 taps.  The corner tables
 // (weights and window or memory offsets of the 4 corners) of all 9 taps are
@@ -36,8 +36,11 @@
 // corner fetches of block s+2 and a slice of the next window.  The blend
 // pairs the two corners of a corner row channel by channel (a byte permute)
 // and takes each pair's weighted sum with one bf16 dot product into an fp32
-// accumulator (the products of two bf16 values are exact in fp32), so a
-// multiply-add costs one instruction; the sum is rounded to bf16 once.
+// accumulator (the products of two bf16 values are exact in fp32): two
+// instructions per two multiply-adds, with no widening of the bf16 corner
+// values; the sum is rounded to bf16 once.  On this chip VALU work beside
+// the MFMAs is not hidden behind them, so the blend's instruction count is
+// part of every step's time.
 
 #include <type_traits>
 
