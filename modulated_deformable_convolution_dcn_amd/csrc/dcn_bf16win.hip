@@ -19,8 +19,7 @@
 // consumed (two window buffers), so the copy costs no time of its own after
 // the first.  A tile with any inside-image corner beyond its window (an
 // offset larger than R near the tile's edge: 1 of the detection workload's
-// 256 tiles) runs the same pipeline with
-// every corner fetched from memory
+// 256 tiles) runs the same pipeline with every corner fetched from memory
 // instead, so the result never depends on R.  The choice is made once per
 // tile: a load under a branch inside the pipelined slots would make the
 // compiler wait for every load in flight.
