@@ -332,57 +332,69 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 //   layout 3 (bf16 16x16x32 fragments, VEC = 8): [CB/32][NO/16][g][16][8]
 //            = channel 32q + 8g + e, output 16*nt + col -- fragment (q, nt)
 //            is one 1 KB run in lane order.
-// Index of (channel c_in, output o_in) inside one packed block.
-__device__ __forceinline__ int packed_index(int c_in, int o_in, int layout, int NO, int VEC) {
-  const int nt = o_in >> 4, col = o_in & 15;
+// The (channel c_in, output o_in) of element `in` of one packed block: the
+// layouts above read backwards.  In every layout the lowest 16 / sizeof(T)
+// packed elements of a 16-byte run are consecutive channels of one output.
+__device__ __forceinline__ void packed_source(int in, int layout, int NO, int VEC, int& c_in,
+                                              int& o_in) {
+  const int NT = NO >> 4;
   switch (layout) {
-    case 0: return ((c_in / VEC) * NO + o_in) * VEC + c_in % VEC;
+    case 0:
+      c_in = ((in / VEC) / NO) * VEC + in % VEC;
+      o_in = (in / VEC) % NO;
+      return;
     case 1: {
-      const int wv = c_in >> 4, g = (c_in >> 2) & 3, e = c_in & 3;
-      return (((wv * (NO / 16) + nt) * 4 + g) * 16 + col) * 4 + e;
+      const int t = in >> 8;
+      c_in = (t / NT) * 16 + ((in >> 6) & 3) * 4 + (in & 3);
+      o_in = (t % NT) * 16 + ((in >> 2) & 15);
+      return;
     }
     case 2: {
-      const int half = c_in >> 5, g = (c_in >> 3) & 3, q = (c_in >> 2) & 1, e = c_in & 3;
-      return ((((half * (NO / 16) + nt) * 2 + q) * 4 + g) * 16 + col) * 4 + e;
+      const int t = in >> 9;
+      c_in = (t / NT) * 32 + ((in >> 6) & 3) * 8 + ((in >> 8) & 1) * 4 + (in & 3);
+      o_in = (t % NT) * 16 + ((in >> 2) & 15);
+      return;
     }
     default: {
-      const int q = c_in >> 5, g = (c_in >> 3) & 3, e = c_in & 7;
-      return (((q * (NO / 16) + nt) * 4 + g) * 16 + col) * 8 + e;
+      const int t = in >> 9;
+      c_in = (t / NT) * 32 + ((in >> 7) & 3) * 8 + (in & 7);
+      o_in = (t % NT) * 16 + ((in >> 3) & 15);
+      return;
     }
   }
 }
 
-// Pass 1: every weight element, read in its own order [O][C][kh][kw]
-// (coalesced), written to its packed place.
+// One 16-byte run of the packed weight per thread: a whole 16-byte write,
+// its elements read from weight [O][C][kh][kw].  Consecutive threads take
+// the same run position in the blocks of consecutive taps, so their reads of
+// weight[o, c, tap] are consecutive words.  Padding channels and outputs are
+// written as zeros.
 template <class T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ w, T* __restrict__ wp,
                                                    int O, int C, int K, int CB, int NO, int VEC,
-                                                   int nchunk, int layout) {
-  const int64_t total = (int64_t)O * C * K;
-  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < total;
-       s += (int64_t)gridDim.x * 256) {
-    const int tap = (int)(s % K);
-    const int64_t oc = s / K;
-    const int c = (int)(oc % C), o = (int)(oc / C);
-    const int otile = o / NO, chunk = c / CB;
-    const int64_t block = ((int64_t)otile * K + tap) * nchunk + chunk;
-    wp[block * CB * NO + packed_index(c - chunk * CB, o - otile * NO, layout, NO, VEC)] = w[s];
-  }
-}
-
-// Before pass 1, only when C or O is not a multiple of the block: zero every
-// block that holds padding (pass 1 then overwrites its real entries).
-template <class T>
-__global__ __launch_bounds__(256) void pack_pad_kernel(T* __restrict__ wp, int O, int C, int K,
-                                                       int CB, int NO, int nchunk,
-                                                       int64_t total) {
-  const int blk = CB * NO;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int64_t block = idx / blk;  // [otile][tap][chunk]
-    const int chunk = (int)(block % nchunk);
-    const int otile = (int)(block / ((int64_t)nchunk * K));
-    if ((chunk + 1) * CB > C || (otile + 1) * NO > O) wp[idx] = static_cast<T>(0.0f);
+                                                   int nchunk, int layout, int64_t nruns) {
+  constexpr int G = 16 / (int)sizeof(T);
+  const int rpb = CB * NO / G;  // runs per block
+  for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < nruns;
+       r += (int64_t)gridDim.x * 256) {
+    // r = ((otile * nchunk + chunk) * rpb + run) * K + tap
+    const int tap = (int)(r % K);
+    const int64_t r2 = r / K;
+    const int run = (int)(r2 % rpb);
+    const int64_t oc = r2 / rpb;
+    const int chunk = (int)(oc % nchunk), otile = (int)(oc / nchunk);
+    const int64_t block = ((int64_t)otile * K + tap) * nchunk + chunk;  // [otile][tap][chunk]
+    const int64_t idx = block * CB * NO + (int64_t)run * G;
+    int c_in, o_in;
+    packed_source(run * G, layout, NO, VEC, c_in, o_in);
+    const int o = otile * NO + o_in, c0 = chunk * CB + c_in;
+    T v[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int c = c0 + e;
+      v[e] = o < O && c < C ? w[((int64_t)o * C + c) * K + tap] : static_cast<T>(0.0f);
+    }
+    *reinterpret_cast<u32x4*>(wp + idx) = *reinterpret_cast<const u32x4*>(v);
   }
 }
 
@@ -586,26 +598,19 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
                        int kh, int kw, hipStream_t s) {
   const int64_t total = packed_weight_elems(kc, kh * kw);
   const int K = kh * kw;
-  const bool padded = C % kc.CB != 0 || O % kc.NO != 0;
   const int layout = kc.bf16 ? (kc.kind >= 3 ? 3 : 0) : kc.kind;
-  const unsigned g_src = grid_for((int64_t)O * C * K);
-  if (kc.bf16) {
-    __bf16* wp = static_cast<__bf16*>(wpack);
-    if (padded)
-      hipLaunchKernelGGL(pack_pad_kernel<__bf16>, dim3(grid_for(total)), dim3(256), 0, s, wp, O, C,
-                         K, kc.CB, kc.NO, kc.nchunk, total);
-    hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(g_src), dim3(256), 0, s,
-                       static_cast<const __bf16*>(weight), wp, O, C, K, kc.CB, kc.NO, 8,
-                       kc.nchunk, layout);
-  } else {
-    float* wp = static_cast<float*>(wpack);
-    if (padded)
-      hipLaunchKernelGGL(pack_pad_kernel<float>, dim3(grid_for(total)), dim3(256), 0, s, wp, O, C,
-                         K, kc.CB, kc.NO, kc.nchunk, total);
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(g_src), dim3(256), 0, s,
-                       static_cast<const float*>(weight), wp, O, C, K, kc.CB, kc.NO, 4, kc.nchunk,
-                       layout);
-  }
+  const int G = kc.bf16 ? 8 : 4;  // elements per 16-byte run (CB is a multiple of it)
+  if (kc.CB % G != 0) return hipErrorInvalidValue;
+  const int64_t nruns = total / G;
+  const unsigned grid = grid_for(nruns);
+  if (kc.bf16)
+    hipLaunchKernelGGL(pack_kernel<__bf16>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const __bf16*>(weight), static_cast<__bf16*>(wpack), O, C, K,
+                       kc.CB, kc.NO, 8, kc.nchunk, layout, nruns);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float*>(weight), static_cast<float*>(wpack), O, C, K,
+                       kc.CB, kc.NO, 4, kc.nchunk, layout, nruns);
   return hipGetLastError();
 }
 
