@@ -470,10 +470,12 @@ __global__ __launch_bounds__(256) void bwd_weight_kernel(BwdArgs a, int tiles_pe
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int run = logical % runs_per_img;
-  const int t2 = logical / runs_per_img;
-  const int b = t2 % a.B;
-  const int kb = t2 / a.B;
+  // (tap, chunk) fastest: the workgroups of one XCD share pixel runs, so
+  // neighbouring taps' corner reads meet in that XCD's L2
+  const int kb = logical % (a.K * a.nchunk);
+  const int t2 = logical / (a.K * a.nchunk);
+  const int run = t2 % runs_per_img;
+  const int b = t2 / runs_per_img;
   const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
   const int rl = lane & 15, g = lane >> 4;
   const int sl = tid & 15;
@@ -575,10 +577,12 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
   float* const red = reinterpret_cast<float*>(smem);  // [wave][o][RST]
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int run = logical % runs_per_img;
-  const int t2 = logical / runs_per_img;
-  const int b = t2 % a.B;
-  const int kb = t2 / a.B;
+  // (tap, chunk) fastest: the workgroups of one XCD share pixel runs, so
+  // neighbouring taps' corner reads meet in that XCD's L2
+  const int kb = logical % (a.K * a.nchunk);
+  const int t2 = logical / (a.K * a.nchunk);
+  const int run = t2 % runs_per_img;
+  const int b = t2 / runs_per_img;
   const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
   const int ki = k / a.kw, kj = k - ki * a.kw;
   const int t_begin = run * tiles_per_run;
@@ -632,9 +636,12 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) cv[p][q] = load16(xr, chan_ok ? o4[q] + cbyte : kNoCorner);
   };
-  // s^T[c][px]: 16-byte chunk (px / 4) of row c stored at chunk (px / 4) ^ ((c / 4) & 3),
-  // so a pass's 64 single-float writes and the fragment reads both spread over the banks
-  auto st_at = [](int c, int px) { return c * SST + 4 * ((px >> 2) ^ ((c >> 2) & 3)) + (px & 3); };
+  // s^T[c][px]: 16-byte chunk (px / 4) of row c stored at chunk (px / 4) ^ ((c / 16) & 3).
+  // A pass writes channels 4 sl + e of pixels 4 p + pq: the 80-float step of sl
+  // spreads bits 0-1 of sl over the banks, the swizzle bits 2-3, pq the words,
+  // so the 64 single-float writes hit 64 distinct banks; a fragment read (16
+  // rows of one swizzle group) is spread by the row stride alone.
+  auto st_at = [](int c, int px) { return c * SST + 4 * ((px >> 2) ^ ((c >> 4) & 3)) + (px & 3); };
   auto blend = [&](int slot, int p) {
     const f32x4 w4 = Cw[slot * 16 + 4 * p + pq];
     f32x4 sv = __builtin_bit_cast(f32x4, cv[p][0]) * w4[0];
@@ -694,7 +701,7 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = 16 * u + rl;
-      bf[u] = *reinterpret_cast<const f32x4*>(&sT[c * SST + 4 * (g ^ ((c >> 2) & 3))]);
+      bf[u] = *reinterpret_cast<const f32x4*>(&sT[c * SST + 4 * (g ^ u)]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
