@@ -35,11 +35,15 @@
 
 namespace dcn {
 
-template <bool NHWC, bool FULLC, class Src>
+// NCH: the number of 64-channel chunks when it is known to be 1 (the
+// 64-channel workloads), else 0 (read from the arguments): a compile-time 1
+// removes the per-step divisions by it from the scalar instruction stream.
+template <bool NHWC, bool FULLC, int NCH, class Src>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fused_quad_kernel(Src src) {
   int logical;
   const FusedArgs& a = resolve_args(src, logical);
+  const int nchunk = NCH > 0 ? NCH : a.nchunk;
   constexpr int M = 64;           // output pixels per workgroup
   constexpr int NO = 64;          // output channels per workgroup
   constexpr int CB = 64;          // channels per k-block
@@ -84,7 +88,7 @@ fused_quad_kernel(Src src) {
   // taps [k0, k0 + kn) of this split; kt below counts from k0
   const int k0 = split * a.kper;
   const int kn = min(a.kper, a.K - k0);
-  const int NKB = kn * a.nchunk;
+  const int NKB = kn * nchunk;
   auto clampb = [&](int kb) { return kb < NKB ? kb : NKB - 1; };
   auto clampt = [&](int kt) { return kt < kn ? kt : kn - 1; };
 
@@ -94,7 +98,7 @@ fused_quad_kernel(Src src) {
   const __amdgpu_buffer_rsrc_t mskr =
       make_rsrc(has_mask ? a.mask : a.offset, has_mask ? a.mask_bytes : 0u);
   const float* wblocks = static_cast<const float*>(a.wpack) +
-                         ((size_t)otile * a.K + k0) * a.nchunk * (CB * NO);
+                         ((size_t)otile * a.K + k0) * nchunk * (CB * NO);
   const uint32_t row_bytes = (uint32_t)a.C * 4;
 
   // ---- (a) coefficients: lane l -> pixel l & 31, corners 2(l>>5), 2(l>>5)+1
@@ -171,12 +175,12 @@ fused_quad_kernel(Src src) {
   const int sl = lane & 7;
   u32x4 gv[4][4];
   auto chan = [&](int kb, uint32_t& cbyte) {
-    const int kt = kb / a.nchunk;
-    const int ch = (kb - kt * a.nchunk) * CB + wc * 32 + sl * 4;
+    const int kt = kb / nchunk;
+    const int ch = (kb - kt * nchunk) * CB + wc * 32 + sl * 4;
     cbyte = (uint32_t)ch * 4;
     return FULLC || ch < a.C;
   };
-  auto slot_of = [&](int kb) { return (kb / a.nchunk) % NSLOT; };
+  auto slot_of = [&](int kb) { return (kb / nchunk) % NSLOT; };
 
   // ---- (c) MFMA: k-slot g (lane / 16) owns the wave's channels 8g .. 8g+7;
   // fragment read q holds channels 8g + 4q + [0, 4), i.e. k-steps 4q .. 4q+3.
@@ -210,8 +214,8 @@ fused_quad_kernel(Src src) {
       coef_finish(clampt(t), dy, dx, mk);
     }
   }
-  coef_load(clampt(3 / a.nchunk), c_dy[0], c_dx[0], c_mk[0]);
-  coef_load(clampt(4 / a.nchunk), c_dy[1], c_dx[1], c_mk[1]);
+  coef_load(clampt(3 / nchunk), c_dy[0], c_dx[0], c_mk[0]);
+  coef_load(clampt(4 / nchunk), c_dy[1], c_dx[1], c_mk[1]);
   {
     const float* src = b_src(0);
 #pragma unroll
@@ -263,9 +267,9 @@ fused_quad_kernel(Src src) {
     const bool ok1 = chan(n1, cb1);
     const bool ok2 = chan(n2, cb2);
     const float* bsrc = b_src(n1);
-    const int tc = (s + 3) / a.nchunk;
-    const bool coef_due = tc * a.nchunk == s + 3 && tc < kn;
-    const int tl = clampt((s + 5) / a.nchunk);
+    const int tc = (s + 3) / nchunk;
+    const bool coef_due = tc * nchunk == s + 3 && tc < kn;
+    const int tl = clampt((s + 5) / nchunk);
     static_for<2>([&](auto MT) {
       constexpr int mt = decltype(MT)::value;
       constexpr int pa = mt == 0 ? 2 : 0;  // passes blended under this group
@@ -387,19 +391,26 @@ bool quad_supported(const KernelConfig& kc) {
 }
 
 namespace {
+template <bool NHWC, int NCH, class Src>
+void launch_quad_fc(bool fullc, dim3 grid, hipStream_t s, const Src& src) {
+  if (fullc) hipLaunchKernelGGL((fused_quad_kernel<NHWC, true, NCH, Src>), grid, dim3(256), 0, s, src);
+  else hipLaunchKernelGGL((fused_quad_kernel<NHWC, false, NCH, Src>), grid, dim3(256), 0, s, src);
+}
+
+// one_chunk: every problem of the launch has C <= 64
 template <class Src>
-hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, int64_t nblk,
-                           hipStream_t s) {
+hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, bool one_chunk,
+                           int64_t nblk, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
   const bool fullc = C % 64 == 0;
-  const dim3 grid((unsigned)nblk), block(256);
+  const dim3 grid((unsigned)nblk);
   if (kc.nhwc) {
-    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<true, true, Src>), grid, block, 0, s, src);
-    else hipLaunchKernelGGL((fused_quad_kernel<true, false, Src>), grid, block, 0, s, src);
+    if (one_chunk) launch_quad_fc<true, 1>(fullc, grid, s, src);
+    else launch_quad_fc<true, 0>(fullc, grid, s, src);
   } else {
-    if (fullc) hipLaunchKernelGGL((fused_quad_kernel<false, true, Src>), grid, block, 0, s, src);
-    else hipLaunchKernelGGL((fused_quad_kernel<false, false, Src>), grid, block, 0, s, src);
+    if (one_chunk) launch_quad_fc<false, 1>(fullc, grid, s, src);
+    else launch_quad_fc<false, 0>(fullc, grid, s, src);
   }
   return hipGetLastError();
 }
@@ -408,7 +419,7 @@ hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, int64_
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
   if (a.nsplit < 1 || a.kper < 1 || (int64_t)(a.nsplit - 1) * a.kper >= a.K)
     return hipErrorInvalidValue;  // every split needs at least one tap
-  return launch_quad_src(kc, a, a.C,
+  return launch_quad_src(kc, a, a.C, a.nchunk == 1,
                          (int64_t)a.B * kc.tiles_per_img * a.nsplit * kc.n_otiles, s);
 }
 
@@ -465,7 +476,9 @@ hipError_t launch_split_reduce(const float* part, int nsplit, uint32_t stride, c
 }
 
 hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
-  return launch_quad_src(kc, m, m.a[0].C, m.start[m.n], s);
+  bool one_chunk = true;
+  for (int i = 0; i < m.n; ++i) one_chunk = one_chunk && m.a[i].nchunk == 1;
+  return launch_quad_src(kc, m, m.a[0].C, one_chunk, m.start[m.n], s);
 }
 
 }  // namespace dcn
