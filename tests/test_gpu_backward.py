@@ -186,3 +186,47 @@ def test_backward_bf16_detection_full_size():
     for k in ("x", "offset", "mask", "weight", "bias"):
         worst = _check("detection_bf16 full grad_%s" % k, got[k], ref[k], norm[k])
         print("  grad_%s worst err/N %.3g" % (k, worst))
+
+
+# A seeded sweep of small random shapes through the whole backward: every
+# data-gradient variant (padded outputs 16 / 64 / 128 / 256), both weight-
+# gradient kernels, fp32 and bf16 plans, odd channel counts, rectangular
+# kernels, one-pixel and kernel-wider-than-map maps, optional mask, both
+# gradient layouts, every offset spread.
+def _sweep(n=24, seed=7):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype = "bf16" if rng.random() < 0.25 else "f32"
+        C = int(rng.choice([8, 16, 40, 64, 72, 128] if dtype == "bf16" else
+                           [4, 8, 12, 32, 36, 64, 72, 128, 132]))
+        O = int(rng.choice([1, 3, 16, 17, 40, 64, 65, 100, 128, 129, 200, 256]))
+        kh, kw = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        ph, pw = int(rng.integers(0, kh)), int(rng.integers(0, kw))
+        H = int(rng.integers(max(1, kh - 2 * ph), 21))
+        W = int(rng.integers(max(1, kw - 2 * pw), 21))
+        spec = synth.Spec("bsweep%d" % len(out), int(rng.integers(1, 3)), C, O, H, W, kh, kw,
+                          ph, pw, dtype, 2000 + len(out),
+                          str(rng.choice(["normal1.5", "normal4", "uniform2", "edge_mix", "zero"])),
+                          str(rng.choice(["sigmoid_normal", "uniform", "none"])),
+                          float(1.0 / np.sqrt(kh * kw * C)), "none")
+        if spec.Ho < 1 or spec.Wo < 1 or spec.pixels * O * spec.K * C > 20e6:
+            continue
+        out.append((spec, "nhwc" if rng.random() < 0.5 else "nchw"))
+    return out
+
+
+SWEEP = _sweep()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_backward_sweep(i):
+    spec, layout = SWEEP[i]
+    d = synth.make_inputs(spec)
+    gout = _grad_out(spec, 100 + i)
+    print("case", i, layout, spec, flush=True)
+    ref, norm = oracle.backward(oracle_shape(spec), d["x"], d["offset"], d["mask"], d["weight"],
+                                gout)
+    got = _run(spec, d, gout, layout)
+    for k in ("x", "offset", "mask", "weight", "bias"):
+        _check("%s/%s grad_%s" % (spec.name, layout, k), got[k], ref[k], norm[k])
