@@ -119,3 +119,39 @@ def test_dsample_zero_weights_and_all_outside_give_zero():
     d1 = dict(d)
     d1["offset"] = np.full_like(d["offset"], 1000.0)
     assert not _run(spec, d1, "nchw").any()
+
+
+# A seeded sweep of small random shapes: group counts and widths (D a
+# multiple of 4, or of 8 for bf16), rectangular kernels up to 7 x 7, any
+# padding, one-pixel maps, offsets from tight to far outside, softmax on and
+# off, both layouts.
+def _sweep(n=24, seed=13):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        bf16 = rng.random() < 0.3
+        kh, kw = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        ph, pw = int(rng.integers(0, kh)), int(rng.integers(0, kw))
+        H = int(rng.integers(max(1, kh - 2 * ph), 21))
+        W = int(rng.integers(max(1, kw - 2 * pw), 21))
+        spec = P5.scaled(B=int(rng.integers(1, 3)), G=int(rng.integers(1, 9)),
+                         D=int(rng.choice([8, 16, 24, 64, 96] if bf16 else [4, 8, 12, 16, 36, 64])),
+                         H=H, W=W, kh=kh, kw=kw, ph=ph, pw=pw,
+                         dtype="bf16" if bf16 else "f32", softmax=bool(rng.random() < 0.6),
+                         seed=400 + len(out), offset_std=float(rng.choice([0.5, 1.5, 4.0, 30.0])))
+        if spec.Ho < 1 or spec.Wo < 1:
+            continue
+        out.append((spec, "nhwc" if rng.random() < 0.5 else "nchw"))
+    return out
+
+
+SWEEP = _sweep()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_dsample_sweep(i):
+    spec, layout = SWEEP[i]
+    d = synth.make_ds_inputs(spec)
+    print("case", i, layout, spec, flush=True)
+    ref, norm = _oracle(spec, d)
+    _check(_run(spec, d, layout), ref, norm, "sweep%d/%s" % (i, layout))

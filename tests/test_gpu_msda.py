@@ -91,3 +91,42 @@ def test_msda_full_size(name):
     got = out.cpu().numpy().reshape(ref.shape)
     assert np.array_equal(got, out2.cpu().numpy().reshape(got.shape)), "not deterministic"
     print("worst err/N %.3g" % _check(got, ref, norm, name + " full"))
+
+
+# A seeded sweep of small random shapes: 1-8 levels of random sizes (down
+# to one pixel), 1-8 points per level, odd head counts and widths (D a
+# multiple of 4, or of 8 for bf16), softmax on and off, points partly or
+# wholly outside their level.
+def _sweep(n=24, seed=11):
+    rng = np.random.default_rng(seed)
+    base = M["msda_decoder_fp32"]
+    out = []
+    for i in range(n):
+        bf16 = rng.random() < 0.3
+        L = int(rng.integers(1, 9))
+        shapes = tuple((int(rng.integers(1, 20)), int(rng.integers(1, 20))) for _ in range(L))
+        D = int(rng.choice([8, 16, 24, 40, 64, 128] if bf16 else [4, 8, 12, 20, 32, 64, 100]))
+        lo = float(rng.choice([-0.05, -0.5, 1.2]))
+        out.append(base.scaled(B=int(rng.integers(1, 3)), Q=int(rng.integers(1, 60)),
+                               G=int(rng.integers(1, 9)), D=D, K=int(rng.integers(1, 9)),
+                               shapes=shapes, softmax=bool(rng.random() < 0.6), seed=300 + i,
+                               loc_lo=lo, loc_hi=lo + float(rng.choice([0.3, 1.1, 2.0])),
+                               dtype="bf16" if bf16 else "f32"))
+    return out
+
+
+SWEEP = _sweep()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_msda_sweep(i):
+    import torch
+    from modulated_deformable_convolution_dcn_amd import msda
+    spec = SWEEP[i]
+    d = synth.make_msda_inputs(spec)
+    print("case", i, spec, flush=True)
+    ref, norm = oracle.msda(d["value"], spec.shapes, d["locations"], d["weights"], spec.softmax)
+    dev = _device(spec, d)
+    out = msda(dev["value"], spec.shapes, dev["locations"], dev["weights"], softmax=spec.softmax)
+    torch.cuda.synchronize()
+    _check(out.cpu().numpy().reshape(ref.shape), ref, norm, "sweep%d" % i)
