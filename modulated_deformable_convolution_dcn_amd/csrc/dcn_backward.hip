@@ -551,29 +551,29 @@ __global__ __launch_bounds__(256) void bwd_weight_kernel(BwdArgs a, int tiles_pe
 // sample of the forward.  One workgroup per (tap, chunk, image, run of
 // 64-pixel tiles); wave w owns pixels [16w, 16w + 16) of every tile and
 // accumulates dW[all o][chunk's 64 c] over them in registers, so the main
-// loop has no barrier: per tile it blends its 16 samples x 64 channels
-// (corners loaded one tile ahead, 16 lanes per pixel, one 16-byte load per
-// corner) into a private transposed tile s[c][px] in LDS, then runs
-// 4 x NTO x 4 MFMAs: A = g^T fragments (4 consecutive pixels of one output,
-// one 16-byte load from an NCHW gradient), B = s^T fragments (one 16-byte
-// LDS read).  The four waves' partial sums meet in LDS once per run, then one
-// atomic add per weight element.
+// loop has no barrier.  Per tile it blends its 16 samples x 64 channels in 4
+// passes (corners loaded one tile ahead, 16 lanes per pixel, one 16-byte load
+// per corner): pass p gives lane (sl, q) = (lane % 16, lane / 16) channels
+// 4 sl .. 4 sl + 3 of pixel 4 q + p.  Those registers are the B operand of
+// MFMA k-step p as they stand -- k = q, column n = sl of output tile u holds
+// channel 4 n + u -- so the samples never go through LDS; A = g^T fragments
+// (4 consecutive pixels of one output, one 16-byte load from an NCHW
+// gradient; element p is pixel 4 q + p).  Tile u's column n is channel
+// 4 n + u of the chunk, which the epilogue undoes.  The four waves' partial
+// sums meet in LDS once per run, then one atomic add per weight element.
 template <int NTO, bool GV>  // 16-output tiles (OP / 16: 1 or 4); GV: NCHW g, Ho*Wo % 4 == 0
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
   constexpr int OP = 16 * NTO;
-  constexpr int SST = 20;                       // s^T row: 16 pixels + 4 (bank spread)
-  constexpr int ST_FLOATS = 64 * SST;           // one wave's s^T tile
   constexpr int RST = 64 + 4;                   // epilogue row: 64 channels + 4
-  constexpr int LOOP_BYTES = 4 * (ST_FLOATS * 4 + 2 * 16 * 32);
+  constexpr int LOOP_BYTES = 4 * 2 * 16 * 32;   // per wave: tables of two tiles
   constexpr int RED_BYTES = 4 * OP * RST * 4;
   constexpr int SMEM = LOOP_BYTES > RED_BYTES ? LOOP_BYTES : RED_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* const sT = reinterpret_cast<float*>(smem) + wave * ST_FLOATS;
-  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * ST_FLOATS * 4) + wave * 32;  // [2][16]
-  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * ST_FLOATS * 4 + 4 * 32 * 16) + wave * 32;
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem) + wave * 32;  // [2][16]
+  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * 32 * 16) + wave * 32;
   float* const red = reinterpret_cast<float*>(smem);  // [wave][o][RST]
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -626,24 +626,19 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
     }
   };
 
-  // ---- corners: pass p -> pixel 4p + lane / 16, channels 4 (lane % 16) ..
+  // ---- corners: pass p -> pixel 4 (lane / 16) + p, channels 4 (lane % 16) ..
   const int sl = lane & 15, pq = lane >> 4;
   const uint32_t cbyte = (uint32_t)(chunk * 64 + 4 * sl) * 4;
   const bool chan_ok = chunk * 64 + 4 * sl < a.C;
   u32x4 cv[4][4];
   auto c_issue = [&](int slot, int p) {
-    const u32x4 o4 = Co[slot * 16 + 4 * p + pq];
+    const u32x4 o4 = Co[slot * 16 + 4 * pq + p];
 #pragma unroll
     for (int q = 0; q < 4; ++q) cv[p][q] = load16(xr, chan_ok ? o4[q] + cbyte : kNoCorner);
   };
-  // s^T[c][px]: 16-byte chunk (px / 4) of row c stored at chunk (px / 4) ^ ((c / 16) & 3).
-  // A pass writes channels 4 sl + e of pixels 4 p + pq: the 80-float step of sl
-  // spreads bits 0-1 of sl over the banks, the swizzle bits 2-3, pq the words,
-  // so the 64 single-float writes hit 64 distinct banks; a fragment read (16
-  // rows of one swizzle group) is spread by the row stride alone.
-  auto st_at = [](int c, int px) { return c * SST + 4 * ((px >> 2) ^ ((c >> 4) & 3)) + (px & 3); };
+  // the modulated sample of pass p: channels 4 sl .. 4 sl + 3 of pixel 4 pq + p
   auto blend = [&](int slot, int p) {
-    const f32x4 w4 = Cw[slot * 16 + 4 * p + pq];
+    const f32x4 w4 = Cw[slot * 16 + 4 * pq + p];
     f32x4 sv = __builtin_bit_cast(f32x4, cv[p][0]) * w4[0];
 #pragma unroll
     for (int q = 1; q < 4; ++q) {
@@ -651,8 +646,7 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(w4[q], v[e], sv[e]);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sT[st_at(4 * sl + e, 4 * p + pq)] = sv[e];
+    return sv;
   };
 
   // ---- g^T fragments: lane -> output 16t + lane % 16, pixels 4 (lane / 16) ..
@@ -691,25 +685,19 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
       t_build(P ^ 1, tile + 1);
       t_load(tile + 2 < t_end ? tile + 2 : tile + 1);
     }
+    // dW[o][c] += sum over the wave's 16 pixels: k-step p takes pixels
+    // 4 q + p (q = lane / 16) -- the samples of pass p -- and column n of
+    // tile u is channel 4 n + u
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      blend(P, p);
+      const f32x4 sv = blend(P, p);
       if (more) c_issue(P ^ 1, p);
-    }
-    // dW[o][c] += sum over the wave's 16 pixels: 4 k-steps of 4 pixels
-    f32x4 bf[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = 16 * u + rl;
-      bf[u] = *reinterpret_cast<const f32x4*>(&sT[c * SST + 4 * (g ^ u)]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int t = 0; t < NTO; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(gf[t][e], bf[u][e], acc[t][u], 0, 0, 0);
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(gf[t][p], sv[u], acc[t][u], 0, 0, 0);
+    }
     if (more) g_load(tile + 1);
   };
 
@@ -730,14 +718,15 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
 
   // ---- the four waves' partial sums, then one atomic add per element
   __syncthreads();  // every wave is done with its s^T tile and tables
-  // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r (output), column l % 16 (channel)
+  // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r (output), column
+  // l % 16 (channel 4 (l % 16) + u of tile u)
 #pragma unroll
   for (int t = 0; t < NTO; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        red[(wave * OP + 16 * t + 4 * g + r) * RST + 16 * u + rl] = acc[t][u][r];
+        red[(wave * OP + 16 * t + 4 * g + r) * RST + 4 * rl + u] = acc[t][u][r];
   __syncthreads();
   for (int e = tid; e < OP * 64; e += 256) {
     const int o = e >> 6, c = e & 63;
