@@ -23,10 +23,12 @@
 //              far corners straight to memory), and the mask / offset sums
 //              reduced over the 16 lanes of the pixel;
 //   bwd_weight one workgroup per (tap, chunk, image, run of pixel tiles):
-//              the modulated column tile and the g tile go to LDS transposed
-//              and MFMA accumulates dW[c, o] over the run, then one atomic
-//              add per weight element;
-//   bwd_bias   a per-channel sum of g.
+//              MFMA accumulates dW over the run in registers, then one
+//              atomic add per weight element; up to 64 outputs each wave
+//              feeds its blended samples to the MFMA straight from
+//              registers (bwd_weight2), wider outputs go through LDS tiles
+//              (bwd_weight);
+//   bwd_bias   a per-output sum of g.
 
 #include <type_traits>
 
