@@ -462,97 +462,13 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 }
 
 // ---------------------------------------------------------------- weight grad
-template <int NT>  // 16-column output tiles per wave = OP / 16
-__global__ __launch_bounds__(256) void bwd_weight_kernel(BwdArgs a, int tiles_per_run,
-                                                         int runs_per_img) {
-  constexpr int OP = 16 * NT;
-  constexpr int ST_ = TILE + GPAD;
-  __shared__ __attribute__((aligned(16))) float ST[64 * ST_];   // [channel][pixel]
-  __shared__ __attribute__((aligned(16))) float GT[OP * ST_];   // [output][pixel]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  // (tap, chunk) fastest: the workgroups of one XCD share pixel runs, so
-  // neighbouring taps' corner reads meet in that XCD's L2
-  const int kb = logical % (a.K * a.nchunk);
-  const int t2 = logical / (a.K * a.nchunk);
-  const int run = t2 % runs_per_img;
-  const int b = t2 / runs_per_img;
-  const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
-  const int rl = lane & 15, g = lane >> 4;
-  const int sl = tid & 15;
-  const int ch = chunk * 64 + 4 * sl;
-  const bool chan_ok = ch < a.C;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
-
-  f32x4 acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int t_end = min((run + 1) * tiles_per_run, a.tiles_per_img);
-  for (int tile = run * tiles_per_run; tile < t_end; ++tile) {
-    const int hw0 = tile * TILE;
-    __syncthreads();  // previous tile's operands consumed
-    // modulated column tile, transposed: ST[c][px]
-#pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-      const int px = 16 * p + (tid >> 4);
-      const int hw = hw0 + px;
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if (hw < a.HoWo && chan_ok) {
-        const int ho = hw / a.Wo, wo = hw - (hw / a.Wo) * a.Wo;
-        const TapTerms t = tap_terms(a, b, ho, wo, k);
-        const float m = a.mask ? a.mask[((size_t)(b * a.K + k)) * a.HoWo + hw] : 1.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t off = t.ok[q] ? ((uint32_t)t.pix[q] * (uint32_t)a.C + (uint32_t)ch) * 4u
-                                       : kNoCorner;
-          const f32x4 v = __builtin_bit_cast(f32x4, load16(xr, off));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] = __builtin_fmaf(t.w[q], v[e], s[e]);
-        }
-        s = s * m;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ST[(4 * sl + e) * ST_ + px] = s[e];
-    }
-    // g tile, transposed: GT[o][px]
-    for (int e = tid; e < OP * TILE; e += 256) {
-      const int o = e / TILE, px = e % TILE;
-      const int hw = hw0 + px;
-      GT[o * ST_ + px] = (o < a.O && hw < a.HoWo) ? gout_at(a, b, o, hw) : 0.0f;
-    }
-    __syncthreads();
-    // dW[c, o] += sum_px ST[c][px] GT[o][px]: wave w -> channel rows 16w..
-#pragma unroll
-    for (int j = 0; j < TILE / 16; ++j) {
-      const f32x4 af = *reinterpret_cast<const f32x4*>(&ST[(16 * wave + rl) * ST_ + 16 * j + 4 * g]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f32x4 bf = *reinterpret_cast<const f32x4*>(&GT[(16 * nt + rl) * ST_ + 16 * j + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[e], acc[nt], 0, 0, 0);
-      }
-    }
-  }
-  const int i = k / a.kw, jj = k - (k / a.kw) * a.kw;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int o = 16 * nt + rl;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = chunk * 64 + 16 * wave + 4 * g + r;
-      if (c < a.C && o < a.O)
-        atomic_add(a.gw + (((size_t)o * a.C + c) * a.kh + i) * a.kw + jj, acc[nt][r]);
-    }
-  }
-}
-
-// Weight gradient, wave-private pipeline (fp32, up to 64 outputs).
+// Weight gradient, wave-private pipeline (fp32).
 // dW[o, c, k] = sum over pixels of g[px, o] * s[px, k, c], s the modulated
-// sample of the forward.  One workgroup per (tap, chunk, image, run of
-// 64-pixel tiles); wave w owns pixels [16w, 16w + 16) of every tile and
-// accumulates dW[all o][chunk's 64 c] over them in registers, so the main
+// sample of the forward.  One workgroup per (output tile of OP, tap, chunk,
+// image, run of 64-pixel tiles), output tiles fastest so that the tiles of
+// one sample run meet its corners in the same L2; wave w owns pixels
+// [16w, 16w + 16) of every tile and accumulates dW[the tile's o][chunk's
+// 64 c] over them in registers, so the main
 // loop has no barrier.  Per tile it blends its 16 samples x 64 channels in 4
 // passes (corners loaded one tile ahead, 16 lanes per pixel, one 16-byte load
 // per corner): pass p gives lane (sl, q) = (lane % 16, lane / 16) channels
@@ -565,7 +481,7 @@ __global__ __launch_bounds__(256) void bwd_weight_kernel(BwdArgs a, int tiles_pe
 // sums meet in LDS once per run, then one atomic add per weight element.
 template <int NTO, bool GV>  // 16-output tiles (OP / 16: 1 or 4); GV: NCHW g, Ho*Wo % 4 == 0
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
-bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
+bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img) {
   constexpr int OP = 16 * NTO;
   constexpr int RST = 64 + 4;                   // epilogue row: 64 channels + 4
   constexpr int LOOP_BYTES = 4 * 2 * 16 * 32;   // per wave: tables of two tiles
@@ -579,14 +495,18 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
   float* const red = reinterpret_cast<float*>(smem);  // [wave][o][RST]
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  // (tap, chunk) fastest: the workgroups of one XCD share pixel runs, so
-  // neighbouring taps' corner reads meet in that XCD's L2
-  const int kb = logical % (a.K * a.nchunk);
-  const int t2 = logical / (a.K * a.nchunk);
+  // output tile, then (tap, chunk) fastest: the workgroups of one XCD share
+  // pixel runs, so one run's corner reads (every output tile reads the same
+  // ones, neighbouring taps nearly the same) meet in that XCD's L2
+  const int otile = logical % n_otiles;
+  const int t1 = logical / n_otiles;
+  const int kb = t1 % (a.K * a.nchunk);
+  const int t2 = t1 / (a.K * a.nchunk);
   const int run = t2 % runs_per_img;
   const int b = t2 / runs_per_img;
   const int k = kb / a.nchunk, chunk = kb - k * a.nchunk;
   const int ki = k / a.kw, kj = k - ki * a.kw;
+  const int o0 = otile * OP;  // first output of the tile
   const int t_begin = run * tiles_per_run;
   const int t_end = min(t_begin + tiles_per_run, a.tiles_per_img);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
@@ -658,7 +578,7 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
     const int hw = tile * 64 + 16 * wave + 4 * g;
 #pragma unroll
     for (int t = 0; t < NTO; ++t) {
-      const int o = 16 * t + rl;
+      const int o = o0 + 16 * t + rl;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (o < a.O) {
         if constexpr (GV) {
@@ -731,11 +651,11 @@ bwd_weight2_kernel(BwdArgs a, int tiles_per_run, int runs_per_img) {
         red[(wave * OP + 16 * t + 4 * g + r) * RST + 4 * rl + u] = acc[t][u][r];
   __syncthreads();
   for (int e = tid; e < OP * 64; e += 256) {
-    const int o = e >> 6, c = e & 63;
-    const int cc = chunk * 64 + c;
+    const int ol = e >> 6, c = e & 63;
+    const int o = o0 + ol, cc = chunk * 64 + c;
     if (o >= a.O || cc >= a.C) continue;
-    const float v = red[(0 * OP + o) * RST + c] + red[(1 * OP + o) * RST + c] +
-                    red[(2 * OP + o) * RST + c] + red[(3 * OP + o) * RST + c];
+    const float v = red[(0 * OP + ol) * RST + c] + red[(1 * OP + ol) * RST + c] +
+                    red[(2 * OP + ol) * RST + c] + red[(3 * OP + ol) * RST + c];
     atomic_add(a.gw + (((size_t)o * a.C + cc) * a.kh + ki) * a.kw + kj, v);
   }
 }
@@ -893,12 +813,14 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.gw) {
-    // runs of pixel tiles.  The wave-private kernel (O <= 64) holds two
-    // workgroups per CU: at most 512 workgroups, so the grid is one round
-    // and each run's closing reduction is spread over many tiles.  The
-    // other: about 2048 workgroups.
-    const int64_t per_run_units = (int64_t)a.K * a.nchunk * a.B;
-    int64_t runs = OP <= 64 ? 512 / per_run_units : (2048 + per_run_units - 1) / per_run_units;
+    // output tiles of 16 (O <= 16) or 64, and runs of pixel tiles: two
+    // workgroups per CU, at most 512 workgroups when the units allow, so the
+    // grid is about one round and each run's closing reduction is spread
+    // over many tiles
+    const int wop = OP <= 16 ? 16 : 64;
+    const int n_ot = (a.O + wop - 1) / wop;
+    const int64_t per_run_units = (int64_t)a.K * a.nchunk * a.B * n_ot;
+    int64_t runs = 512 / per_run_units;
     if (runs > a.tiles_per_img) runs = a.tiles_per_img;
     if (runs < 1) runs = 1;
     const int tiles_per_run = (int)((a.tiles_per_img + runs - 1) / runs);
@@ -908,16 +830,12 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     const dim3 grid((unsigned)g), block(256);
     const bool gv = !a.nhwc_g && a.HoWo % 4 == 0;
 #define DCN_W2(NTO)                                                                         \
-  if (gv) hipLaunchKernelGGL((bwd_weight2_kernel<NTO, true>), grid, block, 0, s, a,         \
+  if (gv) hipLaunchKernelGGL((bwd_weight2_kernel<NTO, true>), grid, block, 0, s, a, n_ot,   \
                              tiles_per_run, runs_per_img);                                  \
-  else hipLaunchKernelGGL((bwd_weight2_kernel<NTO, false>), grid, block, 0, s, a,           \
+  else hipLaunchKernelGGL((bwd_weight2_kernel<NTO, false>), grid, block, 0, s, a, n_ot,     \
                           tiles_per_run, runs_per_img)
-    switch (OP) {
-      case 16: DCN_W2(1); break;
-      case 64: DCN_W2(4); break;
-      case 128: hipLaunchKernelGGL(bwd_weight_kernel<8>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
-      default: hipLaunchKernelGGL(bwd_weight_kernel<16>, grid, block, 0, s, a, tiles_per_run, runs_per_img); break;
-    }
+    if (wop == 16) DCN_W2(1);
+    else DCN_W2(4);
 #undef DCN_W2
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
