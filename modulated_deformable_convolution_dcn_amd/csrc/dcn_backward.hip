@@ -149,7 +149,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   constexpr int SINK = bwd_window_floats(OP);
   __shared__ __attribute__((aligned(16))) float win[SINK + 64];
   // two sets of tables of the block's 64 sampling points (written by wave 0):
-  //   Ti {y0, x0, validity bits, pixel inside the output}, Tf {ly, lx, mask}
+  //   Ti {y0, x0, validity bits, byte offset of corner (0,0) in x}, Tf {ly, lx, mask}
   //   Si {window offset of corner (0,0), corner flags, image pixel of (0,0)},
   //   Sf {mask x corner weight, 0 for an invalid corner}
   // corner flags: bit q = in the window, bit 4 + q = valid but outside it
@@ -210,7 +210,10 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
     const int y0 = tp.y0;
     const int x0 = tp.x0;
     const uint32_t v4 = t_in ? tp.valid : 0u;
-    Ti[slot][tid] = make_int4(y0, x0, (int)v4, t_in ? 1 : 0);
+    // corner (0,0)'s byte offset; the other corners are a uniform step away
+    // (used only for valid corners, whose offsets are exact and in range)
+    const uint32_t b00 = (uint32_t)((b * a.H + y0) * a.W + x0) * ((uint32_t)a.C * 4u);
+    Ti[slot][tid] = make_int4(y0, x0, (int)v4, (int)b00);
     Tf[slot][tid] = f32x4{tp.p.ly, tp.p.lx, n_m, 0.0f};
     const float hy = 1.0f - tp.p.ly, hx = 1.0f - tp.p.lx;
     const float wv[4] = {hy * hx, hy * tp.p.lx, tp.p.ly * hx, tp.p.ly * tp.p.lx};
@@ -254,6 +257,10 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
     }
   };
 
+  // byte steps from corner (0,0) to corners (0,1), (1,0), (1,1) in x
+  const uint32_t row_b = (uint32_t)a.C * 4u;
+  const uint32_t corner_step[4] = {0u, row_b, (uint32_t)a.W * row_b, (uint32_t)(a.W + 1) * row_b};
+
   for (int chunk = 0; chunk < a.nchunk; ++chunk) {
     for (int e = tid; e < nwin * WSTR; e += NT) win[e] = 0.0f;
     const int ch = chunk * 64 + 4 * sl;
@@ -264,12 +271,11 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
         const int4 ti = Ti[S][(NT / 16) * p + (tid >> 4)];
+        const uint32_t base = (uint32_t)ti.w + (uint32_t)ch * 4u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bool ok = chan_ok && ((ti.z >> q) & 1);
-          const int pix = (b * a.H + ti.x + (q >> 1)) * a.W + ti.y + (q & 1);
-          cv[S][p][q] = load16(xr, ok ? ((uint32_t)pix * (uint32_t)a.C + (uint32_t)ch) * 4u
-                                      : kNoCorner);
+          cv[S][p][q] = load16(xr, ok ? base + corner_step[q] : kNoCorner);
         }
       }
     };
@@ -346,8 +352,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           const float vx[4] = {-hy, hy, -ly, ly};
           const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (!((ti.z >> q) & 1)) continue;
+          for (int q = 0; q < 4; ++q) {  // an outside corner was loaded as zeros: no terms
             const f32x4 v = __builtin_bit_cast(f32x4, cv[P][p][q]);
             float t = gs[0] * v[0];
 #pragma unroll
