@@ -152,7 +152,8 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   //   Ti {y0, x0, validity bits, byte offset of corner (0,0) in x}, Tf {ly, lx, mask}
   //   Si {window offset of corner (0,0), corner flags, image pixel of (0,0)},
   //   Sf {mask x corner weight, 0 for an invalid corner}
-  // corner flags: bit q = in the window, bit 4 + q = valid but outside it
+  // corner flags: bit q = in the window, bit 4 + q = valid but outside it,
+  // bits 8-9 = window row of corner (0,0) mod 4
   __shared__ int4 Ti[2][TILE];
   __shared__ f32x4 Tf[2][TILE];
   __shared__ int4 Si[2][TILE];
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       const bool inwin = use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW;
       if (ok) flags |= inwin ? (1 << q) : (16 << q);
     }
+    flags |= ((y0 - wy0) & 3) << 8;  // window row mod 4 (scatter classes)
     Si[slot][tid] = make_int4(((y0 - wy0) * WW + (x0 - wx0)) * WSTR, flags,
                               (b * a.H + y0) * a.W + x0, (y0 - wy0) + (x0 - wx0));
     Sf[slot][tid] = cf;
@@ -375,13 +377,13 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       // (2b) scatter.  Window position (wy, wx) belongs to wave (wy + wx) mod
       // 8, so no two waves ever update one position and the updates are plain
       // LDS read-add-writes (float atomics cost far more).  Per corner index
-      // the wave lists its positions (position, pixel, weight) in LDS, then
-      // takes them 4 at a time: 16 lanes per item, 4 channels per lane, one
-      // 16-byte read, 4 FMAs and one 16-byte write per lane.  A batch that
-      // names one position twice runs its items one after another with
-      // lane = channel; the next batch's reads follow this batch's writes in
-      // the wave's LDS order.  Far corners of the wave's 8 pixels go to
-      // memory with atomics.
+      // the wave lists its positions (position, pixel, weight) in LDS, grouped
+      // by window row mod 4, and takes one of each group at a time: 16
+      // lanes per item, 4 channels per lane, one 16-byte read, 4 FMAs and one
+      // 16-byte write per lane.  Equal positions fall in one group, so a batch
+      // never names a position twice, and the next batch's reads follow this
+      // batch's writes in the wave's LDS order.  Far corners of the wave's 8
+      // pixels go to memory with atomics.
       if (want_gx) {
         const int4 si = Si[P][lane];  // lane = pixel
         const f32x4 sf = Sf[P][lane];
@@ -404,42 +406,51 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
             if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
               atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
           }
-          const uint64_t m_own = __ballot(own);
-          const int n = __builtin_popcountll(m_own);
-          if (own) {
-            const int idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_own >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m_own, 0));
-            ilist[wave][idx] = make_int2(((si.x + cwin) << 6) | lane, __float_as_int(sfq));
+          // position classes (window row mod 4): a class's items are listed
+          // together, and batch j takes the j-th item of each class (lane
+          // group g <- class g), so no two items of a batch name one position
+          const int posq = si.x + cwin;
+          const int cls = ((si.y >> 8) + (q >> 1)) & 3;
+          uint64_t mc[4];
+          int nc[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            mc[g] = __ballot(own && cls == g);
+            nc[g] = __builtin_popcountll(mc[g]);
           }
-          for (int j = 0; j < n; j += 4) {
-            const bool valid = j + grp < n;
-            const int2 it = ilist[wave][valid ? j + grp : 0];
-            const int pos = valid ? it.x >> 6 : SINK;
-            const int p = it.x & 63;
-            const float c = valid ? __int_as_float(it.y) : 0.0f;
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gsT[p * SST + 4 * sub]);
-            float* dst = &win[pos + 4 * sub];
-            // positions of the 4 items (wave-uniform): any repeat?
-            const int s0 = __builtin_amdgcn_readlane(pos, 0), s1 = __builtin_amdgcn_readlane(pos, 16);
-            const int s2 = __builtin_amdgcn_readlane(pos, 32), s3 = __builtin_amdgcn_readlane(pos, 48);
-            const bool rep = (s1 != SINK && s1 == s0) ||
-                             (s2 != SINK && (s2 == s0 || s2 == s1)) ||
-                             (s3 != SINK && (s3 == s0 || s3 == s1 || s3 == s2));
-            if (!rep) {
+          const int b1 = nc[0], b2 = b1 + nc[1], b3 = b2 + nc[2];
+          const int nb = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
+          if (own) {
+            const uint64_t mm = cls == 0 ? mc[0] : cls == 1 ? mc[1] : cls == 2 ? mc[2] : mc[3];
+            const int base = cls == 0 ? 0 : cls == 1 ? b1 : cls == 2 ? b2 : b3;
+            const int idx = base + __builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+            ilist[wave][idx] = make_int2((posq << 6) | lane, __float_as_int(sfq));
+          }
+          const int my_n = grp == 0 ? nc[0] : grp == 1 ? nc[1] : grp == 2 ? nc[2] : nc[3];
+          const int my_base = grp == 0 ? 0 : grp == 1 ? b1 : grp == 2 ? b2 : b3;
+          // 4 batches at a time: their list entries and gs slices are read
+          // back to back, then the read-add-writes in order
+          for (int j0 = 0; j0 < nb; j0 += 4) {
+            int2 its[4];
+            f32x4 g4s[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              its[bb] = ilist[wave][j0 + bb < my_n ? my_base + j0 + bb : 0];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              g4s[bb] = *reinterpret_cast<const f32x4*>(&gsT[(its[bb].x & 63) * SST + 4 * sub]);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              if (j0 + bb >= nb) break;  // uniform
+              const bool valid = j0 + bb < my_n;
+              const int pos = valid ? its[bb].x >> 6 : SINK;
+              const float c = valid ? __int_as_float(its[bb].y) : 0.0f;
+              float* dst = &win[pos + 4 * sub];
               f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4[e], c, w4[e]);
+              for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4s[bb][e], c, w4[e]);
               *reinterpret_cast<f32x4*>(dst) = w4;
-            } else {
-              // one item after another, lane = channel: each lane's own
-              // read-add-write sequence then orders the repeats
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int pi = __builtin_amdgcn_readlane(pos, 16 * i);
-                const int ppi = __builtin_amdgcn_readlane(p, 16 * i);
-                const float ci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 16 * i));
-                win[pi + lane] = __builtin_fmaf(gsT[ppi * SST + lane], ci, win[pi + lane]);
-              }
             }
           }
         });
