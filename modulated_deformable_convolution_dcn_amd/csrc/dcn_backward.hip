@@ -158,8 +158,9 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   __shared__ f32x4 Tf[2][TILE];
   __shared__ int4 Si[2][TILE];
   __shared__ f32x4 Sf[2][TILE];
+  const float* const Sfl = reinterpret_cast<const float*>(&Sf[0][0]);  // [2][TILE][4]
   __shared__ float red[2][3][TILE];  // mask, dy, dx sums of a tap
-  __shared__ int2 ilist[NW][TILE];   // per wave: scatter items of one corner index
+  __shared__ int ilist[NW][2 * TILE];  // per wave: scatter items of one corner pair
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mr = wave & 3, mh = wave >> 2;  // MFMA: pixel rows 16 mr .., channels 32 mh ..
@@ -376,82 +377,89 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       }
       // (2b) scatter.  Window position (wy, wx) belongs to wave (wy + wx) mod
       // 8, so no two waves ever update one position and the updates are plain
-      // LDS read-add-writes (float atomics cost far more).  Per corner index
-      // the wave lists its positions (position, pixel, weight) in LDS, grouped
+      // LDS read-add-writes (float atomics cost far more).  Per corner pair
+      // the wave lists its positions (position, pixel, corner) in LDS, grouped
       // by window row mod 4, and takes one of each group at a time: 16
       // lanes per item, 4 channels per lane, one 16-byte read, 4 FMAs and one
       // 16-byte write per lane.  Equal positions fall in one group, so a batch
       // never names a position twice, and the next batch's reads follow this
-      // batch's writes in the wave's LDS order.  Far corners of the wave's 8
-      // pixels go to memory with atomics.
+      // batch's writes in the wave's LDS order.  The pairs are corners (0,0),
+      // (0,1) and corners (1,0), (1,1): each pair's positions share a window
+      // row.  Far corners of the wave's 8 pixels go to memory with atomics.
       if (want_gx) {
         const int4 si = Si[P][lane];  // lane = pixel
         const f32x4 sf = Sf[P][lane];
         const int grp = lane >> 4, sub = lane & 15;
-        static_for<4>([&](auto Q) {
-          constexpr int q = decltype(Q)::value;
-          constexpr int dq = (q >> 1) + (q & 1);
-          const int cwin = (q >> 1) * WW * WSTR + (q & 1) * WSTR;
-          // the corner weight as a scalar first: taking the bits of a vector
-          // element directly reads element 0 with this compiler
-          const float sfq = sf[q];
-          const bool own = ((si.y >> q) & 1) && ((si.w + dq) & (NW - 1)) == wave;
-          const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 3) == wave;
-          uint64_t m_far = __ballot(far);
-          while (m_far) {
-            const int p = __builtin_ctzll(m_far);
-            m_far &= m_far - 1;
-            const int pix = __builtin_amdgcn_readlane(si.z, p) + (q >> 1) * a.W + (q & 1);
-            const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
-            if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
-              atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
+        const int row0 = si.y >> 8;  // window row of corner (0,0), mod 4
+        static_for<2>([&](auto H) {
+          constexpr int h = decltype(H)::value;  // corners 2h, 2h + 1: one window row
+          bool own[2];
+          int ent[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int q = 2 * h + u, dq = h + u;
+            // the corner weight as a scalar first: taking the bits of a vector
+            // element directly reads element 0 with this compiler
+            const float sfq = sf[q];
+            const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 3) == wave;
+            uint64_t m_far = __ballot(far);
+            while (m_far) {
+              const int p = __builtin_ctzll(m_far);
+              m_far &= m_far - 1;
+              const int pix = __builtin_amdgcn_readlane(si.z, p) + h * a.W + u;
+              const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
+              if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
+                atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
+            }
+            own[u] = ((si.y >> q) & 1) && ((si.w + dq) & (NW - 1)) == wave;
+            // list entry: window position index, then pixel and corner (the
+            // corner weight is read back from the table)
+            ent[u] = (((si.x >> 6) + h * WW + u) << 8) | (lane << 2) | q;
           }
           // position classes (window row mod 4): a class's items are listed
           // together, and batch j takes the j-th item of each class (lane
           // group g <- class g), so no two items of a batch name one position
-          const int posq = si.x + cwin;
-          const int cls = ((si.y >> 8) + (q >> 1)) & 3;
-          uint64_t mc[4];
-          int nc[4];
+          const int cls = (row0 + h) & 3;
+          uint64_t mc[2][4];
+          int nc[2][4];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              mc[u][g] = __ballot(own[u] && cls == g);
+              nc[u][g] = __builtin_popcountll(mc[u][g]);
+            }
+          int cb[5], ncl[4];  // class starts and sizes (class-major, then corner)
+          cb[0] = 0;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            mc[g] = __ballot(own && cls == g);
-            nc[g] = __builtin_popcountll(mc[g]);
+            ncl[g] = nc[0][g] + nc[1][g];
+            cb[g + 1] = cb[g] + ncl[g];
           }
-          const int b1 = nc[0], b2 = b1 + nc[1], b3 = b2 + nc[2];
-          const int nb = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
-          if (own) {
-            const uint64_t mm = cls == 0 ? mc[0] : cls == 1 ? mc[1] : cls == 2 ? mc[2] : mc[3];
-            const int base = cls == 0 ? 0 : cls == 1 ? b1 : cls == 2 ? b2 : b3;
-            const int idx = base + __builtin_amdgcn_mbcnt_hi(
-                                       (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
-            ilist[wave][idx] = make_int2((posq << 6) | lane, __float_as_int(sfq));
-          }
-          const int my_n = grp == 0 ? nc[0] : grp == 1 ? nc[1] : grp == 2 ? nc[2] : nc[3];
-          const int my_base = grp == 0 ? 0 : grp == 1 ? b1 : grp == 2 ? b2 : b3;
-          // 4 batches at a time: their list entries and gs slices are read
-          // back to back, then the read-add-writes in order
-          for (int j0 = 0; j0 < nb; j0 += 4) {
-            int2 its[4];
-            f32x4 g4s[4];
+          const int nb = max(max(ncl[0], ncl[1]), max(ncl[2], ncl[3]));
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              its[bb] = ilist[wave][j0 + bb < my_n ? my_base + j0 + bb : 0];
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              g4s[bb] = *reinterpret_cast<const f32x4*>(&gsT[(its[bb].x & 63) * SST + 4 * sub]);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              if (j0 + bb >= nb) break;  // uniform
-              const bool valid = j0 + bb < my_n;
-              const int pos = valid ? its[bb].x >> 6 : SINK;
-              const float c = valid ? __int_as_float(its[bb].y) : 0.0f;
-              float* dst = &win[pos + 4 * sub];
-              f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4s[bb][e], c, w4[e]);
-              *reinterpret_cast<f32x4*>(dst) = w4;
+          for (int u = 0; u < 2; ++u)
+            if (own[u]) {
+              const uint64_t mm = cls == 0 ? mc[u][0] : cls == 1 ? mc[u][1] : cls == 2 ? mc[u][2] : mc[u][3];
+              int base = cls == 0 ? cb[0] : cls == 1 ? cb[1] : cls == 2 ? cb[2] : cb[3];
+              if (u == 1) base += cls == 0 ? nc[0][0] : cls == 1 ? nc[0][1] : cls == 2 ? nc[0][2] : nc[0][3];
+              const int idx = base + __builtin_amdgcn_mbcnt_hi(
+                                         (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+              ilist[wave][idx] = ent[u];
             }
+          const int my_n = grp == 0 ? ncl[0] : grp == 1 ? ncl[1] : grp == 2 ? ncl[2] : ncl[3];
+          const int my_base = grp == 0 ? cb[0] : grp == 1 ? cb[1] : grp == 2 ? cb[2] : cb[3];
+          for (int j = 0; j < nb; ++j) {
+            const bool valid = j < my_n;
+            const int it = ilist[wave][valid ? my_base + j : 0];
+            const int pos = valid ? (it >> 8) * WSTR : SINK;
+            const float c = valid ? Sfl[P * TILE * 4 + (it & 255)] : 0.0f;
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 2) & 63) * SST + 4 * sub]);
+            float* dst = &win[pos + 4 * sub];
+            f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4[e], c, w4[e]);
+            *reinterpret_cast<f32x4*>(dst) = w4;
           }
         });
       }
