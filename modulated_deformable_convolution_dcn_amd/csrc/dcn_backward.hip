@@ -449,16 +449,33 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
             }
           const int my_n = grp == 0 ? ncl[0] : grp == 1 ? ncl[1] : grp == 2 ? ncl[2] : ncl[3];
           const int my_base = grp == 0 ? cb[0] : grp == 1 ? cb[1] : grp == 2 ? cb[2] : cb[3];
-          for (int j = 0; j < nb; ++j) {
+          // software pipeline: while batch j updates the window, the weight
+          // and gs slice of batch j + 1 and the list entry of batch j + 2 are
+          // in flight
+          auto entry = [&](int j) { return ilist[wave][j < my_n ? my_base + j : 0]; };
+          int e_next = entry(1), pos;
+          float c;
+          f32x4 g4;
+          auto fetch = [&](int j, int it) {
             const bool valid = j < my_n;
-            const int it = ilist[wave][valid ? my_base + j : 0];
-            const int pos = valid ? (it >> 8) * WSTR : SINK;
-            const float c = valid ? Sfl[P * TILE * 4 + (it & 255)] : 0.0f;
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 2) & 63) * SST + 4 * sub]);
+            pos = valid ? (it >> 8) * WSTR : SINK;
+            const float cw = Sfl[P * TILE * 4 + (it & 255)];
+            c = valid ? cw : 0.0f;
+            g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 2) & 63) * SST + 4 * sub]);
+          };
+          fetch(0, entry(0));
+          for (int j = 0; j < nb; ++j) {
             float* dst = &win[pos + 4 * sub];
             f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
+            const float cj = c;
+            const f32x4 gj = g4;
+            {  // the last batch fetches entry 0 and the sink: harmless
+              const int e = e_next;
+              e_next = entry(j + 2);
+              fetch(j + 1, e);
+            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(g4[e], c, w4[e]);
+            for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(gj[e], cj, w4[e]);
             *reinterpret_cast<f32x4*>(dst) = w4;
           }
         });
