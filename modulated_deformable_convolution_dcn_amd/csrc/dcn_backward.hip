@@ -420,35 +420,40 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           // together, and batch j takes the j-th item of each class (lane
           // group g <- class g), so no two items of a batch name one position
           const int cls = (row0 + h) & 3;
-          uint64_t mc[2][4];
-          int nc[2][4];
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
+          // wave-uniform: class bits and owners as masks; per class and
+          // corner the bucket sizes, packed one byte per class (every count
+          // is at most 128): bucket starts of corner 0 and corner 1 items,
+          // class sizes
+          const uint64_t X = __ballot(cls & 1), Y = __ballot(cls & 2);
+          const uint64_t O0 = __ballot(own[0]), O1 = __ballot(own[1]);
+          uint32_t st0 = 0, st1 = 0, szs = 0;
+          int nb = 0;
+          {
+            int acc = 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              mc[u][g] = __ballot(own[u] && cls == g);
-              nc[u][g] = __builtin_popcountll(mc[u][g]);
+              const uint64_t cm = ((g & 1) ? X : ~X) & ((g & 2) ? Y : ~Y);
+              const int n0 = __builtin_popcountll(O0 & cm), n1 = __builtin_popcountll(O1 & cm);
+              st0 |= (uint32_t)acc << (8 * g);
+              st1 |= (uint32_t)(acc + n0) << (8 * g);
+              szs |= (uint32_t)(n0 + n1) << (8 * g);
+              acc += n0 + n1;
+              nb = max(nb, n0 + n1);
             }
-          int cb[5], ncl[4];  // class starts and sizes (class-major, then corner)
-          cb[0] = 0;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            ncl[g] = nc[0][g] + nc[1][g];
-            cb[g + 1] = cb[g] + ncl[g];
           }
-          const int nb = max(max(ncl[0], ncl[1]), max(ncl[2], ncl[3]));
+          // lanes of another class than this lane's
+          const uint64_t other = (X ^ ((cls & 1) ? ~0ull : 0ull)) | (Y ^ ((cls & 2) ? ~0ull : 0ull));
 #pragma unroll
           for (int u = 0; u < 2; ++u)
             if (own[u]) {
-              const uint64_t mm = cls == 0 ? mc[u][0] : cls == 1 ? mc[u][1] : cls == 2 ? mc[u][2] : mc[u][3];
-              int base = cls == 0 ? cb[0] : cls == 1 ? cb[1] : cls == 2 ? cb[2] : cb[3];
-              if (u == 1) base += cls == 0 ? nc[0][0] : cls == 1 ? nc[0][1] : cls == 2 ? nc[0][2] : nc[0][3];
-              const int idx = base + __builtin_amdgcn_mbcnt_hi(
-                                         (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+              const uint64_t mm = (u ? O1 : O0) & ~other;
+              const int idx = (int)__builtin_amdgcn_ubfe(u ? st1 : st0, 8 * cls, 8) +
+                              (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
               ilist[wave][idx] = ent[u];
             }
-          const int my_n = grp == 0 ? ncl[0] : grp == 1 ? ncl[1] : grp == 2 ? ncl[2] : ncl[3];
-          const int my_base = grp == 0 ? cb[0] : grp == 1 ? cb[1] : grp == 2 ? cb[2] : cb[3];
+          const int my_n = (int)__builtin_amdgcn_ubfe(szs, 8 * grp, 8);
+          const int my_base = (int)__builtin_amdgcn_ubfe(st0, 8 * grp, 8);
           // software pipeline: while batch j updates the window, the weight
           // and gs slice of batch j + 1 and the list entry of batch j + 2 are
           // in flight
