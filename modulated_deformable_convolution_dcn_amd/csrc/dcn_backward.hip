@@ -163,7 +163,9 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   __shared__ int ilist[NW][2 * TILE];  // per wave: scatter items of one corner pair
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mr = wave & 3, mh = wave >> 2;  // MFMA: pixel rows 16 mr .., channels 32 mh ..
+  // MFMA: wave -> pixel rows 32 mr .. 32 mr + 31, channels 16 mh .. 16 mh + 15
+  // (one weight fragment per k-step shared by two pixel tiles)
+  const int mr = wave & 1, mh = wave >> 1;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int tile = logical % tiles_per_img, b = logical / tiles_per_img;
   const int ty = tile / tiles_x, tx = tile - (tile / tiles_x) * tiles_x;
@@ -247,16 +249,13 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 
   // corner values of the sum passes x 4 corners, one buffer per table slot
   u32x4 cv[2][NPASS][4];
-  f32x4 bw[WPRE ? NQ : 1][2];
+  f32x4 bw[WPRE ? NQ : 1];
   auto w_load = [&](int kb) {
     if constexpr (WPRE) {
       const float* wt = a.wt + (size_t)kb * OP * 64;
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          bw[q][nt] = *reinterpret_cast<const f32x4*>(
-              &wt[((4 * q + g) * 64 + 16 * (2 * mh + nt) + rl) * 4]);
+        bw[q] = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * mh + rl) * 4]);
     }
   };
 
@@ -304,36 +303,35 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       }
       if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
       // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows
-      // 16 (w % 4) .., channels 32 (w / 4) ..
+      // 32 (w % 2) .., channels 16 (w / 2) ..
       f32x4 acc[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < 2; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const float* wt = a.wt + (size_t)kb * OP * 64;
 #pragma unroll 4
       for (int q = 0; q < NQ; ++q) {
-        const f32x4 af =
-            *reinterpret_cast<const f32x4*>(&Gs[(16 * mr + rl) * GST + 16 * q + 4 * g]);
-        f32x4 bf[2];
+        f32x4 af[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if constexpr (WPRE)
-            bf[nt] = bw[q][nt];
-          else
-            bf[nt] = *reinterpret_cast<const f32x4*>(
-                &wt[((4 * q + g) * 64 + 16 * (2 * mh + nt) + rl) * 4]);
-        }
+        for (int pt = 0; pt < 2; ++pt)
+          af[pt] = *reinterpret_cast<const f32x4*>(
+              &Gs[(32 * mr + 16 * pt + rl) * GST + 16 * q + 4 * g]);
+        f32x4 bf;
+        if constexpr (WPRE)
+          bf = bw[q];
+        else
+          bf = *reinterpret_cast<const f32x4*>(&wt[((4 * q + g) * 64 + 16 * mh + rl) * 4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[nt][e], acc[nt], 0, 0, 0);
+          for (int pt = 0; pt < 2; ++pt)
+            acc[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[pt][e], bf[e], acc[pt], 0, 0, 0);
       }
       // MFMA 16x16 layout: lane l, register r -> row 4(l/16) + r, column l % 16
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gsT[(16 * mr + 4 * g + r) * SST + 16 * (2 * mh + nt) + rl] = acc[nt][r];
+          gsT[(32 * mr + 16 * pt + 4 * g + r) * SST + 16 * mh + rl] = acc[pt][r];
       __syncthreads();  // gsT and tables P ^ 1 visible
 
       // (2) weights and corner loads of tap k + 1, then tap k's sums and scatter
