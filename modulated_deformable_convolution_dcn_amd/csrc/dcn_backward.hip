@@ -108,31 +108,31 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 // g tile, the gs tile, the tables and the scatter lists the kernel uses
 // <= 160 KB of LDS).
 constexpr int bwd_window_floats(int OP) {
-  return OP <= 16 ? 31744 : OP <= 64 ? 28672 : OP <= 128 ? 24576 : 15872;
+  return OP <= 16 ? 31552 : OP <= 64 ? 28480 : OP <= 128 ? 24384 : 15872;
 }
 constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 
 // One workgroup = an 8 x 8 block of output pixels of one image.  Its
 // sampling points cluster around the block, so the input gradient of the
 // window [wy0, wy0 + WH) x [wx0, wx0 + WW) (the block's footprint grown by R
-// on every side) is accumulated in LDS with LDS atomics and flushed to
-// memory once per 64-channel chunk; corners outside the window (far
-// offsets) go straight to memory.  R < 0: no window.
+// on every side) is accumulated in LDS and flushed to memory once per
+// 64-channel chunk; corners outside the window (far offsets) go straight to
+// memory with atomics.  R < 0: no window.
 //
 // Per 64-channel chunk the taps run as a two-stage pipeline, one barrier
-// pair per tap: while the MFMAs form gs of tap k, wave 0 turns the offsets of
-// tap k + 1 (loaded a tap earlier) into the sampling tables; after the
-// barrier every thread issues the corner loads of tap k + 1 (and, for up to
-// 64 outputs, the weight fragments of tap k + 1) before it works on tap k
-// with the corners loaded one tap earlier.
+// pair per tap: the MFMAs form gs = g W^T of tap k; after the second barrier
+// every thread issues the corner loads of tap k + 1 (and, for up to 64
+// outputs, its weight fragments) before it works on tap k with the corners
+// loaded one tap earlier.  The sampling tables of tap k sit in slot k % 3:
+// wave 0 builds those of tap k + 2 after its own scatter of tap k, in the
+// time the other waves' scatter leaves it before the next barrier.
 //
 // Tap k's work has two layouts.  The mask / offset sums need the corner
 // values: 16 lanes per pixel, 4 channels each (one 16-byte load per corner),
-// reduced over the 16 lanes.  The input-gradient scatter needs none: one
-// pixel per wave-step, lane = channel, so each LDS atomic instruction covers
-// one window position's 64 consecutive channels (no bank conflicts; a far
-// corner is one coalesced 256-byte atomic run).  The sums of tap k are
-// staged in LDS and written by one wave at the next tap.
+// reduced over the 16 lanes and staged in LDS for one wave to write at the
+// next tap.  The input-gradient scatter needs none: each window position
+// belongs to one wave, which adds 16 lanes x 4 channels per item with plain
+// LDS read-add-writes (see step (2b)).
 template <int OP>  // padded output channels: 16, 64, 128 or 256
 __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int tiles_x,
                                                        int tiles_per_img) {
@@ -154,11 +154,10 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   //   Sf {mask x corner weight, 0 for an invalid corner}
   // corner flags: bit q = in the window, bit 4 + q = valid but outside it,
   // bits 8-9 = window row of corner (0,0) mod 4
-  __shared__ int4 Ti[2][TILE];
-  __shared__ f32x4 Tf[2][TILE];
-  __shared__ int4 Si[2][TILE];
-  __shared__ f32x4 Sf[2][TILE];
-  const float* const Sfl = reinterpret_cast<const float*>(&Sf[0][0]);  // [2][TILE][4]
+  __shared__ f32x4 Tf[3][TILE];
+  __shared__ int4 Si[3][TILE];
+  __shared__ f32x4 Sf[3][TILE];
+  const float* const Sfl = reinterpret_cast<const float*>(&Sf[0][0]);  // [3][TILE][4]
   __shared__ float red[2][3][TILE];  // mask, dy, dx sums of a tap
   __shared__ int ilist[NW][2 * TILE];  // per wave: scatter items of one corner pair
 
@@ -217,8 +216,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
     // corner (0,0)'s byte offset; the other corners are a uniform step away
     // (used only for valid corners, whose offsets are exact and in range)
     const uint32_t b00 = (uint32_t)((b * a.H + y0) * a.W + x0) * ((uint32_t)a.C * 4u);
-    Ti[slot][tid] = make_int4(y0, x0, (int)v4, (int)b00);
-    Tf[slot][tid] = f32x4{tp.p.ly, tp.p.lx, n_m, 0.0f};
+    Tf[slot][tid] = f32x4{tp.p.ly, tp.p.lx, n_m, __int_as_float((int)v4)};
     const float hy = 1.0f - tp.p.ly, hx = 1.0f - tp.p.lx;
     const float wv[4] = {hy * hx, hy * tp.p.lx, tp.p.ly * hx, tp.p.ly * tp.p.lx};
     f32x4 cf;
@@ -231,9 +229,10 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       const bool inwin = use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW;
       if (ok) flags |= inwin ? (1 << q) : (16 << q);
     }
-    flags |= ((y0 - wy0) & 3) << 8;  // window row mod 4 (scatter classes)
+    flags |= ((y0 - wy0) & 3) << 8;                    // window row mod 4 (scatter classes)
+    flags |= (((y0 - wy0) + (x0 - wx0)) & (NW - 1)) << 10;  // owner wave of corner (0,0)
     Si[slot][tid] = make_int4(((y0 - wy0) * WW + (x0 - wx0)) * WSTR, flags,
-                              (b * a.H + y0) * a.W + x0, (y0 - wy0) + (x0 - wx0));
+                              (b * a.H + y0) * a.W + x0, (int)b00);
     Sf[slot][tid] = cf;
   };
   // wave 1: the mask / offset gradients of tap k from the staged sums
@@ -268,39 +267,44 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
     const int ch = chunk * 64 + 4 * sl;
     const bool chan_ok = ch < a.C;            // sum layout
 
-    auto c_issue = [&](auto SLOT) {  // corner loads of the tap in table SLOT
-      constexpr int S = decltype(SLOT)::value;
+    // corner loads of the tap in table slot ts into register buffer BUF
+    auto c_issue = [&](auto BUF, int ts) {
+      constexpr int S = decltype(BUF)::value;
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
-        const int4 ti = Ti[S][(NT / 16) * p + (tid >> 4)];
-        const uint32_t base = (uint32_t)ti.w + (uint32_t)ch * 4u;
+        const int4 si = Si[ts][(NT / 16) * p + (tid >> 4)];
+        const uint32_t base = (uint32_t)si.w + (uint32_t)ch * 4u;
+        const int v4 = si.y | (si.y >> 4);  // in the window or not
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const bool ok = chan_ok && ((ti.z >> q) & 1);
+          const bool ok = chan_ok && ((v4 >> q) & 1);
           cv[S][p][q] = load16(xr, ok ? base + corner_step[q] : kNoCorner);
         }
       }
     };
 
-    // prologue: tables and corners of tap 0, offsets of tap 1, weights of tap 0
+    // prologue: tables of taps 0 and 1, offsets of tap 2, corners and
+    // weights of tap 0.  Tap k's tables live in slot k % 3; wave 0 builds
+    // those of tap k + 2 after its own scatter of tap k.
     if (tid < TILE) {
       t_load(0);
       t_build(0, 0);
-      t_load(a.K > 1 ? 1 : 0);
+      if (a.K > 1) {
+        t_load(1);
+        t_build(1, 1);
+      }
+      t_load(a.K > 2 ? 2 : 0);
     }
-    __syncthreads();  // tables of tap 0 visible; window zeroed
-    c_issue(std::integral_constant<int, 0>{});
+    __syncthreads();  // tables of taps 0, 1 visible; window zeroed
+    c_issue(std::integral_constant<int, 0>{}, 0);
     w_load(chunk);
 
-    auto step = [&](int k, auto PAR) {
-      constexpr int P = decltype(PAR)::value;  // k & 1: tables / corner buffer of tap k
+    auto step = [&](int k, int ts, auto PAR) {
+      constexpr int P = decltype(PAR)::value;  // k & 1: corner buffer and sums of tap k
+      const int ts1 = ts == 2 ? 0 : ts + 1, ts2 = ts1 == 2 ? 0 : ts1 + 1;  // slots of k + 1, k + 2
       const int kb = k * a.nchunk + chunk;
       const bool more = k + 1 < a.K;
-      __syncthreads();  // step k-1 is done with gsT, tables P ^ 1 and its sums
-      if (wave == 0 && more) {  // (0) tables of tap k + 1, then the offsets of tap k + 2
-        t_build(P ^ 1, k + 1);
-        t_load(k + 2 < a.K ? k + 2 : 0);
-      }
+      __syncthreads();  // step k-1 is done with gsT and its sums
       if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
       // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows
       // 32 (w % 2) .., channels 16 (w / 2) ..
@@ -332,21 +336,20 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           gsT[(32 * mr + 16 * pt + 4 * g + r) * SST + 16 * mh + rl] = acc[pt][r];
-      __syncthreads();  // gsT and tables P ^ 1 visible
+      __syncthreads();  // gsT visible
 
       // (2) weights and corner loads of tap k + 1, then tap k's sums and scatter
       if (more) {
         w_load(kb + a.nchunk);
-        c_issue(std::integral_constant<int, P ^ 1>{});
+        c_issue(std::integral_constant<int, P ^ 1>{}, ts1);
       }
       // (2a) sums: pass p -> pixel (NT / 16) p + tid / 16, 4 channels per lane
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
         const int px = (NT / 16) * p + (tid >> 4);
-        const int4 ti = Ti[P][px];
-        const f32x4 tf = Tf[P][px];
+        const f32x4 tf = Tf[ts][px];
         float sm = 0.f, sdy = 0.f, sdx = 0.f;
-        if (ti.z != 0 && chan_ok) {
+        if (__float_as_int(tf[3]) != 0 && chan_ok) {  // any valid corner
           const float ly = tf[0], lx = tf[1], hy = 1.0f - ly, hx = 1.0f - lx;
           const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
           const float vy[4] = {-hx, -lx, hx, lx};
@@ -385,10 +388,11 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       // (0,1) and corners (1,0), (1,1): each pair's positions share a window
       // row.  Far corners of the wave's 8 pixels go to memory with atomics.
       if (want_gx) {
-        const int4 si = Si[P][lane];  // lane = pixel
-        const f32x4 sf = Sf[P][lane];
+        const int4 si = Si[ts][lane];  // lane = pixel
+        const f32x4 sf = Sf[ts][lane];
         const int grp = lane >> 4, sub = lane & 15;
-        const int row0 = si.y >> 8;  // window row of corner (0,0), mod 4
+        const int row0 = (si.y >> 8) & 3;  // window row of corner (0,0), mod 4
+        const int own0 = (si.y >> 10) & (NW - 1);  // owner wave of corner (0,0)
         static_for<2>([&](auto H) {
           constexpr int h = decltype(H)::value;  // corners 2h, 2h + 1: one window row
           bool own[2];
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
               if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
                 atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
             }
-            own[u] = ((si.y >> q) & 1) && ((si.w + dq) & (NW - 1)) == wave;
+            own[u] = ((si.y >> q) & 1) && ((own0 + dq) & (NW - 1)) == wave;
             // list entry: window position index, then pixel and corner (the
             // corner weight is read back from the table)
             ent[u] = (((si.x >> 6) + h * WW + u) << 8) | (lane << 2) | q;
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           auto fetch = [&](int j, int it) {
             const bool valid = j < my_n;
             pos = valid ? (it >> 8) * WSTR : SINK;
-            const float cw = Sfl[P * TILE * 4 + (it & 255)];
+            const float cw = Sfl[ts * TILE * 4 + (it & 255)];
             c = valid ? cw : 0.0f;
             g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 2) & 63) * SST + 4 * sub]);
           };
@@ -483,13 +487,22 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           }
         });
       }
+      // (2c) wave 0, in the time the other waves' scatter leaves it: tables of
+      // tap k + 2 into the slot of tap k - 1 (unused since this step's first
+      // barrier), then the offsets of tap k + 3
+      if (wave == 0 && k + 2 < a.K) {
+        t_build(ts2, k + 2);
+        t_load(k + 3 < a.K ? k + 3 : 0);
+      }
     };
-    int k = 0;
+    int k = 0, ts = 0;
     for (; k + 1 < a.K; k += 2) {
-      step(k, std::integral_constant<int, 0>{});
-      step(k + 1, std::integral_constant<int, 1>{});
+      step(k, ts, std::integral_constant<int, 0>{});
+      ts = ts == 2 ? 0 : ts + 1;
+      step(k + 1, ts, std::integral_constant<int, 1>{});
+      ts = ts == 2 ? 0 : ts + 1;
     }
-    if (k < a.K) step(k, std::integral_constant<int, 0>{});
+    if (k < a.K) step(k, ts, std::integral_constant<int, 0>{});
 
     // (3) the last tap's sums, then flush the window's input gradient of this chunk
     __syncthreads();
