@@ -148,12 +148,14 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   // the window, then 64 floats that take the scatter's discarded adds
   constexpr int SINK = bwd_window_floats(OP);
   __shared__ __attribute__((aligned(16))) float win[SINK + 64];
-  // two sets of tables of the block's 64 sampling points (written by wave 0):
-  //   Ti {y0, x0, validity bits, byte offset of corner (0,0) in x}, Tf {ly, lx, mask}
-  //   Si {window offset of corner (0,0), corner flags, image pixel of (0,0)},
+  // three sets of tables of the block's 64 sampling points (written by wave 0):
+  //   Tf {ly, lx, mask, validity bits as an int}
+  //   Si {window offset of corner (0,0), corner flags, image pixel of (0,0),
+  //       byte offset of corner (0,0) in x}
   //   Sf {mask x corner weight, 0 for an invalid corner}
   // corner flags: bit q = in the window, bit 4 + q = valid but outside it,
-  // bits 8-9 = window row of corner (0,0) mod 4
+  // bits 8-9 = window column of corner (0,0) mod 4, bits 10-12 = its window
+  // row mod 8
   __shared__ f32x4 Tf[3][TILE];
   __shared__ int4 Si[3][TILE];
   __shared__ f32x4 Sf[3][TILE];
@@ -229,8 +231,8 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       const bool inwin = use_win && wy >= 0 && wy < WH && wx >= 0 && wx < WW;
       if (ok) flags |= inwin ? (1 << q) : (16 << q);
     }
-    flags |= ((y0 - wy0) & 3) << 8;                    // window row mod 4 (scatter classes)
-    flags |= (((y0 - wy0) + (x0 - wx0)) & (NW - 1)) << 10;  // owner wave of corner (0,0)
+    flags |= ((x0 - wx0) & 3) << 8;          // window column mod 4 (scatter classes)
+    flags |= ((y0 - wy0) & (NW - 1)) << 10;  // window row mod 8 (owner wave of the row)
     Si[slot][tid] = make_int4(((y0 - wy0) * WW + (x0 - wx0)) * WSTR, flags,
                               (b * a.H + y0) * a.W + x0, (int)b00);
     Sf[slot][tid] = cf;
@@ -376,116 +378,122 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           red[P][2][px] = tf[2] * sdx;
         }
       }
-      // (2b) scatter.  Window position (wy, wx) belongs to wave (wy + wx) mod
-      // 8, so no two waves ever update one position and the updates are plain
-      // LDS read-add-writes (float atomics cost far more).  Per corner pair
-      // the wave lists its positions (position, pixel, corner) in LDS, grouped
-      // by window row mod 4, and takes one of each group at a time: 16
-      // lanes per item, 4 channels per lane, one 16-byte read, 4 FMAs and one
-      // 16-byte write per lane.  Equal positions fall in one group, so a batch
-      // never names a position twice, and the next batch's reads follow this
-      // batch's writes in the wave's LDS order.  The pairs are corners (0,0),
-      // (0,1) and corners (1,0), (1,1): each pair's positions share a window
-      // row.  Far corners of the wave's 8 pixels go to memory with atomics.
+      // (2b) scatter.  Window row wy belongs to wave wy mod 8, so no two waves
+      // ever update one position and the updates are plain LDS read-add-writes
+      // (float atomics cost far more).  An item is one pixel's corner pair
+      // (h, 0), (h, 1): two neighbouring positions of one row, so one owner.
+      // The wave lists its items (position, in-window bits, pixel, pair) in
+      // LDS, grouped by window column mod 4, and takes one of each group at a
+      // time: 16 lanes per item, 4 channels per lane; the gs slice is read
+      // once, then position (h, 0) and position (h, 1) each get one 16-byte
+      // read, 4 FMAs and one 16-byte write per lane, in that order.  Equal
+      // pairs fall in one group, so a batch never names a position twice in
+      // one of its two updates, and a pair's second position met as another
+      // group's first is updated after it.  Far corners of the wave's 8
+      // pixels go to memory with atomics.
       if (want_gx) {
         const int4 si = Si[ts][lane];  // lane = pixel
         const f32x4 sf = Sf[ts][lane];
         const int grp = lane >> 4, sub = lane & 15;
-        const int row0 = (si.y >> 8) & 3;  // window row of corner (0,0), mod 4
-        const int own0 = (si.y >> 10) & (NW - 1);  // owner wave of corner (0,0)
-        static_for<2>([&](auto H) {
-          constexpr int h = decltype(H)::value;  // corners 2h, 2h + 1: one window row
-          bool own[2];
-          int ent[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int q = 2 * h + u, dq = h + u;
-            // the corner weight as a scalar first: taking the bits of a vector
-            // element directly reads element 0 with this compiler
-            const float sfq = sf[q];
-            const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 3) == wave;
-            uint64_t m_far = __ballot(far);
-            while (m_far) {
-              const int p = __builtin_ctzll(m_far);
-              m_far &= m_far - 1;
-              const int pix = __builtin_amdgcn_readlane(si.z, p) + h * a.W + u;
-              const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
-              if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
-                atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
-            }
-            own[u] = ((si.y >> q) & 1) && ((own0 + dq) & (NW - 1)) == wave;
-            // list entry: window position index, then pixel and corner (the
-            // corner weight is read back from the table)
-            ent[u] = (((si.x >> 6) + h * WW + u) << 8) | (lane << 2) | q;
-          }
-          // position classes (window row mod 4): a class's items are listed
-          // together, and batch j takes the j-th item of each class (lane
-          // group g <- class g), so no two items of a batch name one position
-          const int cls = (row0 + h) & 3;
-          // wave-uniform: class bits and owners as masks; per class and
-          // corner the bucket sizes, packed one byte per class (every count
-          // is at most 128): bucket starts of corner 0 and corner 1 items,
-          // class sizes
-          const uint64_t X = __ballot(cls & 1), Y = __ballot(cls & 2);
-          const uint64_t O0 = __ballot(own[0]), O1 = __ballot(own[1]);
-          uint32_t st0 = 0, st1 = 0, szs = 0;
-          int nb = 0;
-          {
-            int acc = 0;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const uint64_t cm = ((g & 1) ? X : ~X) & ((g & 2) ? Y : ~Y);
-              const int n0 = __builtin_popcountll(O0 & cm), n1 = __builtin_popcountll(O1 & cm);
-              st0 |= (uint32_t)acc << (8 * g);
-              st1 |= (uint32_t)(acc + n0) << (8 * g);
-              szs |= (uint32_t)(n0 + n1) << (8 * g);
-              acc += n0 + n1;
-              nb = max(nb, n0 + n1);
-            }
-          }
-          // lanes of another class than this lane's
-          const uint64_t other = (X ^ ((cls & 1) ? ~0ull : 0ull)) | (Y ^ ((cls & 2) ? ~0ull : 0ull));
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            if (own[u]) {
-              const uint64_t mm = (u ? O1 : O0) & ~other;
-              const int idx = (int)__builtin_amdgcn_ubfe(u ? st1 : st0, 8 * cls, 8) +
-                              (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
-              ilist[wave][idx] = ent[u];
-            }
-          const int my_n = (int)__builtin_amdgcn_ubfe(szs, 8 * grp, 8);
-          const int my_base = (int)__builtin_amdgcn_ubfe(st0, 8 * grp, 8);
-          // software pipeline: while batch j updates the window, the weight
-          // and gs slice of batch j + 1 and the list entry of batch j + 2 are
-          // in flight
-          auto entry = [&](int j) { return ilist[wave][j < my_n ? my_base + j : 0]; };
-          int e_next = entry(1), pos;
-          float c;
-          f32x4 g4;
-          auto fetch = [&](int j, int it) {
-            const bool valid = j < my_n;
-            pos = valid ? (it >> 8) * WSTR : SINK;
-            const float cw = Sfl[ts * TILE * 4 + (it & 255)];
-            c = valid ? cw : 0.0f;
-            g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 2) & 63) * SST + 4 * sub]);
-          };
-          fetch(0, entry(0));
-          for (int j = 0; j < nb; ++j) {
-            float* dst = &win[pos + 4 * sub];
-            f32x4 w4 = *reinterpret_cast<const f32x4*>(dst);
-            const float cj = c;
-            const f32x4 gj = g4;
-            {  // the last batch fetches entry 0 and the sink: harmless
-              const int e = e_next;
-              e_next = entry(j + 2);
-              fetch(j + 1, e);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(gj[e], cj, w4[e]);
-            *reinterpret_cast<f32x4*>(dst) = w4;
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          // the corner weight as a scalar first: taking the bits of a vector
+          // element directly reads element 0 with this compiler
+          const float sfq = sf[q];
+          const bool far = ((si.y >> (4 + q)) & 1) && (lane >> 3) == wave;
+          uint64_t m_far = __ballot(far);
+          while (m_far) {
+            const int p = __builtin_ctzll(m_far);
+            m_far &= m_far - 1;
+            const int pix = __builtin_amdgcn_readlane(si.z, p) + (q >> 1) * a.W + (q & 1);
+            const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
+            if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
+              atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
           }
         });
+        // position classes (window column mod 4): a class's items are listed
+        // together, and batch j takes the j-th item of each class (lane
+        // group g <- class g)
+        const int cls = (si.y >> 8) & 3;
+        const int row8 = (si.y >> 10) & (NW - 1);
+        bool own[2];
+        int ent[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int inw = (si.y >> (2 * h)) & 3;  // corners (h, 0), (h, 1) in the window
+          own[h] = inw != 0 && ((row8 + h) & (NW - 1)) == wave;
+          // list entry: window position index of (h, 0), in-window bits,
+          // pixel, pair (the corner weights are read back from the table)
+          ent[h] = (((si.x >> 6) + h * WW) << 9) | (inw << 7) | (lane << 1) | h;
+        }
+        // wave-uniform: class bits and owners as masks; per class and pair
+        // the bucket sizes, packed one byte per class (every count is at most
+        // 128): bucket starts of pair 0 and pair 1 items, class sizes
+        const uint64_t X = __ballot(cls & 1), Y = __ballot(cls & 2);
+        const uint64_t O0 = __ballot(own[0]), O1 = __ballot(own[1]);
+        uint32_t st0 = 0, st1 = 0, szs = 0;
+        int nb = 0;
+        {
+          int acc = 0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint64_t cm = ((g & 1) ? X : ~X) & ((g & 2) ? Y : ~Y);
+            const int n0 = __builtin_popcountll(O0 & cm), n1 = __builtin_popcountll(O1 & cm);
+            st0 |= (uint32_t)acc << (8 * g);
+            st1 |= (uint32_t)(acc + n0) << (8 * g);
+            szs |= (uint32_t)(n0 + n1) << (8 * g);
+            acc += n0 + n1;
+            nb = max(nb, n0 + n1);
+          }
+        }
+        // lanes of another class than this lane's
+        const uint64_t other = (X ^ ((cls & 1) ? ~0ull : 0ull)) | (Y ^ ((cls & 2) ? ~0ull : 0ull));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (own[h]) {
+            const uint64_t mm = (h ? O1 : O0) & ~other;
+            const int idx = (int)__builtin_amdgcn_ubfe(h ? st1 : st0, 8 * cls, 8) +
+                            (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+            ilist[wave][idx] = ent[h];
+          }
+        const int my_n = (int)__builtin_amdgcn_ubfe(szs, 8 * grp, 8);
+        const int my_base = (int)__builtin_amdgcn_ubfe(st0, 8 * grp, 8);
+        // software pipeline: while batch j updates the window, the weights
+        // and gs slice of batch j + 1 and the list entry of batch j + 2 are
+        // in flight
+        auto entry = [&](int j) { return ilist[wave][j < my_n ? my_base + j : 0]; };
+        int e_next = entry(1), pa, pb;
+        float2 c;
+        f32x4 g4;
+        auto fetch = [&](int j, int it) {
+          const bool valid = j < my_n;
+          const int p0 = (it >> 9) * WSTR;
+          pa = valid && ((it >> 7) & 1) ? p0 : SINK;
+          pb = valid && ((it >> 8) & 1) ? p0 + WSTR : SINK;
+          c = *reinterpret_cast<const float2*>(&Sfl[ts * TILE * 4 + ((it & 127) << 1)]);
+          g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 1) & 63) * SST + 4 * sub]);
+        };
+        fetch(0, entry(0));
+        for (int j = 0; j < nb; ++j) {
+          float* da = &win[pa + 4 * sub];
+          float* db = &win[pb + 4 * sub];
+          f32x4 w4 = *reinterpret_cast<const f32x4*>(da);
+          const float2 cj = c;
+          const f32x4 gj = g4;
+          {  // the last batch fetches entry 0 and the sink: harmless
+            const int e = e_next;
+            e_next = entry(j + 2);
+            fetch(j + 1, e);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = __builtin_fmaf(gj[e], cj.x, w4[e]);
+          *reinterpret_cast<f32x4*>(da) = w4;
+          f32x4 v4 = *reinterpret_cast<const f32x4*>(db);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = __builtin_fmaf(gj[e], cj.y, v4[e]);
+          *reinterpret_cast<f32x4*>(db) = v4;
+        }
       }
       // (2c) wave 0, in the time the other waves' scatter leaves it: tables of
       // tap k + 2 into the slot of tap k - 1 (unused since this step's first
