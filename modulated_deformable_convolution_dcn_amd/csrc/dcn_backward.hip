@@ -108,7 +108,7 @@ __device__ __forceinline__ float gout_at(const BwdArgs& a, int b, int o, int hw)
 // g tile, the gs tile, the tables and the scatter lists the kernel uses
 // <= 160 KB of LDS).
 constexpr int bwd_window_floats(int OP) {
-  return OP <= 16 ? 31552 : OP <= 64 ? 28480 : OP <= 128 ? 24384 : 15872;
+  return OP <= 64 ? 28480 : OP <= 128 ? 24384 : 15872;
 }
 constexpr int WSTR = 64;  // floats per window position: the chunk's 64 channels
 
@@ -143,8 +143,12 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   constexpr int NT = 64 * NW;        // threads
   constexpr int NPASS = TILE * 16 / NT;  // sum passes (16 lanes per pixel)
   constexpr int NQ = OP / 16;
-  __shared__ __attribute__((aligned(16))) float Gs[TILE * GST];
-  __shared__ __attribute__((aligned(16))) float gsT[TILE * SST];
+  // up to 64 outputs the g^T fragments stay in registers and the gs tile has
+  // two buffers: one barrier per tap, and a wave done with its scatter of
+  // tap k goes on to the MFMAs of tap k + 1 while others still scatter
+  constexpr bool ONEBAR = OP <= 64;
+  __shared__ __attribute__((aligned(16))) float Gs[ONEBAR ? 4 : TILE * GST];
+  __shared__ __attribute__((aligned(16))) float gsT[(ONEBAR ? 2 : 1) * TILE * SST];
   // the window, then 64 floats that take the scatter's discarded adds
   constexpr int SINK = bwd_window_floats(OP);
   __shared__ __attribute__((aligned(16))) float win[SINK + 64];
@@ -184,15 +188,34 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
   };
 
   // g tile [64 pixels][OP outputs], zero outside
-  for (int e = tid; e < TILE * OP; e += NT) {
-    const int o = e / TILE, px = e % TILE;
-    int hw;
-    const bool in = px_hw(px, hw);
-    Gs[px * GST + o] = (o < a.O && in) ? gout_at(a, b, o, hw) : 0.0f;
+  if constexpr (!ONEBAR) {
+    for (int e = tid; e < TILE * OP; e += NT) {
+      const int o = e / TILE, px = e % TILE;
+      int hw;
+      const bool in = px_hw(px, hw);
+      Gs[px * GST + o] = (o < a.O && in) ? gout_at(a, b, o, hw) : 0.0f;
+    }
   }
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const int rl = lane & 15, g = lane >> 4;
+  // the same g values as MFMA A fragments of this wave's two pixel tiles:
+  // ga[q][pt][e] = g[pixel 32 mr + 16 pt + rl][output 16 q + 4 g + e]
+  f32x4 ga[ONEBAR ? NQ : 1][2];
+  if constexpr (ONEBAR) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      int hw;
+      const bool in = px_hw(32 * mr + 16 * pt + rl, hw);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int o = 16 * q + 4 * g + e;
+          ga[q][pt][e] = (in && o < a.O) ? gout_at(a, b, o, hw) : 0.0f;
+        }
+    }
+  }
   const int sl = tid & 15;  // 4-channel slice of the 64-channel chunk (sum layout)
   const int nwin = use_win ? WH * WW : 0;
 
@@ -301,15 +324,9 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
     c_issue(std::integral_constant<int, 0>{}, 0);
     w_load(chunk);
 
-    auto step = [&](int k, int ts, auto PAR) {
-      constexpr int P = decltype(PAR)::value;  // k & 1: corner buffer and sums of tap k
-      const int ts1 = ts == 2 ? 0 : ts + 1, ts2 = ts1 == 2 ? 0 : ts1 + 1;  // slots of k + 1, k + 2
-      const int kb = k * a.nchunk + chunk;
-      const bool more = k + 1 < a.K;
-      __syncthreads();  // step k-1 is done with gsT and its sums
-      if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
-      // (1) gs[px, c] = sum_o g[px, o] W[o, c, k]: wave w -> pixel rows
-      // 32 (w % 2) .., channels 16 (w / 2) ..
+    // (1) gs[px, c] = sum_o g[px, o] W[o, c, tap] into tile gt: wave w ->
+    // pixel rows 32 (w % 2) .., channels 16 (w / 2) ..
+    auto mfma_tap = [&](int kb, float* gt) {
       f32x4 acc[2];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -318,9 +335,13 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       for (int q = 0; q < NQ; ++q) {
         f32x4 af[2];
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-          af[pt] = *reinterpret_cast<const f32x4*>(
-              &Gs[(32 * mr + 16 * pt + rl) * GST + 16 * q + 4 * g]);
+        for (int pt = 0; pt < 2; ++pt) {
+          if constexpr (ONEBAR)
+            af[pt] = ga[q][pt];
+          else
+            af[pt] = *reinterpret_cast<const f32x4*>(
+                &Gs[(32 * mr + 16 * pt + rl) * GST + 16 * q + 4 * g]);
+        }
         f32x4 bf;
         if constexpr (WPRE)
           bf = bw[q];
@@ -337,8 +358,25 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gsT[(32 * mr + 16 * pt + 4 * g + r) * SST + 16 * mh + rl] = acc[pt][r];
-      __syncthreads();  // gsT visible
+          gt[(32 * mr + 16 * pt + 4 * g + r) * SST + 16 * mh + rl] = acc[pt][r];
+    };
+    if constexpr (ONEBAR) mfma_tap(chunk, gsT);  // tap 0 into buffer 0
+
+    auto step = [&](int k, int ts, auto PAR) {
+      constexpr int P = decltype(PAR)::value;  // k & 1: corner buffer and sums of tap k
+      const int ts1 = ts == 2 ? 0 : ts + 1, ts2 = ts1 == 2 ? 0 : ts1 + 1;  // slots of k + 1, k + 2
+      const int kb = k * a.nchunk + chunk;
+      const bool more = k + 1 < a.K;
+      float* const gt = gsT + (ONEBAR ? P * TILE * SST : 0);  // gs tile of tap k
+      // two barriers: step k-1 is done with the gs tile and its sums, then
+      // the MFMAs of tap k; one barrier: the MFMAs of tap k were the end of
+      // every wave's step k-1
+      __syncthreads();
+      if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
+      if constexpr (!ONEBAR) {
+        mfma_tap(kb, gt);
+        __syncthreads();  // gs tile visible
+      }
 
       // (2) weights and corner loads of tap k + 1, then tap k's sums and scatter
       if (more) {
@@ -356,7 +394,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           const float wv[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
           const float vy[4] = {-hx, -lx, hx, lx};
           const float vx[4] = {-hy, hy, -ly, ly};
-          const f32x4 gs = *reinterpret_cast<const f32x4*>(&gsT[px * SST + 4 * sl]);
+          const f32x4 gs = *reinterpret_cast<const f32x4*>(&gt[px * SST + 4 * sl]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {  // an outside corner was loaded as zeros: no terms
             const f32x4 v = __builtin_bit_cast(f32x4, cv[P][p][q]);
@@ -408,7 +446,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
             const int pix = __builtin_amdgcn_readlane(si.z, p) + (q >> 1) * a.W + (q & 1);
             const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sfq), p));
             if (chunk * 64 + lane < a.C)  // lanes past C would reach the next pixel
-              atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gsT[p * SST + lane] * c);
+              atomic_add(a.gx + (size_t)pix * a.C + chunk * 64 + lane, gt[p * SST + lane] * c);
           }
         });
         // position classes (window column mod 4): a class's items are listed
@@ -472,7 +510,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
           pa = valid && ((it >> 7) & 1) ? p0 : SINK;
           pb = valid && ((it >> 8) & 1) ? p0 + WSTR : SINK;
           c = *reinterpret_cast<const float2*>(&Sfl[ts * TILE * 4 + ((it & 127) << 1)]);
-          g4 = *reinterpret_cast<const f32x4*>(&gsT[((it >> 1) & 63) * SST + 4 * sub]);
+          g4 = *reinterpret_cast<const f32x4*>(&gt[((it >> 1) & 63) * SST + 4 * sub]);
         };
         fetch(0, entry(0));
         for (int j = 0; j < nb; ++j) {
@@ -502,6 +540,11 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
         t_build(ts2, k + 2);
         t_load(k + 3 < a.K ? k + 3 : 0);
       }
+      // (2d) one barrier per tap: the MFMAs of tap k + 1 into the other gs
+      // buffer (last read in step k - 1, which every wave had finished before
+      // this step's barrier)
+      if constexpr (ONEBAR)
+        if (more) mfma_tap(kb + a.nchunk, gsT + (P ^ 1) * TILE * SST);
     };
     int k = 0, ts = 0;
     for (; k + 1 < a.K; k += 2) {
