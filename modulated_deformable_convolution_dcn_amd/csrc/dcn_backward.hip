@@ -260,14 +260,20 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
                               (b * a.H + y0) * a.W + x0, (int)b00);
     Sf[slot][tid] = cf;
   };
-  // wave 1: the mask / offset gradients of tap k from the staged sums
-  auto sums_store = [&](int slot, int k) {
+  // wave 1: the mask / offset gradients of tap k from the staged sums.  Every
+  // (pixel, tap) element belongs to this workgroup alone, so the first chunk
+  // stores it (the outputs need no zero fill) and later chunks add to it.
+  auto sums_store = [&](int slot, int k, bool first) {
     int hw;
     if (!px_hw(lane, hw)) return;
-    if (a.gmask) atomic_add(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, red[slot][0][lane]);
+    auto put = [&](float* d, float v) {
+      if (first) *d = v;
+      else atomic_add(d, v);
+    };
+    if (a.gmask) put(a.gmask + (size_t)(b * a.K + k) * a.HoWo + hw, red[slot][0][lane]);
     if (a.goff) {
-      atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, red[slot][1][lane]);
-      atomic_add(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, red[slot][2][lane]);
+      put(a.goff + (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hw, red[slot][1][lane]);
+      put(a.goff + (size_t)(b * 2 * a.K + 2 * k + 1) * a.HoWo + hw, red[slot][2][lane]);
     }
   };
 
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
       // the MFMAs of tap k; one barrier: the MFMAs of tap k were the end of
       // every wave's step k-1
       __syncthreads();
-      if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1);
+      if (wave == 1 && k > 0) sums_store(P ^ 1, k - 1, chunk == 0);
       if constexpr (!ONEBAR) {
         mfma_tap(kb, gt);
         __syncthreads();  // gs tile visible
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 
     // (3) the last tap's sums, then flush the window's input gradient of this chunk
     __syncthreads();
-    if (wave == 1) sums_store((a.K - 1) & 1, a.K - 1);
+    if (wave == 1) sums_store((a.K - 1) & 1, a.K - 1, chunk == 0);
     for (int e = tid; e < nwin * 64; e += NT) {
       const int pos = e >> 6, c = e & 63;
       const int y = wy0 + pos / WW, xx = wx0 + pos % WW;
@@ -587,7 +593,15 @@ __global__ __launch_bounds__(512) void bwd_data_kernel(BwdArgs a, int R, int til
 // gradient; element p is pixel 4 q + p).  Tile u's column n is channel
 // 4 n + u of the chunk, which the epilogue undoes.  The four waves' partial
 // sums meet in LDS once per run, then one atomic add per weight element.
-template <int NTO, bool GV>  // 16-output tiles (OP / 16: 1 or 4); GV: NCHW g, Ho*Wo % 4 == 0
+// The loop body has no branches: the next tile's table, corner loads and g
+// fragments are issued unconditionally (past the run's end they read clamped
+// offsets, zeros or in-range data that is never used), so the compiler keeps
+// one register assignment and needs no copies at the loop's joins.
+//   NTO: 16-output tiles (OP / 16: 1 or 4)
+//   GV: NCHW g, Ho*Wo % 4 == 0 and one image of g below 2^31 bytes (16-byte
+//       buffer loads of g^T fragments, two tiles ahead)
+//   FULLC: C % 64 == 0 (every lane's channels exist)
+template <int NTO, bool GV, bool FULLC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img) {
   constexpr int OP = 16 * NTO;
@@ -630,7 +644,8 @@ bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img)
     const size_t ob = (size_t)(b * 2 * a.K + 2 * k) * a.HoWo + hc;
     n_dy = a.offset[ob];
     n_dx = a.offset[ob + a.HoWo];
-    n_m = hw < a.HoWo ? (a.mask ? a.mask[(size_t)(b * a.K + k) * a.HoWo + hc] : 1.0f) : 0.0f;
+    const float mv = a.mask ? a.mask[(size_t)(b * a.K + k) * a.HoWo + hc] : 1.0f;
+    n_m = hw < a.HoWo ? mv : 0.0f;
   };
   auto t_build = [&](int slot, int tile) {
     const int hw = tile * 64 + 16 * wave + tl;
@@ -659,7 +674,7 @@ bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img)
   // ---- corners: pass p -> pixel 4 (lane / 16) + p, channels 4 (lane % 16) ..
   const int sl = lane & 15, pq = lane >> 4;
   const uint32_t cbyte = (uint32_t)(chunk * 64 + 4 * sl) * 4;
-  const bool chan_ok = chunk * 64 + 4 * sl < a.C;
+  const bool chan_ok = FULLC || chunk * 64 + 4 * sl < a.C;
   u32x4 cv[4][4];
   auto c_issue = [&](int slot, int p) {
     const u32x4 o4 = Co[slot * 16 + 4 * pq + p];
@@ -681,24 +696,39 @@ bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img)
 
   // ---- g^T fragments: lane -> output 16t + lane % 16, pixels 4 (lane / 16) ..
   const int rl = lane & 15, g = lane >> 4;
-  f32x4 gf[NTO];  // of the current tile; the next tile's are loaded after its MFMAs
-  auto g_load = [&](int tile) {
-    const int hw = tile * 64 + 16 * wave + 4 * g;
+  // gf[P]: fragments of the tile in slot P, loaded two tiles ahead
+  f32x4 gf[2][NTO];
+  // GV: one image of g through a buffer descriptor; output o's row starts at
+  // byte o * Ho*Wo * 4, and a lane whose output or pixels fall outside reads
+  // zeros (kNoCorner)
+  const __amdgpu_buffer_rsrc_t gr =
+      make_rsrc(a.gout + (size_t)b * a.O * a.HoWo, GV ? (uint32_t)a.O * a.HoWo * 4u : 0u);
+  uint32_t g_row[NTO];
 #pragma unroll
-    for (int t = 0; t < NTO; ++t) {
-      const int o = o0 + 16 * t + rl;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (o < a.O) {
-        if constexpr (GV) {
-          if (hw < a.HoWo)
-            v = *reinterpret_cast<const f32x4*>(a.gout + ((size_t)b * a.O + o) * a.HoWo + hw);
-        } else {
+  for (int t = 0; t < NTO; ++t) {
+    const int o = o0 + 16 * t + rl;
+    g_row[t] = o < a.O ? (uint32_t)o * (uint32_t)a.HoWo * 4u : kNoCorner;
+  }
+  auto g_load = [&](f32x4* dst, int tile) {
+    const int hw = tile * 64 + 16 * wave + 4 * g;
+    if constexpr (GV) {
+      const bool hw_ok = hw < a.HoWo;  // Ho*Wo % 4 == 0: all four pixels or none
+#pragma unroll
+      for (int t = 0; t < NTO; ++t)
+        dst[t] = __builtin_bit_cast(
+            f32x4, load16(gr, hw_ok ? g_row[t] + (uint32_t)hw * 4u : kNoCorner));
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTO; ++t) {
+        const int o = o0 + 16 * t + rl;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (o < a.O) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (hw + e < a.HoWo) v[e] = gout_at(a, b, o, hw + e);
         }
+        dst[t] = v;
       }
-      gf[t] = v;
     }
   };
 
@@ -708,36 +738,40 @@ bwd_weight2_kernel(BwdArgs a, int n_otiles, int tiles_per_run, int runs_per_img)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Tile `tile` (slot P): the table of tile + 1 into the other slot and the
+  // offsets of tile + 2 first, then per pass the blend of this tile, the
+  // corner loads of tile + 1 into the freed registers and the MFMAs; last the
+  // g^T fragments of tile + 2 into this tile's buffer.  Past the run's end
+  // (t_load clamps its pixel) the work is wasted but harmless.
   auto step = [&](int tile, auto PAR) {
     constexpr int P = decltype(PAR)::value;  // slot / buffer of this tile
-    const bool more = tile + 1 < t_end;
-    if (more) {
-      t_build(P ^ 1, tile + 1);
-      t_load(tile + 2 < t_end ? tile + 2 : tile + 1);
-    }
+    t_build(P ^ 1, tile + 1);
+    t_load(tile + 2);
     // dW[o][c] += sum over the wave's 16 pixels: k-step p takes pixels
     // 4 q + p (q = lane / 16) -- the samples of pass p -- and column n of
     // tile u is channel 4 n + u
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const f32x4 sv = blend(P, p);
-      if (more) c_issue(P ^ 1, p);
+      c_issue(P ^ 1, p);
 #pragma unroll
       for (int t = 0; t < NTO; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(gf[t][p], sv[u], acc[t][u], 0, 0, 0);
+          acc[t][u] =
+              __builtin_amdgcn_mfma_f32_16x16x4f32(gf[P][t][p], sv[u], acc[t][u], 0, 0, 0);
     }
-    if (more) g_load(tile + 1);
+    g_load(gf[P], tile + 2);
   };
 
   if (t_begin < t_end) {
     t_load(t_begin);
     t_build(0, t_begin);
-    t_load(t_begin + 1 < t_end ? t_begin + 1 : t_begin);
+    t_load(t_begin + 1);
 #pragma unroll
     for (int p = 0; p < 4; ++p) c_issue(0, p);
-    g_load(t_begin);
+    g_load(gf[0], t_begin);
+    g_load(gf[1], t_begin + 1);
     int tile = t_begin;
     for (; tile + 1 < t_end; tile += 2) {
       step(tile, std::integral_constant<int, 0>{});
@@ -815,20 +849,33 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     p[e] = 0.0f;
 }
 
+// Two small buffers in one launch: [0, n0) of p0, then [0, n1) of p1.
+__global__ __launch_bounds__(256) void fill_zero2_kernel(float* __restrict__ p0, int64_t n0,
+                                                         float* __restrict__ p1, int64_t n1) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n0 + n1;
+       e += (int64_t)gridDim.x * 256) {
+    if (e < n0) p0[e] = 0.0f;
+    else p1[e - n0] = 0.0f;
+  }
+}
+
 // weight [O][C][kh][kw] -> per (tap, 64-channel chunk) block [OP/4][64][4]:
 // element (o, c) at ((o / 4) * 64 + c % 64) * 4 + o % 4, so one 16-byte read
-// gives a lane 4 consecutive outputs of one channel (4 MFMA k-steps).
+// gives a lane 4 consecutive outputs of one channel (4 MFMA k-steps).  One
+// thread per packed element, padding (o >= O or c >= C) written as zero in
+// the same pass.
 __global__ __launch_bounds__(256) void bwd_pack_kernel(const float* __restrict__ w,
                                                        float* __restrict__ wt, int O, int C,
                                                        int K, int OP, int nchunk) {
-  const int64_t total = (int64_t)O * C * K;
-  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < total;
-       s += (int64_t)gridDim.x * 256) {
-    const int tap = (int)(s % K);
-    const int64_t oc = s / K;
-    const int c = (int)(oc % C), o = (int)(oc / C);
-    const int64_t blk = (int64_t)tap * nchunk + c / 64;
-    wt[blk * OP * 64 + ((o / 4) * 64 + c % 64) * 4 + o % 4] = w[s];
+  const int64_t total = (int64_t)K * nchunk * OP * 64;
+  for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < total;
+       d += (int64_t)gridDim.x * 256) {
+    const int64_t blk = d / (OP * 64);
+    const int rem = (int)(d - blk * (OP * 64));
+    const int o = (rem >> 8) * 4 + (rem & 3);
+    const int c = (int)(blk % nchunk) * 64 + ((rem >> 2) & 63);
+    const int tap = (int)(blk / nchunk);
+    wt[d] = (o < O && c < C) ? w[((int64_t)o * C + c) * K + tap] : 0.0f;
   }
 }
 
@@ -886,17 +933,22 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
   BwdArgs a = a0;
   const int OP = bwd_out_pad(a.O);
   hipError_t e;
-  // zero the accumulated outputs and the padded weight blocks
+  // zero the outputs that atomics accumulate into (the offset and mask
+  // gradients are stored by their owning workgroup, the re-packed weight
+  // writes its own padding)
   const int64_t nx = (int64_t)a.B * a.H * a.W * a.C;
   if ((e = zero(a.gx, nx, s)) != hipSuccess) return e;
-  if ((e = zero(a.goff, (int64_t)a.B * 2 * a.K * a.HoWo, s)) != hipSuccess) return e;
-  if ((e = zero(a.gmask, (int64_t)a.B * a.K * a.HoWo, s)) != hipSuccess) return e;
-  if ((e = zero(a.gw, (int64_t)a.O * a.C * a.K, s)) != hipSuccess) return e;
-  if ((e = zero(a.gb, a.O, s)) != hipSuccess) return e;
+  {
+    const int64_t nw = a.gw ? (int64_t)a.O * a.C * a.K : 0, nb = a.gb ? a.O : 0;
+    if (nw + nb > 0) {
+      hipLaunchKernelGGL(fill_zero2_kernel, dim3(grid_of(nw + nb)), dim3(256), 0, s, a.gw, nw,
+                         a.gb, nb);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
   const int64_t nws = bwd_workspace_floats(a.O, a.C, a.K);
-  if ((e = zero(ws, nws, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_pack_kernel, dim3(grid_of((int64_t)a.O * a.C * a.K)), dim3(256), 0, s,
-                     weight, ws, a.O, a.C, a.K, OP, a.nchunk);
+  hipLaunchKernelGGL(bwd_pack_kernel, dim3(grid_of(nws)), dim3(256), 0, s, weight, ws, a.O, a.C,
+                     a.K, OP, a.nchunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.wt = ws;
   if (a.gx || a.goff || a.gmask) {
@@ -936,14 +988,19 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
     const int64_t g = per_run_units * runs_per_img;
     if (g > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)g), block(256);
-    const bool gv = !a.nhwc_g && a.HoWo % 4 == 0;
-#define DCN_W2(NTO)                                                                         \
-  if (gv) hipLaunchKernelGGL((bwd_weight2_kernel<NTO, true>), grid, block, 0, s, a, n_ot,   \
-                             tiles_per_run, runs_per_img);                                  \
-  else hipLaunchKernelGGL((bwd_weight2_kernel<NTO, false>), grid, block, 0, s, a, n_ot,     \
-                          tiles_per_run, runs_per_img)
-    if (wop == 16) DCN_W2(1);
-    else DCN_W2(4);
+    const bool gv = !a.nhwc_g && a.HoWo % 4 == 0 && (int64_t)a.O * a.HoWo * 4 < (1ll << 31);
+    const bool fullc = a.C % 64 == 0;
+#define DCN_W2(NTO, GV, FC) \
+  hipLaunchKernelGGL((bwd_weight2_kernel<NTO, GV, FC>), grid, block, 0, s, a, n_ot, tiles_per_run, \
+                     runs_per_img)
+#define DCN_W2F(NTO)                          \
+  if (gv && fullc) DCN_W2(NTO, true, true);   \
+  else if (gv) DCN_W2(NTO, true, false);      \
+  else if (fullc) DCN_W2(NTO, false, true);   \
+  else DCN_W2(NTO, false, false)
+    if (wop == 16) DCN_W2F(1);
+    else DCN_W2F(4);
+#undef DCN_W2F
 #undef DCN_W2
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
