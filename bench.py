@@ -458,12 +458,11 @@ def main() -> int:
     ms_per_step = (sum(e[0].elapsed_time(e[2]) for e in events) / args.steps if args.cold
                    else elapsed * 1e3 / args.steps)
     P = spec.pixels * nbr
-    # runs of the split tap sum (1: none): the scratch holds one fp32 partial
-    # output per run, element count rounded up to 64
-    n_out = spec.B * spec.O * spec.Ho * spec.Wo
-    tap_split = 1
-    if not extra and not args.backward and plan.workspace_bytes > plan.packed_weight_bytes:
-        tap_split = (plan.workspace_bytes - plan.packed_weight_bytes) // (-(-n_out // 64) * 64 * 4)
+    # runs of the split tap sum (1: none) and tap groups per workgroup (the
+    # forward runs with the full workspace; multi-branch launches never split)
+    one_launch = bool(extra) and not args.sequential
+    tap_split = plan.tap_runs if not one_launch and not args.backward else 1
+    tap_groups = plan.tap_groups if not one_launch and not args.backward else 1
     # the backward runs two contractions of the forward's size (dL/dsample and dL/dW)
     flops = spec.gemm_flops * nbr * (2 if args.backward else 1)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -489,7 +488,7 @@ def main() -> int:
                    "pad": [spec.ph, spec.pw], "out_layout": args.layout,
                    "input_layout": args.input_layout, "row_bands": nb,
                    "pass": "backward" if args.backward else "forward",
-                   "tap_split": tap_split,
+                   "tap_split": tap_split, "tap_groups": tap_groups,
                    "branches": nbr, "branch_launch": ("one per branch" if args.sequential
                                                       else "one for all") if nbr > 1 else None},
         "tflops": tflops,

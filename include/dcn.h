@@ -107,11 +107,26 @@ dcn_status dcn_output_size(dcn_plan plan, int32_t* ho, int32_t* wo);
  * repacked as [tap][channel block][out channel] tiles (page 1 reorders the
  * weight to rows (i, j, c), columns o before its one matmul), zero-padded to
  * the kernel's tile sizes, then -- for plans whose grid would leave most of
- * the GPU idle (fp32 with 17..64 output channels and few output tiles) --
- * scratch for a split of the tap sum: the taps are divided into up to 4 runs
- * computed side by side into fp32 partial outputs that a second kernel adds
- * (in run order, deterministic) together with the bias. */
+ * the GPU idle even with two tap groups per workgroup (see dcn_tap_schedule)
+ * -- scratch for a split of the tap sum: the taps are divided into up to 4
+ * runs computed side by side into fp32 partial outputs that a second kernel
+ * adds (in run order, deterministic) together with the bias. */
 dcn_status dcn_workspace_bytes(dcn_plan plan, size_t* bytes);
+
+/* How the plan's forward divides the sum over the K taps (fp32 plans with
+ * 17..64 output channels and few output tiles; every other plan reports 1,
+ * K, 1):
+ *   *runs          workgroups per output tile, each summing a contiguous run
+ *                  of taps into a partial output (1: no split; used only when
+ *                  the workspace holds dcn_workspace_bytes bytes)
+ *   *taps_per_run  taps per run (the last run may have fewer)
+ *   *groups        tap groups inside each workgroup: 2 = 8 waves, each half
+ *                  summing half of the workgroup's taps, the halves added in
+ *                  on-chip memory (no workspace needed)
+ * Any pointer may be NULL.  The choice is the whole map's; row-band calls use
+ * it too, so bands stay bit-identical to the whole-map call. */
+dcn_status dcn_tap_schedule(dcn_plan plan, int32_t* runs, int32_t* taps_per_run,
+                            int32_t* groups);
 
 /* Bytes of the packed weight at the start of the workspace (<= the
  * dcn_workspace_bytes size).  dcn_pack_weight writes only these bytes; a

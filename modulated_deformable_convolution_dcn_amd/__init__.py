@@ -99,6 +99,11 @@ class Plan:
         self.workspace_bytes = ws.value
         _lib.check(lib.dcn_packed_weight_bytes(h, ctypes.byref(ws)), "dcn_packed_weight_bytes")
         self.packed_weight_bytes = ws.value
+        runs, kper, groups = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _lib.check(lib.dcn_tap_schedule(h, ctypes.byref(runs), ctypes.byref(kper),
+                                        ctypes.byref(groups)), "dcn_tap_schedule")
+        # tap runs (with a full workspace), taps per run, tap groups per workgroup
+        self.tap_runs, self.taps_per_run, self.tap_groups = runs.value, kper.value, groups.value
 
     def __del__(self):
         h = getattr(self, "_h", None)

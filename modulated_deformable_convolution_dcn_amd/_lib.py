@@ -22,7 +22,7 @@ DCN_OUT_NCHW, DCN_OUT_NHWC = 0, 1
 
 # every symbol include/dcn.h declares
 EXPORTS = ("dcn_create", "dcn_destroy", "dcn_output_size", "dcn_workspace_bytes",
-           "dcn_packed_weight_bytes",
+           "dcn_tap_schedule", "dcn_packed_weight_bytes",
            "dcn_pack_weight", "dcn_forward_packed", "dcn_forward", "dcn_forward_rows",
            "dcn_forward_multi", "dcn_nchw_to_nhwc", "dcn_backward_workspace_bytes",
            "dcn_backward", "dcn_msda_create", "dcn_msda_destroy", "dcn_msda_value_positions",
@@ -76,6 +76,8 @@ def load():
         "dcn_destroy": (st, [vp]),
         "dcn_output_size": (st, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "dcn_workspace_bytes": (st, [vp, ctypes.POINTER(sz)]),
+        "dcn_tap_schedule": (st, [vp, ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
         "dcn_packed_weight_bytes": (st, [vp, ctypes.POINTER(sz)]),
         "dcn_pack_weight": (st, [vp, vp, vp, sz, vp]),
         "dcn_forward_packed": (st, [vp, vp, vp, vp, vp, sz, vp, vp, vp]),

@@ -40,6 +40,7 @@ struct dcn_plan_s {
   size_t wpack_bytes;    // packed weight at the start of the workspace (256-B multiple)
   size_t ws_bytes;       // + scratch for the split tap sum (0 bytes when the plan never splits)
   int nsplit, kper;      // tap split of the whole-map grid (1, K: none); bands use the same
+  int wsplit;            // tap groups per workgroup of the whole-map grid (1 or 2); bands too
   uint32_t x_bytes;
 };
 
@@ -119,23 +120,36 @@ dcn::KernelConfig choose_config(const dcn_desc& d, int Ho, int Wo) {
   return kc;
 }
 
-// The 32x32-per-wave kernel holds two workgroups per CU (one wave per SIMD
-// each); 256 CUs give 512 resident workgroups.  A grid that fills at most half
-// of them splits its tap sum over up to 4 workgroups per tile (each split a
-// contiguous run of taps, at least one), so the chip holds two per CU; a
-// reduce then adds the splits and the bias.
+// The 32x32-per-wave kernel holds two 4-wave workgroups per CU (one wave per
+// SIMD each); 256 CUs give 512 resident workgroups.  A grid that fills at most
+// half of them first runs 8-wave workgroups whose two tap groups each sum half
+// of the taps (added in LDS, no partial outputs in memory), so the chip holds
+// two waves per SIMD; if even those fill at most half of the 256 resident
+// 8-wave workgroups, the tap sum is also split over up to 4 workgroups per
+// tile (each split a contiguous run of taps, at least one per tap group) and
+// a reduce adds the splits and the bias.
 constexpr int64_t kResidentQuadWG = 512;
 
-void choose_split(const dcn::KernelConfig& kc, int K, int64_t nwg, int& nsplit, int& kper) {
+void choose_split(const dcn::KernelConfig& kc, int K, int64_t nwg, int& nsplit, int& kper,
+                  int& wsplit) {
   nsplit = 1;
   kper = K;
+  wsplit = 1;
   if (kc.kind != 2 || nwg <= 0 || 2 * nwg > kResidentQuadWG) return;
-  int ns = (int)(kResidentQuadWG / nwg);
-  if (ns > 4) ns = 4;
-  if (ns > K) ns = K;
-  if (ns < 2) return;
-  kper = (int)ceil_div(K, ns);
-  nsplit = (int)ceil_div(K, kper);
+  if (K >= 2) wsplit = 2;
+  const int64_t resident = kResidentQuadWG / wsplit;
+  int64_t cap = resident / nwg;
+  if (cap > 4) cap = 4;
+  if (cap > K / wsplit) cap = K / wsplit;
+  for (int ns = (int)cap; ns >= 2; --ns) {
+    const int kp = (int)ceil_div(K, ns);
+    const int n = (int)ceil_div(K, kp);
+    if (K - (n - 1) * kp >= wsplit) {  // the last run keeps a tap per group
+      kper = kp;
+      nsplit = n;
+      return;
+    }
+  }
 }
 
 // Floats between consecutive splits' partial outputs: the output's element
@@ -232,7 +246,7 @@ dcn_status dcn_create(const dcn_desc* desc, dcn_plan* plan) {
     p->kc = kc;
     p->wpack_bytes = (size_t)((wp * E + 255) / 256 * 256);
     choose_split(kc, (int)K, (int64_t)d.batch * kc.tiles_per_img * kc.n_otiles, p->nsplit,
-                 p->kper);
+                 p->kper, p->wsplit);
     const int64_t scratch =
         p->nsplit > 1 ? p->nsplit * split_stride(d.batch, d.out_ch, HoWo) * 4 : 0;
     p->ws_bytes = p->wpack_bytes + (size_t)scratch;
@@ -357,6 +371,7 @@ dcn_status make_args(const char* who, dcn_plan plan, int32_t row0, int32_t rows,
   a.nsplit = 1;
   a.kper = plan->K;
   a.split_stride = 0;
+  a.wsplit = 1;
   return ok();
 }
 
@@ -373,6 +388,7 @@ dcn_status forward_band(const char* who, dcn_plan plan, int32_t row0, int32_t ro
     if (st != DCN_OK || empty) return st;
     a.dbg_corner = dbg_corner;
     a.dbg_weight = dbg_weight;
+    a.wsplit = plan->wsplit;  // like the split: the whole map's choice, also for a band
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     // split tap sum when the plan's whole-map grid is small and the workspace
     // carries the scratch; a band splits like the whole map, so the bands of a
@@ -410,6 +426,15 @@ bool same_kernel(const dcn::KernelConfig& p, const dcn::KernelConfig& q) {
 }
 
 }  // namespace
+
+dcn_status dcn_tap_schedule(dcn_plan plan, int32_t* runs, int32_t* taps_per_run,
+                            int32_t* groups) {
+  if (!plan) return fail(DCN_E_NULL, "dcn_tap_schedule: plan is NULL");
+  if (runs) *runs = plan->nsplit;
+  if (taps_per_run) *taps_per_run = plan->kper;
+  if (groups) *groups = plan->wsplit;
+  return ok();
+}
 
 dcn_status dcn_forward_packed(dcn_plan plan, const void* x, const void* offset, const void* mask,
                               void* workspace, size_t workspace_bytes, const void* bias,
@@ -458,10 +483,13 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
                                 workspace_bytes[i], biases ? biases[i] : nullptr, outs[i],
                                 args[i], cfg[i], empty);
       if (st != DCN_OK) return st;
+      // tap groups as in the branch's own calls (never a split into runs), so
+      // each branch reproduces its own forward_packed call bit for bit
+      args[i].wsplit = plans[i]->wsplit;
       live[i] = !empty;
     }
-    // one launch per group of branches that run the same kernel variant; the
-    // general kernel takes its branches one launch each
+    // one launch per group of branches that run the same kernel variant (and
+    // tap-group count); the general kernel takes its branches one launch each
     bool done[dcn::kMaxBranches] = {};
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     for (int i = 0; i < n; ++i) {
@@ -475,7 +503,9 @@ dcn_status dcn_forward_multi(int32_t n, const dcn_plan* plans, const void* x,
       dcn::MultiArgs m{};
       int64_t total = 0;
       for (int j = i; j < n; ++j) {
-        if (!live[j] || done[j] || !same_kernel(cfg[i], cfg[j])) continue;
+        if (!live[j] || done[j] || !same_kernel(cfg[i], cfg[j]) ||
+            args[j].wsplit != args[i].wsplit)
+          continue;
         m.start[m.n] = (int)total;
         m.a[m.n] = args[j];
         ++m.n;

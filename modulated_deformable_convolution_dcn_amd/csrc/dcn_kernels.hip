@@ -615,7 +615,8 @@ hipError_t launch_pack(const KernelConfig& kc, const void* weight, void* wpack, 
 }
 
 hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  if (kc.kind != 2 && a.nsplit != 1) return hipErrorInvalidValue;  // only that kernel splits taps
+  // only that kernel splits taps or runs tap groups
+  if (kc.kind != 2 && (a.nsplit != 1 || a.wsplit != 1)) return hipErrorInvalidValue;
   if (kc.kind == 1) return launch_fused_wsk(kc, a, s);
   if (kc.kind == 2) return launch_fused_quad(kc, a, s);
   if (kc.kind == 3) return launch_fused_bf16w(kc, a, s);
@@ -628,8 +629,8 @@ hipError_t launch_fused(const KernelConfig& kc, const FusedArgs& a, hipStream_t 
 
 hipError_t launch_fused_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
   if (m.n < 1 || m.n > kMaxBranches) return hipErrorInvalidValue;
-  for (int i = 0; i < m.n; ++i)
-    if (m.a[i].nsplit != 1) return hipErrorInvalidValue;  // one grid slot per tile
+  for (int i = 0; i < m.n; ++i)  // one grid slot per tile; tap groups only in that kernel
+    if (m.a[i].nsplit != 1 || (kc.kind != 2 && m.a[i].wsplit != 1)) return hipErrorInvalidValue;
   if (kc.kind == 1) return launch_fused_wsk_multi(kc, m, s);
   if (kc.kind == 2) return launch_fused_quad_multi(kc, m, s);
   if (kc.kind == 3) return launch_fused_bf16w_multi(kc, m, s);

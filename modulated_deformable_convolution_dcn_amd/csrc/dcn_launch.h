@@ -45,6 +45,10 @@ struct FusedArgs {
   int nsplit;          // 1: the whole sum plus bias, straight into out
   int kper;            // taps per split (K when nsplit is 1)
   uint32_t split_stride;  // floats between consecutive splits' partial outputs
+  // Tap groups inside each workgroup (32x32-per-wave kernel only, else 1):
+  // 2 = 8-wave workgroups whose two 4-wave groups each sum half of the
+  // split's taps, added in LDS; every split then has at least 2 taps.
+  int wsplit;
   // Test hook (dcn_debug_corner_table; nullptr on every other call): the
   // kernel also writes each (b, tap, pixel)'s corner-table entry as it builds
   // it -- corner token index (b*H + y)*W + x (-1 for an outside corner) and

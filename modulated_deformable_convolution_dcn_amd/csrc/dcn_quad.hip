@@ -27,6 +27,12 @@
 // 2, 3), then rows 16-31 while blending block s+1 rows 0-15 (passes 0, 1).
 // Each blended pass frees its corner registers, which immediately take the
 // same pass of the next block (one full step before they are needed).
+//
+// Tap groups (WS = 2): for grids too small to hold two 4-wave workgroups per
+// CU, a workgroup has 8 waves, two groups of four, each running the pipeline
+// above over one half of the workgroup's taps; the four partial sums of each
+// pixel meet in LDS at the end, so the chip holds two waves per SIMD with no
+// partial outputs in memory.
 
 #include <type_traits>
 
@@ -38,8 +44,9 @@ namespace dcn {
 // NCH: the number of 64-channel chunks when it is known to be 1 (the
 // 64-channel workloads), else 0 (read from the arguments): a compile-time 1
 // removes the per-step divisions by it from the scalar instruction stream.
-template <bool NHWC, bool FULLC, int NCH, class Src>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// WS: tap groups per workgroup (1: 4 waves, 2: 8 waves).
+template <bool NHWC, bool FULLC, int NCH, int WS, class Src>
+__global__ __launch_bounds__(256 * WS) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 fused_quad_kernel(Src src) {
   int logical;
   const FusedArgs& a = resolve_args(src, logical);
@@ -51,10 +58,12 @@ fused_quad_kernel(Src src) {
   constexpr int NT = NO / 16;     // 16-column MFMA tiles
   constexpr int AST = 32;         // column-tile row: 32 channels, 16-byte chunks XOR-swizzled
   constexpr int NSLOT = 3;        // coefficient ring
+  constexpr int NWV = 4 * WS;     // waves
+  constexpr int NTH = 64 * NWV;   // threads
   constexpr int A_FLOATS = PW * AST;
-  constexpr int MAIN_BYTES = 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 32;
+  constexpr int MAIN_BYTES = NWV * A_FLOATS * 4 + NWV * NSLOT * PW * 32;
   constexpr int RST = PW + 4;
-  constexpr int RED_BYTES = 4 * NO * RST * 4;
+  constexpr int RED_BYTES = NWV * NO * RST * 4;
   constexpr int SMEM = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
 
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -62,12 +71,13 @@ fused_quad_kernel(Src src) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wh = wave >> 1;  // pixel half
+  const int wq = WS == 1 ? 0 : wave >> 2;               // tap group
+  const int wh = WS == 1 ? wave >> 1 : (wave >> 1) & 1;  // pixel half
   const int wc = wave & 1;   // channel half
 
   float* const Aw = reinterpret_cast<float*>(smem) + wave * A_FLOATS;
-  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + 4 * A_FLOATS * 4) + wave * NSLOT * PW;
-  u32x4* const Co = reinterpret_cast<u32x4*>(smem + 4 * A_FLOATS * 4 + 4 * NSLOT * PW * 16) +
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + NWV * A_FLOATS * 4) + wave * NSLOT * PW;
+  u32x4* const Co = reinterpret_cast<u32x4*>(smem + NWV * A_FLOATS * 4 + NWV * NSLOT * PW * 16) +
                     wave * NSLOT * PW;
   float* const red = reinterpret_cast<float*>(smem);  // [wave][NO][RST]
   // Column tile: row r (pixel), 16-byte chunk k (channels 4k .. 4k+3) at
@@ -85,9 +95,14 @@ fused_quad_kernel(Src src) {
   const int tile = t2 % a.tiles_per_img;
   const int b = t2 / a.tiles_per_img;
   const int hw0 = tile * M + wh * PW;  // first pixel of this wave
-  // taps [k0, k0 + kn) of this split; kt below counts from k0
-  const int k0 = split * a.kper;
-  const int kn = min(a.kper, a.K - k0);
+  // taps [k0, k0 + kn) of this split and tap group (group 0 takes the first
+  // ceil(n / 2) of the split's n taps, group 1 the rest: the host gives every
+  // split at least WS taps); kt below counts from k0
+  const int ks = split * a.kper;
+  const int kns = min(a.kper, a.K - ks);
+  const int khalf = WS == 1 ? kns : (kns + 1) >> 1;
+  const int k0 = WS == 1 ? ks : ks + wq * khalf;
+  const int kn = WS == 1 ? kns : (wq == 0 ? khalf : kns - khalf);
   const int NKB = kn * nchunk;
   auto clampb = [&](int kb) { return kb < NKB ? kb : NKB - 1; };
   auto clampt = [&](int kt) { return kt < kn ? kt : kn - 1; };
@@ -336,7 +351,8 @@ fused_quad_kernel(Src src) {
   }
   if (s < NKB) step(s, S0{});
 
-  // ---- epilogue: sum the two channel halves of each pixel half, + bias, store
+  // ---- epilogue: sum the two channel halves (and tap groups) of each pixel
+  // half, + bias, store: (g0 c0 + g0 c1) + (g1 c0 + g1 c1)
   __syncthreads();  // every wave is done with its column tile and tables
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -350,16 +366,21 @@ fused_quad_kernel(Src src) {
   const int base_hw = tile * M;
   if constexpr (!NHWC) {
     // thread -> (pixel half, output channel, run of 4 pixels)
-    for (int e = tid; e < 2 * NO * (PW / 4); e += 256) {
+    for (int e = tid; e < 2 * NO * (PW / 4); e += NTH) {
       const int h = e / (NO * (PW / 4));
       const int rem = e - h * NO * (PW / 4);
       const int col = rem / (PW / 4);
       const int r4 = rem - col * (PW / 4);
       const int o = otile * NO + col;
       if (o >= a.O) continue;
-      const int w0 = h * 2;  // waves (h, 0) and (h, 1)
+      const int w0 = h * 2;  // waves (h, 0) and (h, 1) of tap group 0
       f32x4 v = *reinterpret_cast<const f32x4*>(&red[(w0 * NO + col) * RST + r4 * 4]);
       v += *reinterpret_cast<const f32x4*>(&red[((w0 + 1) * NO + col) * RST + r4 * 4]);
+      if constexpr (WS == 2) {
+        f32x4 u = *reinterpret_cast<const f32x4*>(&red[((w0 + 4) * NO + col) * RST + r4 * 4]);
+        u += *reinterpret_cast<const f32x4*>(&red[((w0 + 5) * NO + col) * RST + r4 * 4]);
+        v += u;
+      }
       v += biasp ? biasp[o] : 0.0f;
       const int hw = base_hw + h * PW + r4 * 4;
       float* dst = outp + ((size_t)b * a.O + o) * a.HoWo + hw;
@@ -372,15 +393,17 @@ fused_quad_kernel(Src src) {
       }
     }
   } else {
-    for (int e = tid; e < M * NO; e += 256) {
+    for (int e = tid; e < M * NO; e += NTH) {
       const int col = e % NO;
       const int px = e / NO;
       const int h = px / PW, row = px - h * PW;
       const int o = otile * NO + col;
       const int hw = base_hw + px;
       if (o >= a.O || hw >= a.HoWo) continue;
-      const float v = red[(2 * h * NO + col) * RST + row] + red[((2 * h + 1) * NO + col) * RST + row] +
-                      (biasp ? biasp[o] : 0.0f);
+      float v = red[(2 * h * NO + col) * RST + row] + red[((2 * h + 1) * NO + col) * RST + row];
+      if constexpr (WS == 2)
+        v += red[((2 * h + 4) * NO + col) * RST + row] + red[((2 * h + 5) * NO + col) * RST + row];
+      v += biasp ? biasp[o] : 0.0f;
       outp[((size_t)b * a.HoWo + hw) * a.O + o] = v;
     }
   }
@@ -391,36 +414,39 @@ bool quad_supported(const KernelConfig& kc) {
 }
 
 namespace {
-template <bool NHWC, int NCH, class Src>
+template <bool NHWC, int NCH, int WS, class Src>
 void launch_quad_fc(bool fullc, dim3 grid, hipStream_t s, const Src& src) {
-  if (fullc) hipLaunchKernelGGL((fused_quad_kernel<NHWC, true, NCH, Src>), grid, dim3(256), 0, s, src);
-  else hipLaunchKernelGGL((fused_quad_kernel<NHWC, false, NCH, Src>), grid, dim3(256), 0, s, src);
+  const dim3 block(256 * WS);
+  if (fullc) hipLaunchKernelGGL((fused_quad_kernel<NHWC, true, NCH, WS, Src>), grid, block, 0, s, src);
+  else hipLaunchKernelGGL((fused_quad_kernel<NHWC, false, NCH, WS, Src>), grid, block, 0, s, src);
 }
 
-// one_chunk: every problem of the launch has C <= 64
-template <class Src>
-hipError_t launch_quad_src(const KernelConfig& kc, const Src& src, int C, bool one_chunk,
-                           int64_t nblk, hipStream_t s) {
-  if (nblk <= 0) return hipSuccess;
-  if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
-  const bool fullc = C % 64 == 0;
-  const dim3 grid((unsigned)nblk);
-  if (kc.nhwc) {
-    if (one_chunk) launch_quad_fc<true, 1>(fullc, grid, s, src);
-    else launch_quad_fc<true, 0>(fullc, grid, s, src);
+template <int WS, class Src>
+void launch_quad_ws(bool nhwc, bool one_chunk, bool fullc, dim3 grid, hipStream_t s,
+                    const Src& src) {
+  if (nhwc) {
+    if (one_chunk) launch_quad_fc<true, 1, WS>(fullc, grid, s, src);
+    else launch_quad_fc<true, 0, WS>(fullc, grid, s, src);
   } else {
-    if (one_chunk) launch_quad_fc<false, 1>(fullc, grid, s, src);
-    else launch_quad_fc<false, 0>(fullc, grid, s, src);
+    if (one_chunk) launch_quad_fc<false, 1, WS>(fullc, grid, s, src);
+    else launch_quad_fc<false, 0, WS>(fullc, grid, s, src);
   }
-  return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_fused_quad(const KernelConfig& kc, const FusedArgs& a, hipStream_t s) {
-  if (a.nsplit < 1 || a.kper < 1 || (int64_t)(a.nsplit - 1) * a.kper >= a.K)
-    return hipErrorInvalidValue;  // every split needs at least one tap
-  return launch_quad_src(kc, a, a.C, a.nchunk == 1,
-                         (int64_t)a.B * kc.tiles_per_img * a.nsplit * kc.n_otiles, s);
+  // every split needs at least one tap, and with two tap groups two
+  if (a.nsplit < 1 || a.kper < a.wsplit || (a.wsplit != 1 && a.wsplit != 2) ||
+      (int64_t)(a.nsplit - 1) * a.kper >= a.K || a.K - (int64_t)(a.nsplit - 1) * a.kper < a.wsplit)
+    return hipErrorInvalidValue;
+  const int64_t nblk = (int64_t)a.B * kc.tiles_per_img * a.nsplit * kc.n_otiles;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nblk);
+  const bool fullc = a.C % 64 == 0, one_chunk = a.nchunk == 1;
+  if (a.wsplit == 2) launch_quad_ws<2>(kc.nhwc, one_chunk, fullc, grid, s, a);
+  else launch_quad_ws<1>(kc.nhwc, one_chunk, fullc, grid, s, a);
+  return hipGetLastError();
 }
 
 namespace {
@@ -476,9 +502,23 @@ hipError_t launch_split_reduce(const float* part, int nsplit, uint32_t stride, c
 }
 
 hipError_t launch_fused_quad_multi(const KernelConfig& kc, const MultiArgs& m, hipStream_t s) {
+  if (m.n < 1) return hipSuccess;
   bool one_chunk = true;
-  for (int i = 0; i < m.n; ++i) one_chunk = one_chunk && m.a[i].nchunk == 1;
-  return launch_quad_src(kc, m, m.a[0].C, one_chunk, m.start[m.n], s);
+  const int ws = m.a[0].wsplit;
+  for (int i = 0; i < m.n; ++i) {
+    one_chunk = one_chunk && m.a[i].nchunk == 1;
+    // one tap-group count per launch, never a split into runs
+    if (m.a[i].wsplit != ws || (ws != 1 && ws != 2) || m.a[i].nsplit != 1 ||
+        m.a[i].K < ws)
+      return hipErrorInvalidValue;
+  }
+  const int64_t nblk = m.start[m.n];
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffff || !quad_supported(kc)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nblk);
+  if (ws == 2) launch_quad_ws<2>(kc.nhwc, one_chunk, m.a[0].C % 64 == 0, grid, s, m);
+  else launch_quad_ws<1>(kc.nhwc, one_chunk, m.a[0].C % 64 == 0, grid, s, m);
+  return hipGetLastError();
 }
 
 }  // namespace dcn

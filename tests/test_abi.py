@@ -108,22 +108,29 @@ def test_output_size_and_workspace():
         assert p.packed_weight_bytes == p.workspace_bytes  # grids that fill the GPU: no split
 
 
-@pytest.mark.parametrize("shape,nsplit", [
-    ((1, 64, 256, 256, 64, 7, 7, 3, 3), 1),     # 1024 workgroups: no split
-    ((1, 64, 128, 128, 64, 7, 7, 3, 3), 2),     # 256 workgroups: two runs of taps
-    ((1, 64, 64, 64, 64, 7, 7, 3, 3), 4),       # 64 workgroups: four runs (13, 13, 13, 10)
-    ((1, 64, 20, 20, 64, 1, 3, 0, 1), 3),       # K = 3: at most one run per tap
-    ((1, 64, 20, 20, 64, 1, 1, 0, 0), 1),       # K = 1: nothing to split
-    ((2, 96, 90, 90, 48, 3, 3, 1, 1), 2),       # 2 images x 127 tiles = 254 workgroups
+@pytest.mark.parametrize("shape,nsplit,kper,groups", [
+    ((1, 64, 256, 256, 64, 7, 7, 3, 3), 1, 49, 1),  # 1024 workgroups: no split
+    ((1, 64, 128, 128, 64, 7, 7, 3, 3), 1, 49, 2),  # 256 tiles: 8-wave workgroups, 25 + 24 taps
+    ((1, 64, 64, 64, 64, 7, 7, 3, 3), 4, 13, 2),    # 64 tiles: four runs (13, 13, 13, 10)
+    ((1, 64, 40, 40, 64, 1, 5, 0, 2), 2, 3, 2),     # K = 5, 25 tiles: runs of 3 and 2 taps
+    ((1, 64, 20, 20, 64, 1, 3, 0, 1), 1, 3, 2),     # K = 3: no run could keep a tap per group
+    ((1, 64, 20, 20, 64, 1, 1, 0, 0), 1, 1, 1),     # K = 1: nothing to split
+    ((2, 96, 90, 90, 48, 3, 3, 1, 1), 1, 9, 2),     # 2 images x 127 tiles = 254 workgroups
+    ((1, 64, 64, 64, 128, 7, 7, 3, 3), 1, 49, 1),   # 128 outputs: another kernel, no split
 ])
-def test_tap_split_workspace(shape, nsplit):
+def test_tap_split_workspace(shape, nsplit, kper, groups):
     """fp32 plans of 17..64 output channels whose grid would fill at most half
-    of the 512 resident workgroups split their taps; the scratch holds one
-    fp32 partial output per run (element count rounded up to 64)."""
+    of the 512 resident 4-wave workgroups run 8-wave workgroups of two tap
+    groups; if those fill at most half of the 256 resident 8-wave workgroups,
+    the taps are also split into runs (at least one tap per group each), and
+    the scratch holds one fp32 partial output per run (element count rounded
+    up to 64)."""
     B, C, H, W_, O, kh, kw, ph, pw = shape
     p = Plan(Desc(B, C, H, W_, O, kh, kw, ph, pw))
     K = kh * kw
-    assert p.packed_weight_bytes == ((K * -(-C // 64) * 64 * 64 * 4 + 255) // 256) * 256
+    assert (p.tap_runs, p.taps_per_run, p.tap_groups) == (nsplit, kper, groups)
+    if O <= 64:
+        assert p.packed_weight_bytes == ((K * -(-C // 64) * 64 * 64 * 4 + 255) // 256) * 256
     n = B * O * p.Ho * p.Wo
     scratch = 0 if nsplit == 1 else nsplit * (-(-n // 64) * 64) * 4
     assert p.workspace_bytes == p.packed_weight_bytes + scratch
