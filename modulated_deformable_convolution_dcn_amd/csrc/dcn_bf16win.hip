@@ -301,9 +301,13 @@ fused_bf16win_kernel(Src src) {
     u32x4 fv[2];       // window loads in flight, by load index parity
 
     // ---- prologue: block 0 blended into As[0]; the corners of block 1, the
-    // weights of block 0 and the first two window loads of chunk 1 in flight
+    // weights of blocks 0 and 1 and the first two window loads of chunk 1 in
+    // flight
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) bw[0][nt] = b_load(0, 0, nt);
+    for (int nt = 0; nt < NTW; ++nt) {
+      bw[0][nt] = b_load(0, 0, nt);
+      bw[1][nt] = b_load(0, 1, nt);
+    }
     {
       const u32x4 ent = Cx[0][pp];
       const u32x2 w = Cw[0][pp];
@@ -337,7 +341,8 @@ fused_bf16win_kernel(Src src) {
     // channel j % 8) of block s+1; after a corner row's last unit the fetch of
     // its two corners for block s+2; after the last unit the bf16 rounding
     // and the column-tile write; column-tile fragments AFD tiles ahead; the
-    // weight fragments of block s+1 in the first two slots.
+    // weight fragments of block s+2 in the first two slots (ring slot
+    // (s + 2) % 3 = (s - 1) % 3, free since block s-1's MFMAs).
     // Window of chunk c+1: load u is issued at step s = KT (c + 1) + u - KT - 2
     // (two steps before it is written) and written at step (c, u), u < FPT,
     // before that step's barrier: after the last fetch from the buffer (chunk
@@ -351,8 +356,7 @@ fused_bf16win_kernel(Src src) {
         const int par = (c + t) & 1;  // s & 1 (KT is odd)
         const char* A = As[par];
         char* An = As[par ^ 1];
-        const int c1 = t + 1 >= KT && c + 1 < nch ? c + 1 : c;  // chunks of s+1, s+2,
-        const int c2 = t + 2 >= KT && c + 1 < nch ? c + 1 : c;  // clamped at the end
+        const int c2 = t + 2 >= KT && c + 1 < nch ? c + 1 : c;  // chunk of s+2, clamped at the end
 
         if constexpr (WIN && t < FPT) {
           if (c + 1 < nch) fill_store((c + 1) & 1, t, fv[t & 1]);
@@ -377,7 +381,7 @@ fused_bf16win_kernel(Src src) {
               __builtin_bit_cast(bf16x8, af[mt % (AFD + 1)]),
               __builtin_bit_cast(bf16x8, bw[t % 3][nt]), acc[mt][nt], 0, 0, 0);
           if constexpr (nt == 0 && mt + AFD < MT) af[(mt + AFD) % (AFD + 1)] = a_frag(A, mt + AFD);
-          if constexpr (mt == 0) bw[t1 % 3][nt] = b_load(c1, t1, nt);
+          if constexpr (mt == 0) bw[t2 % 3][nt] = b_load(c2, t2, nt);
           // blend unit: corner row cp, channel e = 2 * (dword) + (half)
           constexpr int cp = j / 8, e = j % 8;
           r[e] = pair_dot(gv[2 * cp][e / 2], gv[2 * cp + 1][e / 2], e & 1, wt[cp],
