@@ -326,9 +326,10 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
 //   layout 1 (k split over waves, CB = 64, VEC = 4): [wave][NO/16][g][16][4]
 //            = channel 16*wave + 4g + e, output 16*nt + col -- one wave's MFMA
 //            B fragments for a block are one contiguous run per nt;
-//   layout 2 (32 x 32 per wave, CB = 64, VEC = 4): [half][NO/16][q][g][16][4]
-//            = channel 32*half + 8g + 4q + e, output 16*nt + col -- one
-//            1 KB run per (nt, q) for the wave owning that channel half;
+//   layout 2 (32 x 32 per wave, CB = 64, VEC = 4): [half][NO/32][q][lane][4]
+//            = channel 32*half + 16*(lane/32) + 4q + e, output 32n + lane%32
+//            (32x32x2 MFMA B fragments) -- one 1 KB run per (n, q) for the
+//            wave owning that channel half;
 //   layout 3 (bf16 16x16x32 fragments, VEC = 8): [CB/32][NO/16][g][16][8]
 //            = channel 32q + 8g + e, output 16*nt + col -- fragment (q, nt)
 //            is one 1 KB run in lane order.
@@ -350,9 +351,9 @@ __device__ __forceinline__ void packed_source(int in, int layout, int NO, int VE
       return;
     }
     case 2: {
-      const int t = in >> 9;
-      c_in = (t / NT) * 32 + ((in >> 6) & 3) * 8 + ((in >> 8) & 1) * 4 + (in & 3);
-      o_in = (t % NT) * 16 + ((in >> 2) & 15);
+      const int ln = (in >> 2) & 63, t = in >> 10, NN = NO >> 5;
+      c_in = (t / NN) * 32 + (ln >> 5) * 16 + ((in >> 8) & 3) * 4 + (in & 3);
+      o_in = (t % NN) * 32 + (ln & 31);
       return;
     }
     default: {

@@ -20,13 +20,19 @@
 //     halves are summed through LDS once at the end.
 // The choice keeps the per-MFMA instruction mix small: on gfx950 every VALU
 // op or LDS read issued beside the MFMAs costs matrix-pipe time, and this
-// split needs 4 LDS fragment reads and 8 weight loads per 64 MFMAs.
+// split needs 4 LDS fragment reads and 8 weight loads per 32x32x2 k-block
+// of the wave (32 MFMAs of 2048 multiply-adds each).  The 32x32x2 fp32
+// MFMA does the work of two 16x16x4 ones in one instruction: on this chip,
+// with one VALU op per 1024 multiply-adds beside it, it takes about 9 % less
+// time per multiply-add than the 16x16x4 form in isolation and 2 % less in
+// this kernel on the 256 x 256, 64-channel 7 x 7 shape (the corner gather
+// through the vector L1 bounds the rest).
 //
-// Software pipeline (single column buffer, two 16-row groups): step s runs
-// the MFMAs of block s rows 0-15 while blending block s rows 16-31 (passes
-// 2, 3), then rows 16-31 while blending block s+1 rows 0-15 (passes 0, 1).
-// Each blended pass frees its corner registers, which immediately take the
-// same pass of the next block (one full step before they are needed).
+// Software pipeline (two column-tile buffers per wave): step s runs the
+// MFMAs of block s from buffer s & 1 while blending block s+1 into the other
+// buffer, four passes of 8 pixels.  Each blended pass frees its corner
+// registers, which immediately take the same pass of block s+2 (one full
+// step before they are needed).
 //
 // Tap groups (WS = 2): for grids too small to hold two 4-wave workgroups per
 // CU, a workgroup has 8 waves, two groups of four, each running the pipeline
@@ -40,6 +46,8 @@
 #include "dcn_launch.h"
 
 namespace dcn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // NCH: the number of 64-channel chunks when it is known to be 1 (the
 // 64-channel workloads), else 0 (read from the arguments): a compile-time 1
@@ -55,13 +63,12 @@ fused_quad_kernel(Src src) {
   constexpr int NO = 64;          // output channels per workgroup
   constexpr int CB = 64;          // channels per k-block
   constexpr int PW = 32;          // pixels per wave
-  constexpr int NT = NO / 16;     // 16-column MFMA tiles
   constexpr int AST = 32;         // column-tile row: 32 channels, 16-byte chunks XOR-swizzled
   constexpr int NSLOT = 3;        // coefficient ring
   constexpr int NWV = 4 * WS;     // waves
   constexpr int NTH = 64 * NWV;   // threads
-  constexpr int A_FLOATS = PW * AST;
-  constexpr int MAIN_BYTES = NWV * A_FLOATS * 4 + NWV * NSLOT * PW * 32;
+  constexpr int A_FLOATS = PW * AST;  // one column tile
+  constexpr int MAIN_BYTES = NWV * 2 * A_FLOATS * 4 + NWV * NSLOT * PW * 32;
   constexpr int RST = PW + 4;
   constexpr int RED_BYTES = NWV * NO * RST * 4;
   constexpr int SMEM = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
@@ -75,10 +82,11 @@ fused_quad_kernel(Src src) {
   const int wh = WS == 1 ? wave >> 1 : (wave >> 1) & 1;  // pixel half
   const int wc = wave & 1;   // channel half
 
-  float* const Aw = reinterpret_cast<float*>(smem) + wave * A_FLOATS;
-  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + NWV * A_FLOATS * 4) + wave * NSLOT * PW;
-  u32x4* const Co = reinterpret_cast<u32x4*>(smem + NWV * A_FLOATS * 4 + NWV * NSLOT * PW * 16) +
-                    wave * NSLOT * PW;
+  float* const Aw = reinterpret_cast<float*>(smem) + wave * 2 * A_FLOATS;  // [2][A_FLOATS]
+  f32x4* const Cw = reinterpret_cast<f32x4*>(smem + NWV * 2 * A_FLOATS * 4) + wave * NSLOT * PW;
+  u32x4* const Co =
+      reinterpret_cast<u32x4*>(smem + NWV * 2 * A_FLOATS * 4 + NWV * NSLOT * PW * 16) +
+      wave * NSLOT * PW;
   float* const red = reinterpret_cast<float*>(smem);  // [wave][NO][RST]
   // Column tile: row r (pixel), 16-byte chunk k (channels 4k .. 4k+3) at
   // float r * 32 + 4 * (k ^ ((r >> 1) & 7)): the eight-lane row writes of two
@@ -196,31 +204,47 @@ fused_quad_kernel(Src src) {
     return FULLC || ch < a.C;
   };
   auto slot_of = [&](int kb) { return (kb / nchunk) % NSLOT; };
-
-  // ---- (c) MFMA: k-slot g (lane / 16) owns the wave's channels 8g .. 8g+7;
-  // fragment read q holds channels 8g + 4q + [0, 4), i.e. k-steps 4q .. 4q+3.
-  // Weight block layout [half][nt][q][g][col][e] (channel 32*half + 8g + 4q + e,
-  // output 16*nt + col): the wave's 8 pieces are 1 KB coalesced runs.
-  const int rl = lane & 15;
-  const int g = lane >> 4;
-  f32x4 acc[2][NT];
+  // the modulated sample of pass p: 4 corner slices times their weights
+  auto blend = [&](const f32x4& w, int p) {
+    f32x4 r = __builtin_bit_cast(f32x4, gv[p][0]) * w[0];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int c = 1; c < 4; ++c) {
+      const f32x4 v = __builtin_bit_cast(f32x4, gv[p][c]);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 af[2][2];      // [row group][q]
-  f32x4 bw[2][NT * 2];  // [set][nt * 2 + q]
-  auto b_src = [&](int kb) {
-    return wblocks + (size_t)kb * (CB * NO) + (size_t)wc * (NT * 2 * 256) + (g * 16 + rl) * 4;
+      for (int kk = 0; kk < 4; ++kk) r[kk] = __builtin_fmaf(w[c], v[kk], r[kk]);
+    }
+    return r;
   };
-  auto a_frag = [&](int mt, int q) {
-    return *reinterpret_cast<const f32x4*>(&Aw[a_at(mt * 16 + rl, 2 * g + q)]);
+
+  // ---- (c) MFMA 32x32x2 (fp32): A row i = pixel (lane % 32), B column j =
+  // output (lane % 32) of a 32-output half n; lane half hh = lane / 32 takes
+  // k = hh of each k-step.  K-step t (0 .. 15) of the wave's 32 channels is
+  // channel 16 hh + t for lane half hh, so fragment read q of a lane holds
+  // channels 16 hh + 4q + [0, 4) of its pixel = k-steps 4q .. 4q+3.
+  // Weight block layout [channel half wc][n][q][lane][e] (channel
+  // 32 wc + 16 (lane / 32) + 4q + e, output 32 n + lane % 32): each of the
+  // wave's 8 fragments is one 1 KB run.
+  const int rl = lane & 31;
+  const int hh = lane >> 5;
+  f32x16 acc[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.0f;
+  f32x4 af[4];          // A fragments (q) of one block
+  f32x4 bw[2][8];       // [set][n * 4 + q]
+  auto b_src = [&](int kb) {
+    return wblocks + (size_t)kb * (CB * NO) + (size_t)wc * (2 * 4 * 256) + lane * 4;
+  };
+  auto a_frag = [&](int buf, int q) {
+    return *reinterpret_cast<const f32x4*>(&Aw[buf * A_FLOATS + a_at(rl, 4 * hh + q)]);
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  // ---- prologue
+  // ---- prologue: tables of taps 0 .. 2, block 0 blended into tile buffer 0,
+  // the corners of block 1 and the weights of block 0 in flight
   {
     float dy, dx, mk;
 #pragma unroll
@@ -234,7 +258,7 @@ fused_quad_kernel(Src src) {
   {
     const float* src = b_src(0);
 #pragma unroll
-    for (int k = 0; k < NT * 2; ++k) bw[0][k] = *reinterpret_cast<const f32x4*>(src + k * 256);
+    for (int k = 0; k < 8; ++k) bw[0][k] = *reinterpret_cast<const f32x4*>(src + k * 256);
   }
   {
     uint32_t cb0, cb1;
@@ -248,100 +272,87 @@ fused_quad_kernel(Src src) {
       for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok0 ? off[c] + cb0 : kNoCorner);
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const u32x4 r = Ops<float>::blend(Cw[s0 * PW + p * 8 + pp], gv[p][0], gv[p][1], gv[p][2],
-                                        gv[p][3]);
-      *reinterpret_cast<u32x4*>(&Aw[a_at(p * 8 + pp, sl)]) = r;
+    for (int p = 0; p < 4; ++p) {
+      const f32x4 r = blend(Cw[s0 * PW + p * 8 + pp], p);
+      *reinterpret_cast<f32x4*>(&Aw[a_at(p * 8 + pp, sl)]) = r;
       const u32x4 off = Co[s1 * PW + p * 8 + pp];
 #pragma unroll
       for (int c = 0; c < 4; ++c) gv[p][c] = load16(xr, ok1 ? off[c] + cb1 : kNoCorner);
     }
-    af[0][0] = a_frag(0, 0);
-    af[0][1] = a_frag(0, 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) af[q] = a_frag(0, q);
   }
 
-  // ---- one step s: two groups of 32 MFMAs with the other work pinned
-  // between them (one action per MFMA slot, in this order).
-  // Group 0 (rows 0-15 of block s): blend of block s passes 2, 3 (rows
-  // 16-31) and their corner loads for block s+1; fragments of rows 16-31;
-  // weight fragments of block s+1.
-  // Group 1 (rows 16-31): blend of block s+1 passes 0, 1 (rows 0-15) and
-  // their corner loads for block s+2; fragments of rows 0-15 of block s+1;
-  // the coefficient table of tap (s+3)/nchunk (four stages in four slots) from
-  // offsets loaded two steps
-  // ago, then the offsets of tap (s+5)/nchunk.
-  // Per pass pair: 4 table reads, then per pass 4 blend terms, the tile
-  // write and 4 corner loads (22 actions).
-  constexpr int NMF = 8 * NT;  // MFMAs per group
-  constexpr int NPA = 22;
+  // ---- one step s: the 32 MFMAs of block s (tile buffer P = s & 1), with
+  // one or two actions pinned after each, in this order: fragment 3 of block
+  // s; per pass p of block s+1 (into buffer P ^ 1) the table reads, the four
+  // blend terms, the tile write, the pass's corner loads for block s+2 and
+  // two of block s+1's weight fragments; fragments 0 .. 2 of block s+1 (after
+  // the MFMAs that read those registers for block s: fragment q serves MFMAs
+  // 8q .. 8q+7); the coefficient table of tap (s+3)/nchunk in four stages from
+  // offsets loaded two steps ago; the offsets of tap (s+5)/nchunk.
+  constexpr int NMF = 32;  // MFMAs per step
+  constexpr int NPA = 13;  // actions per pass
+  constexpr int NACT = 1 + 4 * NPA + 3 + 4 + 1;
   auto step = [&](int s, auto par) {
     constexpr int P = decltype(par)::value;  // s & 1
     const int n1 = clampb(s + 1), n2 = clampb(s + 2);
-    const int sl_s = slot_of(s), sl_1 = slot_of(n1), sl_2 = slot_of(n2);
-    uint32_t cb1, cb2;
-    const bool ok1 = chan(n1, cb1);
+    const int sl_1 = slot_of(n1), sl_2 = slot_of(n2);
+    uint32_t cb2;
     const bool ok2 = chan(n2, cb2);
     const float* bsrc = b_src(n1);
     const int tc = (s + 3) / nchunk;
     const bool coef_due = tc * nchunk == s + 3 && tc < kn;
     const int tl = clampt((s + 5) / nchunk);
-    static_for<2>([&](auto MT) {
-      constexpr int mt = decltype(MT)::value;
-      constexpr int pa = mt == 0 ? 2 : 0;  // passes blended under this group
-      constexpr int NACT = NPA + 2 + (mt == 0 ? NT * 2 : 5);
-      // group 0: blend block s, load block s+1; group 1: blend s+1, load s+2
-      const int slw = mt == 0 ? sl_s : sl_1;
-      const int slo = mt == 0 ? sl_1 : sl_2;
-      const bool okn = mt == 0 ? ok1 : ok2;
-      const uint32_t cbn = mt == 0 ? cb1 : cb2;
-      f32x4 w[2];
-      u32x4 off[2];
-      f32x4 r;
-      auto act = [&](auto X) {
-        constexpr int x = decltype(X)::value;
-        if constexpr (x < 4) {
-          constexpr int pi = x >> 1;
-          if constexpr ((x & 1) == 0) w[pi] = Cw[slw * PW + (pa + pi) * 8 + pp];
-          else off[pi] = Co[slo * PW + (pa + pi) * 8 + pp];
-        } else if constexpr (x < NPA) {
-          constexpr int pi = (x - 4) / 9, y = (x - 4) % 9, p = pa + pi;
-          if constexpr (y < 4) {
-            const f32x4 v = __builtin_bit_cast(f32x4, gv[p][y]);
-            if constexpr (y == 0) {
-              r = v * w[pi][0];
-            } else {
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk) r[kk] = __builtin_fmaf(w[pi][y], v[kk], r[kk]);
-            }
-          } else if constexpr (y == 4) {
-            *reinterpret_cast<f32x4*>(&Aw[a_at(p * 8 + pp, sl)]) = r;
+    f32x4 w;
+    u32x4 off;
+    f32x4 r;
+    auto act = [&](auto X) {
+      constexpr int x = decltype(X)::value;
+      if constexpr (x == 0) {
+        af[3] = a_frag(P, 3);
+      } else if constexpr (x < 1 + 4 * NPA) {
+        constexpr int p = (x - 1) / NPA, y = (x - 1) % NPA;
+        if constexpr (y == 0) {
+          w = Cw[sl_1 * PW + p * 8 + pp];
+        } else if constexpr (y == 1) {
+          off = Co[sl_2 * PW + p * 8 + pp];
+        } else if constexpr (y < 6) {
+          constexpr int c = y - 2;
+          const f32x4 v = __builtin_bit_cast(f32x4, gv[p][c]);
+          if constexpr (c == 0) {
+            r = v * w[0];
           } else {
-            constexpr int c = y - 5;
-            gv[p][c] = load16(xr, okn ? off[pi][c] + cbn : kNoCorner);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) r[kk] = __builtin_fmaf(w[c], v[kk], r[kk]);
           }
-        } else if constexpr (x < NPA + 2) {
-          // rows 16-31 of block s (group 0) / rows 0-15 of block s+1 (group 1)
-          af[mt ^ 1][x - NPA] = a_frag(mt ^ 1, x - NPA);
-        } else if constexpr (mt == 0) {
-          bw[P ^ 1][x - NPA - 2] = *reinterpret_cast<const f32x4*>(bsrc + (x - NPA - 2) * 256);
-        } else if constexpr (x < NPA + 6) {
-          if (coef_due) coef_stage(x - NPA - 2, tc, c_dy[P], c_dx[P], c_mk[P]);
+        } else if constexpr (y == 6) {
+          *reinterpret_cast<f32x4*>(&Aw[(P ^ 1) * A_FLOATS + a_at(p * 8 + pp, sl)]) = r;
+        } else if constexpr (y < 11) {
+          constexpr int c = y - 7;
+          gv[p][c] = load16(xr, ok2 ? off[c] + cb2 : kNoCorner);
         } else {
-          coef_load(tl, c_dy[P], c_dx[P], c_mk[P]);
+          constexpr int k = 2 * p + (y - 11);
+          bw[P ^ 1][k] = *reinterpret_cast<const f32x4*>(bsrc + k * 256);
         }
-      };
-      static_for<NMF>([&](auto J) {
-        constexpr int jj = decltype(J)::value;
-        constexpr int k = jj / NT, nt = jj % NT;  // k-step 0..7, tile
-        constexpr int q = k / 4, e = k % 4;
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][q][e], bw[P][nt * 2 + q][e],
-                                                           acc[mt][nt], 0, 0, 0);
-        static_for<NACT>([&](auto X) {
-          constexpr int x = decltype(X)::value;
-          if constexpr (x * NMF / NACT == jj) act(X);
-        });
-        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (x < 4 + 4 * NPA) {
+        af[x - 1 - 4 * NPA] = a_frag(P ^ 1, x - 1 - 4 * NPA);
+      } else if constexpr (x < 8 + 4 * NPA) {
+        if (coef_due) coef_stage(x - 4 - 4 * NPA, tc, c_dy[P], c_dx[P], c_mk[P]);
+      } else {
+        coef_load(tl, c_dy[P], c_dx[P], c_mk[P]);
+      }
+    };
+    static_for<NMF>([&](auto J) {
+      constexpr int jj = decltype(J)::value;
+      constexpr int n = jj & 1, q = jj >> 3, e = (jj >> 1) & 3;  // k-step 4q + e
+      acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[q][e], bw[P][n * 4 + q][e], acc[n], 0,
+                                                     0, 0);
+      static_for<NACT>([&](auto X) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x * NMF / NACT == jj) act(X);
       });
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
   int s = 0;
@@ -352,14 +363,16 @@ fused_quad_kernel(Src src) {
   if (s < NKB) step(s, S0{});
 
   // ---- epilogue: sum the two channel halves (and tap groups) of each pixel
-  // half, + bias, store: (g0 c0 + g0 c1) + (g1 c0 + g1 c1)
-  __syncthreads();  // every wave is done with its column tile and tables
+  // half, + bias, store: (g0 c0 + g0 c1) + (g1 c0 + g1 c1).  MFMA 32x32
+  // result layout: lane l, register r -> row (pixel) 8 (r / 4) + 4 (l / 32) +
+  // r % 4, column (output of half n) l % 32.
+  __syncthreads();  // every wave is done with its column tiles and tables
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<f32x4*>(&red[(wave * NO + nt * 16 + rl) * RST + mt * 16 + g * 4]) =
-          acc[mt][nt];
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<f32x4*>(&red[(wave * NO + n * 32 + rl) * RST + 8 * r4 + 4 * hh]) =
+          f32x4{acc[n][4 * r4], acc[n][4 * r4 + 1], acc[n][4 * r4 + 2], acc[n][4 * r4 + 3]};
   __syncthreads();
   const float* biasp = static_cast<const float*>(a.bias);  // NULL for a split
   float* const outp = a.out + (size_t)split * a.split_stride;
