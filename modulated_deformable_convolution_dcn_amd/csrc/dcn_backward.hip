@@ -849,25 +849,25 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     p[e] = 0.0f;
 }
 
-// Two small buffers in one launch: [0, n0) of p0, then [0, n1) of p1.
-__global__ __launch_bounds__(256) void fill_zero2_kernel(float* __restrict__ p0, int64_t n0,
-                                                         float* __restrict__ p1, int64_t n1) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n0 + n1;
-       e += (int64_t)gridDim.x * 256) {
-    if (e < n0) p0[e] = 0.0f;
-    else p1[e - n0] = 0.0f;
-  }
-}
 
 // weight [O][C][kh][kw] -> per (tap, 64-channel chunk) block [OP/4][64][4]:
 // element (o, c) at ((o / 4) * 64 + c % 64) * 4 + o % 4, so one 16-byte read
 // gives a lane 4 consecutive outputs of one channel (4 MFMA k-steps).  One
 // thread per packed element, padding (o >= O or c >= C) written as zero in
-// the same pass.
+// the same pass.  The same launch zero-fills the weight and bias gradients
+// (nw and nb elements of gw and gb; the weight and bias kernels add into
+// them with atomics).
 __global__ __launch_bounds__(256) void bwd_pack_kernel(const float* __restrict__ w,
                                                        float* __restrict__ wt, int O, int C,
-                                                       int K, int OP, int nchunk) {
+                                                       int K, int OP, int nchunk,
+                                                       float* __restrict__ gw, int64_t nw,
+                                                       float* __restrict__ gb, int64_t nb) {
   const int64_t total = (int64_t)K * nchunk * OP * 64;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < nw + nb;
+       e += (int64_t)gridDim.x * 256) {
+    if (e < nw) gw[e] = 0.0f;
+    else gb[e - nw] = 0.0f;
+  }
   for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < total;
        d += (int64_t)gridDim.x * 256) {
     const int64_t blk = d / (OP * 64);
@@ -933,22 +933,16 @@ hipError_t launch_backward(const BwdArgs& a0, const float* weight, float* ws, hi
   BwdArgs a = a0;
   const int OP = bwd_out_pad(a.O);
   hipError_t e;
-  // zero the outputs that atomics accumulate into (the offset and mask
-  // gradients are stored by their owning workgroup, the re-packed weight
-  // writes its own padding)
+  // zero the outputs that atomics accumulate into: grad_x here, the weight
+  // and bias gradients in the re-pack launch (the offset and mask gradients
+  // are stored by their owning workgroup, the re-packed weight writes its own
+  // padding)
   const int64_t nx = (int64_t)a.B * a.H * a.W * a.C;
   if ((e = zero(a.gx, nx, s)) != hipSuccess) return e;
-  {
-    const int64_t nw = a.gw ? (int64_t)a.O * a.C * a.K : 0, nb = a.gb ? a.O : 0;
-    if (nw + nb > 0) {
-      hipLaunchKernelGGL(fill_zero2_kernel, dim3(grid_of(nw + nb)), dim3(256), 0, s, a.gw, nw,
-                         a.gb, nb);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
+  const int64_t nw = a.gw ? (int64_t)a.O * a.C * a.K : 0, nb = a.gb ? a.O : 0;
   const int64_t nws = bwd_workspace_floats(a.O, a.C, a.K);
-  hipLaunchKernelGGL(bwd_pack_kernel, dim3(grid_of(nws)), dim3(256), 0, s, weight, ws, a.O, a.C,
-                     a.K, OP, a.nchunk);
+  hipLaunchKernelGGL(bwd_pack_kernel, dim3(grid_of(nws > nw + nb ? nws : nw + nb)), dim3(256), 0,
+                     s, weight, ws, a.O, a.C, a.K, OP, a.nchunk, a.gw, nw, a.gb, nb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.wt = ws;
   if (a.gx || a.goff || a.gmask) {
