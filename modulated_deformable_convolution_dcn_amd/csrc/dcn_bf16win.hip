@@ -256,6 +256,15 @@ fused_bf16win_kernel(Src src) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
                                           __builtin_bit_cast(bf16x2, w), acc, false);
   };
+  // the same with a zero accumulator, as one VOP3P instruction: the
+  // builtin's zero becomes a register move plus the accumulating VOP2 form,
+  // one VALU instruction more per corner row 0 dot
+  auto pair_dot0 = [](uint32_t v0, uint32_t v1, int h, uint32_t w) {
+    const uint32_t pr = __builtin_amdgcn_perm(v1, v0, h ? 0x07060302u : 0x05040100u);
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(pr), "v"(w));
+    return r;
+  };
 
   // ---- (c) MFMA: lane group g supplies channels 8g .. 8g+7 of the block.
   const int rl = lane & 15;
@@ -384,8 +393,10 @@ fused_bf16win_kernel(Src src) {
           if constexpr (mt == 0) bw[t2 % 3][nt] = b_load(c2, t2, nt);
           // blend unit: corner row cp, channel e = 2 * (dword) + (half)
           constexpr int cp = j / 8, e = j % 8;
-          r[e] = pair_dot(gv[2 * cp][e / 2], gv[2 * cp + 1][e / 2], e & 1, wt[cp],
-                          cp == 0 ? 0.0f : r[e]);
+          if constexpr (cp == 0)
+            r[e] = pair_dot0(gv[0][e / 2], gv[1][e / 2], e & 1, wt[0]);
+          else
+            r[e] = pair_dot(gv[2][e / 2], gv[3][e / 2], e & 1, wt[1], r[e]);
           if constexpr (e == 7) {
             gv[2 * cp] = fetch(en[2 * cp], c2);
             gv[2 * cp + 1] = fetch(en[2 * cp + 1], c2);
