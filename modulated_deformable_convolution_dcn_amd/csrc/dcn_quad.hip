@@ -348,10 +348,9 @@ fused_quad_kernel(Src src) {
       constexpr int n = jj & 1, q = jj >> 3, e = (jj >> 1) & 3;  // k-step 4q + e
       acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[q][e], bw[P][n * 4 + q][e], acc[n], 0,
                                                      0, 0);
-      static_for<NACT>([&](auto X) {
-        constexpr int x = decltype(X)::value;
-        if constexpr (x * NMF / NACT == jj) act(X);
-      });
+      // actions x with x * NMF / NACT == jj: x in [x0, x1)
+      constexpr int x0 = (jj * NACT + NMF - 1) / NMF, x1 = ((jj + 1) * NACT + NMF - 1) / NMF;
+      static_for<x1 - x0>([&](auto D) { act(std::integral_constant<int, x0 + decltype(D)::value>{}); });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
